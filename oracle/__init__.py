@@ -1,0 +1,13 @@
+"""fp64 CPU oracle for varlen attention (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg import this package.  It shares no code with the HIP
+path.  Every function is pinned by tests against brute force, a library
+routine on its special cases, closed forms and invariants; none is
+"parity unpinned".
+"""
+from .ref_attention import (attention_rows, bias_head, finish_rows, kv_head_of, logits,
+                            softmax_rows, varlen_attention, visible, visible_counts)
+
+__all__ = ["attention_rows", "bias_head", "finish_rows", "kv_head_of", "logits", "softmax_rows",
+           "varlen_attention", "visible", "visible_counts"]

@@ -1,0 +1,323 @@
+"""Pins that tie the fp64 oracle to something other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees
+with an independent statement of what attention must return: a pure-Python
+brute force written straight from the definitions, PyTorch's own
+``scaled_dot_product_attention`` on the cases where it computes the same
+thing, hand-derived closed forms, and invariants of softmax attention.
+``test_oracle_pins.py`` runs them; ``test_oracle_mutations.py`` plants
+plausible mistakes in the oracle and checks that some pin catches each.
+
+Definitions follow the mtlattn 0.3.0 project page, section "Use" (packed
+layout, cu_seqlens, end-aligned causal rule, last-W-keys window, GQA head
+map, additive bias).
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import ref_attention as ra
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+# ---------------------------------------------------------------- helpers
+def _tiny_case(rng, nseq, max_len, hq, hkv, dqk, dv, cross=False, bias_heads=0, neg_inf=0.0):
+    lq = rng.integers(0, max_len + 1, size=nseq)
+    lk = rng.integers(0, max_len + 1, size=nseq) if cross else lq.copy()
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
+    cu_kv = np.concatenate([[0], np.cumsum(lk)]).astype(np.int64)
+    q = rng.standard_normal((int(cu_q[-1]), hq, dqk))
+    k = rng.standard_normal((int(cu_kv[-1]), hkv, dqk))
+    v = rng.standard_normal((int(cu_kv[-1]), hkv, dv))
+    bias = None
+    if bias_heads:
+        cols = int(max(lk.max(initial=0), 1))
+        bias = rng.standard_normal((int(cu_q[-1]), bias_heads, cols))
+        bias[rng.random(bias.shape) < neg_inf] = -np.inf
+    return q, k, v, cu_q, cu_kv, bias
+
+
+def brute_force(q, k, v, cu_q, cu_kv, scale, causal, window, bias):
+    """Scalar loops over (sequence, head, query, key, dim) with math.exp and
+    math.fsum, written from the definitions without any oracle helper."""
+    tq, hq, dqk = q.shape
+    hkv, dv = k.shape[1], v.shape[2]
+    out = np.zeros((tq, hq, dv))
+    lse = np.full((hq, tq), -math.inf)
+    for s in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[s]), int(cu_q[s + 1]), int(cu_kv[s]), int(cu_kv[s + 1])
+        lq, lk = q1 - q0, k1 - k0
+        for h in range(hq):
+            g = h // (hq // hkv)
+            for i in range(lq):
+                zs = []
+                for j in range(lk):
+                    if causal and not (j <= i + lk - lq):
+                        continue
+                    if window and not (j > i + lk - lq - window):
+                        continue
+                    z = scale * math.fsum(float(q[q0 + i, h, d]) * float(k[k0 + j, g, d])
+                                          for d in range(dqk))
+                    if bias is not None:
+                        z += float(bias[q0 + i, 0 if bias.shape[1] == 1 else h, j])
+                    if z == -math.inf:
+                        continue
+                    zs.append((j, z))
+                if not zs:
+                    continue
+                m = max(z for _, z in zs)
+                w = [(j, math.exp(z - m)) for j, z in zs]
+                l = math.fsum(x for _, x in w)
+                for d in range(dv):
+                    out[q0 + i, h, d] = math.fsum(x * float(v[k0 + j, g, d]) for j, x in w) / l
+                lse[h, q0 + i] = m + math.log(l)
+    return out, lse
+
+
+def _close(a, b, tol):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    same_inf = (a == b)
+    fin = np.isfinite(a) & np.isfinite(b)
+    assert np.all(same_inf | fin), "non-finite mismatch"
+    diff = np.subtract(a, b, out=np.zeros_like(a), where=fin)
+    err = np.max(np.abs(diff), initial=0.0)
+    assert err <= tol, f"max abs err {err} > {tol}"
+
+
+# ---------------------------------------------------------------- pins
+def pin_brute_force_tiny():
+    """All flag combinations on tiny ragged inputs vs scalar brute force."""
+    rng = np.random.default_rng(1234)
+    combos = itertools.product([False, True], [0, 1, 3], [0, 1, 2], [False, True])
+    for causal, window, bias_mode, cross in combos:
+        if window and not causal:
+            continue
+        hq, hkv = (4, 2) if bias_mode != 1 else (4, 1)
+        q, k, v, cu_q, cu_kv, bias = _tiny_case(
+            rng, 3, 6, hq, hkv, 5, 3, cross=cross,
+            bias_heads={0: 0, 1: 1, 2: hq}[bias_mode], neg_inf=0.2)
+        scale = 0.37
+        o1, l1 = oracle.varlen_attention(q, k, v, cu_q, cu_kv, scale, causal, window, bias)
+        o2, l2 = brute_force(q, k, v, cu_q, cu_kv, scale, causal, window, bias)
+        _close(o1, o2, 1e-12)
+        _close(l1, l2, 1e-12)
+
+
+def pin_sdpa_special_case():
+    """Lq == Lk per sequence: torch's float64 CPU SDPA computes the same thing
+    (its top-left causal diagonal equals the end-aligned one when Lq == Lk)."""
+    import torch.nn.functional as F
+    rng = np.random.default_rng(99)
+    for causal, window, with_bias, (hq, hkv) in itertools.product(
+            [False, True], [0, 4], [False, True], [(4, 4), (6, 2), (3, 1)]):
+        if window and not causal:
+            continue
+        lens = [7, 1, 19, 12]
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        T, D = int(cu[-1]), 16
+        q = rng.standard_normal((T, hq, D))
+        k = rng.standard_normal((T, hkv, D))
+        v = rng.standard_normal((T, hkv, 8))
+        bias = rng.standard_normal((T, hq, max(lens))) if with_bias else None
+        out, lse = oracle.varlen_attention(q, k, v, cu, cu, None, causal, window, bias)
+        for s, L in enumerate(lens):
+            sl = slice(int(cu[s]), int(cu[s + 1]))
+            tq = torch.from_numpy(q[sl]).permute(1, 0, 2)[None]
+            tk = torch.from_numpy(k[sl]).permute(1, 0, 2)[None]
+            tv = torch.from_numpy(v[sl]).permute(1, 0, 2)[None]
+            mask = None
+            use_is_causal = causal and not window and not with_bias
+            if causal and not use_is_causal:
+                ones = torch.ones(L, L, dtype=torch.bool)
+                band = torch.tril(ones)
+                if window:
+                    band = band & torch.triu(ones, diagonal=-(window - 1))
+                mask = torch.zeros(L, L, dtype=torch.float64).masked_fill(~band, -math.inf)
+            if with_bias:
+                b = torch.from_numpy(bias[sl, :, :L]).permute(1, 0, 2)[None]
+                mask = b if mask is None else mask + b
+            ref = F.scaled_dot_product_attention(
+                tq, tk, tv, attn_mask=mask, is_causal=use_is_causal, enable_gqa=hq != hkv)
+            _close(out[sl], ref[0].permute(1, 0, 2).numpy(), 1e-12)
+            # lse against scipy's logsumexp over the explicit scores
+            from scipy.special import logsumexp
+            rep = hq // hkv
+            for h in range(hq):
+                z = (q[sl, h, :] @ k[sl, h // rep, :].T) / math.sqrt(D)
+                if with_bias:
+                    z = z + bias[sl, h, :L]
+                i = np.arange(L)[:, None]
+                j = np.arange(L)[None, :]
+                if causal:
+                    z = np.where(j <= i, z, -np.inf)
+                if window:
+                    z = np.where(j > i - window, z, -np.inf)
+                _close(lse[h, sl], logsumexp(z, axis=1), 1e-12)
+
+
+def pin_rows_sum_to_one():
+    rng = np.random.default_rng(5)
+    q, k, v, cu_q, cu_kv, bias = _tiny_case(rng, 4, 40, 2, 2, 8, 4, cross=True, bias_heads=2,
+                                            neg_inf=0.3)
+    for causal, window in [(False, 0), (True, 0), (True, 5)]:
+        for s in range(4):
+            lq = int(cu_q[s + 1] - cu_q[s])
+            if lq == 0:
+                continue
+            _, lse, p = oracle.attention_rows(q, k, v, cu_q, cu_kv, s, 1, np.arange(lq), 0.3,
+                                              causal, window, bias, return_p=True)
+            sums = p.sum(axis=1)
+            nonempty = np.isfinite(lse)
+            assert np.all(np.abs(sums[nonempty] - 1.0) <= 1e-12)
+            assert np.all(sums[~nonempty] == 0.0)
+            assert np.all(p >= 0.0)
+
+
+def pin_one_key_sequence():
+    """A sequence with a single key returns that key's v exactly, lse = its logit."""
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((5, 2, 8))
+    k = rng.standard_normal((1, 2, 8))
+    v = rng.standard_normal((1, 2, 3))
+    cu_q, cu_kv = np.array([0, 5]), np.array([0, 1])
+    out, lse = oracle.varlen_attention(q, k, v, cu_q, cu_kv, 0.25, False, 0, None)
+    for h in range(2):
+        assert np.array_equal(out[:, h, :], np.broadcast_to(v[0, h], (5, 3)))
+        z = 0.25 * (q[:, h, :] @ k[0, h, :])
+        _close(lse[h], z, 1e-14)
+
+
+def pin_zero_queries_mean():
+    """q = 0: every visible key has logit 0, so out is the mean of the visible
+    v rows and lse = ln(count); the visible range is the closed form
+    [max(0, i+off-W+1), min(i+off, Lk-1)]."""
+    rng = np.random.default_rng(7)
+    for causal, window, (lq, lk) in itertools.product(
+            [False, True], [0, 3, 10], [(9, 9), (4, 11), (11, 4), (1, 1)]):
+        if window and not causal:
+            continue
+        q = np.zeros((lq, 2, 4))
+        k = rng.standard_normal((lk, 1, 4))
+        v = rng.standard_normal((lk, 1, 5))
+        out, lse = oracle.varlen_attention(q, k, v, np.array([0, lq]), np.array([0, lk]), None,
+                                           causal, window, None)
+        off = lk - lq
+        for i in range(lq):
+            hi = min(i + off, lk - 1) if causal else lk - 1
+            lo = max(0, i + off - window + 1) if window else 0
+            n = hi - lo + 1
+            for h in range(2):
+                if n <= 0:
+                    assert np.all(out[i, h] == 0.0) and lse[h, i] == -np.inf
+                else:
+                    _close(out[i, h], v[lo:hi + 1, 0].mean(axis=0), 1e-14)
+                    _close(lse[h, i], math.log(n), 1e-14)
+
+
+def pin_key_permutation_invariance():
+    rng = np.random.default_rng(8)
+    q, k, v, cu_q, cu_kv, bias = _tiny_case(rng, 3, 30, 4, 2, 8, 6, cross=True)
+    out, lse = oracle.varlen_attention(q, k, v, cu_q, cu_kv, None, False, 0, None)
+    perm = np.arange(k.shape[0])
+    for s in range(3):
+        a, b = int(cu_kv[s]), int(cu_kv[s + 1])
+        perm[a:b] = a + rng.permutation(b - a)
+    out2, lse2 = oracle.varlen_attention(q, k[perm], v[perm], cu_q, cu_kv, None, False, 0, None)
+    _close(out, out2, 1e-12)
+    _close(lse, lse2, 1e-12)
+
+
+def pin_neg_inf_key_is_removed():
+    """A key whose bias is -inf gets probability exactly 0, and the result
+    equals the result with that key deleted from the sequence."""
+    rng = np.random.default_rng(9)
+    L, D = 13, 8
+    q = rng.standard_normal((L, 2, D))
+    k = rng.standard_normal((L, 2, D))
+    v = rng.standard_normal((L, 2, 4))
+    bias = np.zeros((L, 1, L))
+    j = 5
+    bias[:, :, j] = -np.inf
+    cu = np.array([0, L])
+    out, lse, p = oracle.attention_rows(q, k, v, cu, cu, 0, 1, np.arange(L), None, False, 0, bias,
+                                        return_p=True)
+    assert np.all(p[:, j] == 0.0)
+    keep = np.array([x for x in range(L) if x != j])
+    out2, lse2 = oracle.attention_rows(q, k[keep], v[keep], cu, np.array([0, L - 1]), 0, 1,
+                                       np.arange(L), None, False, 0, None)
+    _close(out, out2, 1e-15)
+    _close(lse, lse2, 1e-14)
+
+
+def pin_mask_counts_closed_form():
+    """Visible keys per row against closed forms, and the per-(sequence, head)
+    totals of the long workloads."""
+    for lq, lk in [(50, 50), (30, 70), (70, 30), (1, 9), (9, 1)]:
+        off = lk - lq
+        i = np.arange(lq)
+        c = oracle.visible_counts(lq, lk, True, 0)
+        assert np.array_equal(c, np.clip(i + off + 1, 0, lk))
+        for W in (1, 4, 33):
+            c = oracle.visible_counts(lq, lk, True, W)
+            hi = np.clip(i + off + 1, 0, lk)
+            lo = np.clip(i + off - W + 1, 0, lk)
+            assert np.array_equal(c, np.maximum(hi - lo, 0))
+        assert np.array_equal(oracle.visible_counts(lq, lk, False, 0), np.full(lq, lk))
+    # causal total L(L+1)/2 and the 16384-token window-4096 total
+    assert oracle.visible_counts(4080, 4080, True, 0).sum() == 4080 * 4081 // 2
+    assert oracle.visible_counts(16384, 16384, True, 4096).sum() == 58_722_304
+    # prefix-LM bias (keys < 1024 or j <= i) leaves max(1024, i+1) finite keys
+    import workloads
+    b = workloads.prefix_lm_bias([8192], 1024)[:, 0, :]
+    finite = torch.isfinite(b).sum(dim=1).numpy()
+    assert np.array_equal(finite, np.maximum(1024, np.arange(8192) + 1))
+    assert finite.sum() == 34_082_304
+
+
+def pin_golden_hand_worked():
+    """Hand-derived tiny cases stored under tests/golden."""
+    env = {"log": math.log, "exp": math.exp, "inf": math.inf}
+
+    def ev(x):
+        if isinstance(x, str):
+            return float(eval(x.replace("-inf", "(-inf)"), {"__builtins__": {}}, env))
+        return float(x)
+
+    data = json.load(open(GOLDEN))
+    for case in data["cases"]:
+        arr = lambda key: np.vectorize(ev, otypes=[np.float64])(np.array(case[key], dtype=object))
+        q, k, v = arr("q"), arr("k"), arr("v")
+        bias = arr("bias") if "bias" in case else None
+        out, lse = oracle.varlen_attention(q, k, v, np.array(case["cu_q"]), np.array(case["cu_kv"]),
+                                           case["scale"], case["causal"], case["window"], bias)
+        _close(out, arr("out"), 1e-14)
+        _close(lse, arr("lse"), 1e-14)
+
+
+def pin_row_subset_matches_full():
+    """Sampled rows (used for full-size parity) equal the same rows of a full run."""
+    rng = np.random.default_rng(10)
+    q, k, v, cu_q, cu_kv, bias = _tiny_case(rng, 2, 300, 2, 1, 8, 4, cross=True, bias_heads=1,
+                                            neg_inf=0.1)
+    out, lse = oracle.varlen_attention(q, k, v, cu_q, cu_kv, None, True, 17, bias)
+    for s in range(2):
+        lq = int(cu_q[s + 1] - cu_q[s])
+        rows = rng.choice(lq, size=min(lq, 11), replace=False) if lq else np.array([], int)
+        o, l = oracle.attention_rows(q, k, v, cu_q, cu_kv, s, 1, rows, None, True, 17, bias)
+        _close(o, out[cu_q[s] + rows, 1], 0.0)
+        _close(l, lse[1, cu_q[s] + rows], 0.0)
+
+
+ALL_PINS = [pin_brute_force_tiny, pin_sdpa_special_case, pin_rows_sum_to_one,
+            pin_one_key_sequence, pin_zero_queries_mean, pin_key_permutation_invariance,
+            pin_neg_inf_key_is_removed, pin_mask_counts_closed_form, pin_golden_hand_worked,
+            pin_row_subset_matches_full]

@@ -1,0 +1,55 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the
+pins catch every one of them.
+
+Each mutation edits one expression of the oracle's source, loads the edited
+copy as a separate module and points the ``oracle`` package at it for the
+duration of the test.  A mutation counts as caught when at least one pin
+raises.
+"""
+import inspect
+import types
+
+import pytest
+
+import oracle
+from oracle import ref_attention
+from oracle_pins import ALL_PINS
+
+MUTATIONS = {
+    "causal_off_by_one": ("ok = ok & (j <= i + off)", "ok = ok & (j < i + off)"),
+    "causal_top_left": ("ok = ok & (j <= i + off)", "ok = ok & (j <= i)"),
+    "diagonal_sign": ("off = lk - lq", "off = lq - lk"),
+    "window_w_plus_one": ("ok = ok & (j > i + off - window)", "ok = ok & (j >= i + off - window)"),
+    "gqa_modulo": ("return h // (hq // hkv)", "return h % hkv"),
+    "scale_dropped": ("z = scale * (qrows @ kseq.T)", "z = (qrows @ kseq.T)"),
+    "bias_sign": ("z = z + bias_rows", "z = z - bias_rows"),
+    "bias_head_always_zero": ("return 0 if bias_heads == 1 else head", "return 0"),
+    "mask_dropped": ("unmasked = mask & (z != -np.inf)", "unmasked = (z != -np.inf)"),
+    "no_normalisation": ("pn = p / safe_l[:, None]", "pn = p"),
+    "lse_log2": ("np.where(np.isfinite(m), m, 0.0) + np.log(safe_l)",
+                 "np.where(np.isfinite(m), m, 0.0) + np.log2(safe_l)"),
+    "lse_without_max": ("np.where(np.isfinite(m), m, 0.0) + np.log(safe_l)", "np.log(safe_l)"),
+    "empty_row_lse_zero": ("np.log(safe_l), -np.inf)", "np.log(safe_l), 0.0)"),
+    "k_rows_from_query_offsets": ("kseq = k[ck0:ck1, g, :]", "kseq = k[cq0:cq0 + lk, g, :]"),
+    "v_from_query_head": ("vseq = v[ck0:ck1, g, :]", "vseq = v[ck0:ck1, head % v.shape[1], :]"),
+    "key_range_upper_open": ("ok = (j >= 0) & (j < lk)", "ok = (j >= 0) & (j < lk - 1)"),
+}
+
+SOURCE = inspect.getsource(ref_attention)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name, monkeypatch):
+    old, new = MUTATIONS[name]
+    assert SOURCE.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    mutated = types.ModuleType("oracle_mutant")
+    exec(compile(SOURCE.replace(old, new), "oracle_mutant", "exec"), mutated.__dict__)
+    for attr in oracle.__all__:
+        monkeypatch.setattr(oracle, attr, getattr(mutated, attr))
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except Exception as e:  # an assertion or a crash both expose the mistake
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin catches mutation {name}"
