@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused varlen attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 15] [--workload gqa_causal_bf16]
+
+One step is one call of the whole hot path (one kernel launch computing
+out and lse) over the workload's packed batch, with q/k/v/cu_seqlens
+already resident in HBM.  The default workload is the bf16 causal GQA
+varlen prefill: 8 sequences (lengths 1677, 2626, 1676, 2065, 630, 4080,
+4078, 3373 drawn from seed 1), Hq=32, Hkv=8, D=128, scale 1/sqrt(128).
+
+Reported value: useful TFLOP/s, i.e. (2*Dqk + 2*Dv) FLOPs per unmasked
+(query, key, head) triple divided by the time of one launch.  The JSON line
+also carries the MFMA roofline of the kernel and the fp64 CPU oracle timed
+on a bounded sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "attn fwd useful TFLOP/s + % of MI355X bf16 MFMA peak (causal GQA D=128)"
+# MI355X dense MFMA peaks (TFLOP/s): 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU for
+# bf16/fp16; fp32 matrix 157.3.
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+HBM_GBPS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "flash_attention_varlen_amd", "csrc", "attn_fwd.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+# ----------------------------------------------------------------- accounting
+def visible_pairs_per_row(lq: int, lk: int, causal: bool, window: int) -> np.ndarray:
+    """Closed-form number of visible keys of each query row (end-aligned)."""
+    i = np.arange(lq, dtype=np.int64)
+    off = lk - lq
+    hi = np.clip(i + off + 1, 0, lk) if causal else np.full(lq, lk, dtype=np.int64)
+    lo = np.clip(i + off - window + 1, 0, lk) if window else np.zeros(lq, dtype=np.int64)
+    return np.maximum(hi - lo, 0)
+
+
+def useful_pairs(w: workloads.Workload, bias=None) -> int:
+    """Unmasked (query, key) pairs summed over sequences and query heads.
+
+    With a bias, keys whose bias is -inf are masked too; the count then
+    comes from the bias tensor itself (per head if it has one per head).
+    """
+    total = 0
+    q0 = 0
+    for lq, lk in zip(w.seqlens_q, w.seqlens_kv):
+        if bias is None:
+            total += int(visible_pairs_per_row(lq, lk, w.causal, w.window).sum()) * w.hq
+        else:
+            import torch
+            b = bias[q0:q0 + lq, :, :lk]
+            finite = torch.isfinite(b)
+            i = torch.arange(lq).view(lq, 1, 1)
+            j = torch.arange(lk).view(1, 1, lk)
+            off = lk - lq
+            vis = torch.ones(lq, 1, lk, dtype=torch.bool)
+            if w.causal:
+                vis &= j <= i + off
+            if w.window:
+                vis &= j > i + off - w.window
+            per_head = (finite & vis).sum(dim=(0, 2))
+            total += int(per_head.sum()) * (w.hq if b.shape[1] == 1 else 1)
+        q0 += lq
+    return total
+
+
+def useful_flops(w: workloads.Workload, bias=None) -> float:
+    return float(useful_pairs(w, bias)) * (2 * w.d_qk + 2 * w.d_v)
+
+
+def algorithmic_bytes(w: workloads.Workload, out_bytes: int) -> float:
+    """q, k, v, out and lse each moved once (the bias once if present)."""
+    e = 4 if w.dtype == "f32" else 2
+    b = w.total_q * w.hq * w.d_qk * e + w.total_kv * w.hkv * (w.d_qk + w.d_v) * e
+    b += w.total_q * w.hq * w.d_v * out_bytes + w.total_q * w.hq * 4
+    if w.bias is not None:
+        b += w.total_q * w.max_seqlen_kv * 4
+    return float(b)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in (KERNEL_SOURCE, os.path.join(os.path.dirname(KERNEL_SOURCE), "attn_fwd.h")):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload_key: str, launches: int = 1):
+    """HBM bytes per launch from the committed PMC summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"traffic_attn_fwd_{workload_key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return float(t["hbm_bytes_per_launch"]) * launches
+
+
+# ----------------------------------------------------------------- CPU oracle baseline
+def _oracle_unit(args):
+    """One (sequence, head) of the oracle, single-threaded BLAS."""
+    s, h, scale, causal, window = args
+    from threadpoolctl import threadpool_limits
+    import oracle
+    with threadpool_limits(1):
+        lq = int(_G["cq"][s + 1] - _G["cq"][s])
+        for r0 in range(0, lq, 256):
+            rows = np.arange(r0, min(lq, r0 + 256))
+            oracle.attention_rows(_G["q"], _G["k"], _G["v"], _G["cq"], _G["ck"], s, h, rows,
+                                  scale, causal, window, _G["b"])
+    return s, h
+
+
+_G = {}
+
+
+def _pool_init(q, k, v, cq, ck, b):
+    _G.update(q=q, k=k, v=v, cq=cq, ck=ck, b=b)
+
+
+def cpu_baseline(inp: workloads.Inputs, heads, cores: int):
+    """Time the fp64 oracle (as it is) over the sampled heads of every
+    sequence on `cores` worker processes; returns the baseline object."""
+    import multiprocessing as mp
+    w = inp.workload
+    q = inp.q.double().numpy()
+    k = inp.k.double().numpy()
+    v = inp.v.double().numpy()
+    b = inp.bias.double().numpy() if inp.bias is not None else None
+    cq = inp.cu_seqlens_q.numpy().astype(np.int64)
+    ck = inp.cu_seqlens_kv.numpy().astype(np.int64)
+    units = [(s, h, w.softmax_scale, w.causal, w.window) for s in range(w.num_seqs)
+             for h in heads]
+    # biggest units first so the pool drains evenly
+    units.sort(key=lambda u: -(w.seqlens_q[u[0]] * w.seqlens_kv[u[0]]))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores, initializer=_pool_init, initargs=(q, k, v, cq, ck, b)) as pool:
+        for _ in pool.imap_unordered(_oracle_unit, units):
+            pass
+    dt = time.perf_counter() - t0
+    pairs_per_head = useful_pairs(w.with_(hq=1, hkv=1), None) if b is None else None
+    if pairs_per_head is None:
+        pairs = useful_pairs(w, inp.bias) * len(heads) / w.hq
+    else:
+        pairs = pairs_per_head * len(heads)
+    flops = pairs * (2 * w.d_qk + 2 * w.d_v)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 NumPy oracle on query heads {list(heads)} of all {w.num_seqs} "
+                      f"sequences ({len(units)} (sequence, head) units, "
+                      f"{pairs:.3e} useful pairs), {dt:.1f} s wall on {cores} processes with "
+                      f"1 BLAS thread each",
+            "seconds": round(dt, 2)}
+
+
+# ----------------------------------------------------------------- GPU timing
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=15)
+    ap.add_argument("--workload", default="gqa_causal_bf16", choices=sorted(workloads.ALL))
+    ap.add_argument("--out-dtype", default="input", choices=["input", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8,
+                    help="query heads per sequence the CPU oracle baseline covers")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (PMC calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build runs the forward on a single MI355X "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}); multi-GPU runs are not "
+              f"part of it.", file=sys.stderr)
+        sys.exit(2)
+
+    w = workloads.ALL[args.workload]
+    print(f"# workload {w.name}: {w.description}", file=sys.stderr, flush=True)
+    inp = workloads.make_inputs(w)
+
+    # The CPU oracle runs first, in forked worker processes, before anything
+    # in this process touches the GPU.
+    cpu = None
+    if not args.no_cpu_baseline:
+        cores = min(len(os.sched_getaffinity(0)), 16)
+        heads = list(range(0, w.hq, max(1, w.hq // args.cpu_heads)))[:args.cpu_heads]
+        print(f"# CPU oracle baseline on {cores} processes, heads {heads} ...", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(inp, heads, cores)
+        print(f"# CPU oracle: {cpu['value']:.4g} TFLOP/s in {cpu['seconds']} s", file=sys.stderr,
+              flush=True)
+
+    import torch
+    import flash_attention_varlen_amd as fav
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fav.load_library()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    cq, ck = inp.cu_seqlens_q.to(dev), inp.cu_seqlens_kv.to(dev)
+    bias = inp.bias.to(dev) if inp.bias is not None else None
+    out_dtype = q.dtype if args.out_dtype == "input" else torch.float32
+    out = torch.empty(w.total_q, w.hq, w.d_v, dtype=out_dtype, device=dev)
+    lse = torch.empty(w.hq, w.total_q, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, scale=w.softmax_scale,
+                             causal=w.causal, window=w.window, attn_bias=bias, out=out, lse=lse,
+                             out_dtype=out_dtype, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-launch events on the launch stream (for the median) and one pair
+    # around the whole timed region
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start_all = torch.cuda.Event(enable_timing=True)
+    end_all = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start_all.record(stream)
+    for s, e in evs:
+        s.record(stream)
+        step()
+        e.record(stream)
+    end_all.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start_all.elapsed_time(end_all)
+    per = sorted(s.elapsed_time(e) for s, e in evs)
+    ms_per_step = total_ms / args.steps
+    kernel_ms = sum(per) / len(per)
+
+    flops = useful_flops(w, inp.bias)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    out_bytes = out.element_size()
+    traffic = stored_traffic(args.workload)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy calibration: {n * 4} bytes read, {n * 4} bytes written per copy, 3 copies",
+              file=sys.stderr, flush=True)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v, RNE cast; no dataset or weights)",
+        "config": {
+            "workload": w.name,
+            "seqlens_q": list(w.seqlens_q),
+            "total_tokens": w.total_q,
+            "hq": w.hq, "hkv": w.hkv, "d_qk": w.d_qk, "d_v": w.d_v,
+            "causal": w.causal, "window": w.window,
+            "bias": w.bias, "out_dtype": str(out_dtype).replace("torch.", ""),
+            "useful_flops_per_step": flops,
+            "pct_of_peak": round(100.0 * value / peak, 2),
+            "median_launch_ms": round(per[len(per) // 2], 4),
+            "host_wall_s": round(wall, 3),
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": algorithmic_bytes(w, out_bytes),
+            "kernel": "attn_fwd_kernel",
+            "kernel_ms": round(kernel_ms, 4),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(f"# GPU: {ms_per_step:.4f} ms/step, {value:.1f} useful TFLOP/s "
+          f"({100 * value / peak:.1f}% of {peak} TFLOP/s)", file=sys.stderr, flush=True)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

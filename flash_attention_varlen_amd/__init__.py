@@ -1,0 +1,204 @@
+"""Fused variable-length attention forward for AMD MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in ``include/mi_attn.h``
+(``libmi_attn.so``, built in-tree by ``flash_attention_varlen_amd.build``).
+PyTorch supplies device memory and the stream; every step of the attention
+runs in the library's HIP kernels.  There is no fallback: if the library is
+missing or refuses a call, an exception is raised.
+
+``varlen_attention`` mirrors the call on the mtlattn 0.3.0 project page
+(section "Use"): q, k, v packed ``[total_tokens, heads, head_dim]``,
+``cu_seqlens_*`` int32 ``[num_seqs + 1]``, ``max_seqlen_q``, ``scale``
+(default ``1/sqrt(head_dim)``), ``causal`` (end-aligned), ``window``
+(last W keys up to the causal diagonal), ``attn_bias`` (additive fp32
+``[total_q, H or 1, max_kv]``, a bool mask becomes 0 / -inf).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = ["mi_attn_varlen_fwd", "mi_attn_last_error", "mi_attn_version", "mi_attn_tile_shape",
+           "varlen_attention", "MiAttnFwdParams", "MiAttnError", "load_library", "LIB_PATH",
+           "F32", "F16", "BF16"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi_attn.so")
+
+# dtype codes and return codes of include/mi_attn.h
+F32, F16, BF16 = 0, 1, 2
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_VALIDATION = 0, -1, -2, -3, -4
+
+
+class MiAttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"mi_attn error {code}: {message}")
+        self.code = code
+
+
+class MiAttnFwdParams(ctypes.Structure):
+    """Field-for-field mirror of ``mi_attn_fwd_params``."""
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_kv", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p), ("tile_counts", ctypes.c_void_p),
+        ("num_seqs", ctypes.c_int64), ("max_seqlen_q", ctypes.c_int64),
+        ("total_q", ctypes.c_int64), ("total_kv", ctypes.c_int64),
+        ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+        ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("q_stride_tok", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
+        ("k_stride_tok", ctypes.c_int64), ("k_stride_head", ctypes.c_int64),
+        ("v_stride_tok", ctypes.c_int64), ("v_stride_head", ctypes.c_int64),
+        ("out_stride_tok", ctypes.c_int64), ("out_stride_head", ctypes.c_int64),
+        ("bias_heads", ctypes.c_int32), ("bias_cols", ctypes.c_int64),
+        ("bias_stride_tok", ctypes.c_int64), ("bias_stride_head", ctypes.c_int64),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmi_attn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing; build it with `python -m flash_attention_varlen_amd.build`")
+    lib = ctypes.CDLL(p)
+    lib.mi_attn_varlen_fwd.argtypes = [ctypes.POINTER(MiAttnFwdParams), ctypes.c_void_p]
+    lib.mi_attn_varlen_fwd.restype = ctypes.c_int
+    lib.mi_attn_last_error.argtypes = []
+    lib.mi_attn_last_error.restype = ctypes.c_char_p
+    lib.mi_attn_version.argtypes = []
+    lib.mi_attn_version.restype = ctypes.c_int
+    lib.mi_attn_tile_shape.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.mi_attn_tile_shape.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def mi_attn_last_error() -> str:
+    return load_library().mi_attn_last_error().decode()
+
+
+def mi_attn_version() -> int:
+    return int(load_library().mi_attn_version())
+
+
+def mi_attn_tile_shape(in_dtype: int, d_qk: int, d_v: int):
+    """(BM, BN) of the kernel for this dtype and head dims."""
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    rc = load_library().mi_attn_tile_shape(in_dtype, d_qk, d_v, ctypes.byref(bm), ctypes.byref(bn))
+    if rc != OK:
+        raise MiAttnError(rc, mi_attn_last_error())
+    return bm.value, bn.value
+
+
+def mi_attn_varlen_fwd(params: MiAttnFwdParams, stream: int = 0) -> None:
+    """Call the C entry point; raise MiAttnError on a non-OK return."""
+    params.struct_size = ctypes.sizeof(MiAttnFwdParams)
+    rc = load_library().mi_attn_varlen_fwd(ctypes.byref(params), ctypes.c_void_p(stream))
+    if rc != OK:
+        raise MiAttnError(rc, mi_attn_last_error())
+
+
+# ---------------------------------------------------------------- torch front end
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t not in codes:
+        raise MiAttnError(ERR_UNSUPPORTED, f"dtype {t} is not supported (fp32, fp16, bf16)")
+    return codes[t]
+
+
+def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
+                     scale: Optional[float] = None, causal: bool = False, window: int = 0,
+                     attn_bias=None, out_dtype=None, return_lse: bool = False, out=None,
+                     lse=None, tile_counts=None, stream=None):
+    """Fused varlen attention forward.  Returns ``out`` or ``(out, lse)``.
+
+    q ``[Tq, Hq, Dqk]``, k ``[Tk, Hkv, Dqk]``, v ``[Tk, Hkv, Dv]`` (device,
+    last dim contiguous); ``out`` is ``[Tq, Hq, Dv]`` in ``out_dtype``
+    (default: q's dtype; ``torch.float32`` is also accepted); ``lse`` is
+    ``[Hq, Tq]`` fp32 (natural log).  Forward only: inputs that require grad
+    are refused.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise MiAttnError(ERR_INVALID_ARG, f"{name} must be a device tensor")
+        if t.dim() != 3 or t.stride(-1) != 1:
+            raise MiAttnError(ERR_INVALID_ARG, f"{name} must be [tokens, heads, dim], last dim contiguous")
+        if t.requires_grad:
+            raise MiAttnError(ERR_UNSUPPORTED, "forward-only library: inputs must not require grad")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise MiAttnError(ERR_INVALID_ARG, "q, k and v must share one dtype")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)):
+        if t.dtype != torch.int32 or not t.is_cuda or t.dim() != 1 or not t.is_contiguous():
+            raise MiAttnError(ERR_INVALID_ARG, f"{name} must be a contiguous int32 device vector")
+    if cu_seqlens_q.numel() != cu_seqlens_kv.numel():
+        raise MiAttnError(ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_kv differ in length")
+    tq, hq, dqk = q.shape
+    tk, hkv, _ = k.shape
+    dv = v.shape[2]
+    if k.shape[2] != dqk or v.shape[0] != tk or v.shape[1] != hkv:
+        raise MiAttnError(ERR_INVALID_ARG, "k/v shapes do not match q")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(tq, hq, dv, dtype=out_dtype, device=q.device)
+    elif out.shape != (tq, hq, dv) or out.dtype != out_dtype or out.stride(-1) != 1:
+        raise MiAttnError(ERR_INVALID_ARG, "out has the wrong shape, dtype or layout")
+    if return_lse and lse is None:
+        lse = torch.empty(hq, tq, dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (hq, tq) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise MiAttnError(ERR_INVALID_ARG, "lse must be a contiguous fp32 [Hq, Tq] tensor")
+    bias = attn_bias
+    if bias is not None:
+        if bias.dtype == torch.bool:
+            bias = torch.zeros(bias.shape, dtype=torch.float32, device=bias.device).masked_fill_(
+                ~bias, float("-inf"))
+        if bias.dtype != torch.float32 or bias.dim() != 3 or bias.stride(-1) != 1 or not bias.is_cuda:
+            raise MiAttnError(ERR_INVALID_ARG, "attn_bias must be fp32 [Tq, H or 1, max_kv] on device")
+        if bias.shape[0] != tq or bias.shape[1] not in (1, hq):
+            raise MiAttnError(ERR_INVALID_ARG, "attn_bias must be [Tq, H or 1, max_kv]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+
+    p = MiAttnFwdParams()
+    p.q, p.k, p.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    p.out = out.data_ptr()
+    p.lse = lse.data_ptr() if lse is not None else None
+    p.cu_seqlens_q, p.cu_seqlens_kv = cu_seqlens_q.data_ptr(), cu_seqlens_kv.data_ptr()
+    p.bias = bias.data_ptr() if bias is not None else None
+    p.tile_counts = tile_counts.data_ptr() if tile_counts is not None else None
+    p.num_seqs = cu_seqlens_q.numel() - 1
+    p.max_seqlen_q = int(max_seqlen_q)
+    p.total_q, p.total_kv = tq, tk
+    p.hq, p.hkv, p.d_qk, p.d_v = hq, hkv, dqk, dv
+    p.q_stride_tok, p.q_stride_head = q.stride(0), q.stride(1)
+    p.k_stride_tok, p.k_stride_head = k.stride(0), k.stride(1)
+    p.v_stride_tok, p.v_stride_head = v.stride(0), v.stride(1)
+    p.out_stride_tok, p.out_stride_head = out.stride(0), out.stride(1)
+    if bias is not None:
+        p.bias_heads = bias.shape[1]
+        p.bias_cols = bias.shape[2]
+        p.bias_stride_tok, p.bias_stride_head = bias.stride(0), bias.stride(1)
+    p.in_dtype = _dtype_code(q.dtype)
+    p.out_dtype = _dtype_code(out_dtype)
+    p.scale = float(scale)
+    p.causal = 1 if causal else 0
+    p.window = int(window)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    mi_attn_varlen_fwd(p, int(stream))
+    return (out, lse) if return_lse else out

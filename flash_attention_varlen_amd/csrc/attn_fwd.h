@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI front end (mi_attn.cpp) and the
+// gfx950 kernels (attn_fwd.hip).  Not installed; see include/mi_attn.h for
+// the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi_attn {
+
+constexpr int kThreads = 256;  // 4 wave64s per workgroup
+constexpr int kBM = 128;       // query rows per workgroup (32 per wave)
+
+// Element type codes (same values as the public MI_ATTN_F32 / F16 / BF16).
+constexpr int kF32 = 0;
+constexpr int kF16 = 1;
+constexpr int kBF16 = 2;
+
+// Kernel arguments, passed by value.  Strides are in elements.
+struct KernelArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  const float* bias;
+  int32_t* tile_counts;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
+  int64_t b_st, b_sh;
+  int64_t total_q;
+  int32_t num_seqs;
+  int32_t hq;
+  int32_t group;  // hq / hkv
+  int32_t bias_heads;
+  int32_t causal;
+  int32_t window;
+  float scale_log2;    // softmax scale * log2(e)
+  int32_t split_keys;  // rows seeing fewer keys get a hi/lo split of P
+  int32_t split_bias;  // with a bias, split P on every tile (16-bit types)
+};
+
+// Keys per tile for an input type.
+int tile_bn(int in_dtype);
+
+// Launch on `stream`; grid = (hq * num_seqs, ceil(max_seqlen_q / kBM)).
+hipError_t launch_attn_fwd(const KernelArgs& a, int in_dtype, int out_dtype, int dqk, int dv,
+                           bool bias, dim3 grid, hipStream_t stream);
+
+}  // namespace mi_attn

@@ -1,0 +1,216 @@
+// C-ABI front end of the varlen attention forward: argument validation
+// (correct-or-refuse, as the triton-msl part-1 post describes in its section
+// "Correct-or-refuse"), grid construction and the launch on the caller's
+// stream.  No device memory is allocated here and no host synchronisation
+// happens unless MI_ATTN_VALIDATE=1 asks for the cu_seqlens check.
+#include "mi_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "attn_fwd.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int32_t dt) { return dt == MI_ATTN_F32 ? 4 : 2; }
+
+bool dims_supported(int32_t dt, int32_t dqk, int32_t dv) {
+  if (dqk == 64 && dv == 64) return true;
+  if (dqk == 128 && dv == 128) return true;
+  if (dqk == 192 && dv == 128) return dt != MI_ATTN_F32;
+  return false;
+}
+
+bool env_flag(const char* name) {
+  const char* v = std::getenv(name);
+  return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+}
+
+// Rows that see fewer keys than this get a hi/lo split of P in the PV
+// product (bf16 keeps 8 mantissa bits, so a plain bf16 P costs up to ~2e-3
+// of absolute output error when only a handful of keys are averaged).
+constexpr int kSplitKeysBf16 = 256;
+constexpr int kSplitKeysF16 = 64;
+
+int validate_cu(const int32_t* cu_dev, int64_t n, int64_t total, int64_t max_len,
+                const char* what) {
+  std::vector<int32_t> cu(static_cast<size_t>(n + 1));
+  hipError_t e = hipMemcpy(cu.data(), cu_dev, sizeof(int32_t) * (n + 1), hipMemcpyDeviceToHost);
+  if (e != hipSuccess)
+    return fail(MI_ATTN_ERR_VALIDATION, "%s: copying cu_seqlens failed: %s", what,
+                hipGetErrorString(e));
+  if (cu[0] != 0) return fail(MI_ATTN_ERR_VALIDATION, "%s[0] = %d, expected 0", what, cu[0]);
+  for (int64_t s = 0; s < n; ++s) {
+    const int64_t len = (int64_t)cu[s + 1] - cu[s];
+    if (len < 0)
+      return fail(MI_ATTN_ERR_VALIDATION, "%s decreases at sequence %lld", what, (long long)s);
+    if (max_len >= 0 && len > max_len)
+      return fail(MI_ATTN_ERR_VALIDATION, "%s: sequence %lld has length %lld > bound %lld", what,
+                  (long long)s, (long long)len, (long long)max_len);
+  }
+  if (cu[n] != total)
+    return fail(MI_ATTN_ERR_VALIDATION, "%s[%lld] = %d, expected total %lld", what, (long long)n,
+                cu[n], (long long)total);
+  return MI_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mi_attn_last_error(void) { return g_last_error.c_str(); }
+
+int mi_attn_version(void) { return MI_ATTN_VERSION; }
+
+int mi_attn_tile_shape(int32_t in_dtype, int32_t d_qk, int32_t d_v, int32_t* bm, int32_t* bn) {
+  if (in_dtype != MI_ATTN_F32 && in_dtype != MI_ATTN_F16 && in_dtype != MI_ATTN_BF16)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "unknown dtype %d", in_dtype);
+  if (!dims_supported(in_dtype, d_qk, d_v))
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "head dims (%d, %d) unsupported for dtype %d", d_qk, d_v,
+                in_dtype);
+  if (bm) *bm = mi_attn::kBM;
+  if (bn) *bn = mi_attn::tile_bn(in_dtype);
+  return MI_ATTN_OK;
+}
+
+int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
+  g_last_error.clear();
+  if (p == nullptr) return fail(MI_ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (p->struct_size < sizeof(mi_attn_fwd_params))
+    return fail(MI_ATTN_ERR_INVALID_ARG, "struct_size %zu < %zu (library built for a newer ABI)",
+                p->struct_size, sizeof(mi_attn_fwd_params));
+  const int32_t dt = p->in_dtype;
+  if (dt != MI_ATTN_F32 && dt != MI_ATTN_F16 && dt != MI_ATTN_BF16)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "unknown in_dtype %d", dt);
+  if (p->out_dtype != dt && p->out_dtype != MI_ATTN_F32)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "out_dtype must equal in_dtype or be F32 (got %d)",
+                p->out_dtype);
+  if (!dims_supported(dt, p->d_qk, p->d_v))
+    return fail(MI_ATTN_ERR_UNSUPPORTED,
+                "head dims (d_qk=%d, d_v=%d) unsupported for this dtype; supported: (64,64), "
+                "(128,128), and (192,128) for 16-bit inputs",
+                p->d_qk, p->d_v);
+  if (p->hq <= 0 || p->hkv <= 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "head counts must be positive (hq=%d, hkv=%d)", p->hq,
+                p->hkv);
+  if (p->hq % p->hkv != 0)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "hq (%d) must be a multiple of hkv (%d)", p->hq, p->hkv);
+  if (p->num_seqs < 0 || p->max_seqlen_q < 0 || p->total_q < 0 || p->total_kv < 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "negative size");
+  if (p->window < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "window must be >= 0");
+  if (p->causal != 0 && p->causal != 1) return fail(MI_ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->window > 0 && !p->causal)
+    return fail(MI_ATTN_ERR_UNSUPPORTED,
+                "a sliding window is defined relative to the causal diagonal; set causal=1");
+  if (!std::isfinite(p->scale)) return fail(MI_ATTN_ERR_INVALID_ARG, "scale is not finite");
+  if (!(p->scale > 0.0f))
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "scale must be > 0 (got %g)", (double)p->scale);
+  if (p->total_q > INT32_MAX || p->total_kv > INT32_MAX)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "total token counts must fit in int32 (cu_seqlens)");
+
+  if (p->num_seqs == 0 || p->max_seqlen_q == 0 || p->total_q == 0) return MI_ATTN_OK;
+
+  if (!p->q || !p->k || !p->v || !p->out || !p->cu_seqlens_q || !p->cu_seqlens_kv)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "q, k, v, out, cu_seqlens_q and cu_seqlens_kv are required");
+  if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->out))
+    return fail(MI_ATTN_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  const int64_t in_mult = 16 / elem_size(dt);
+  const int64_t out_mult = 16 / elem_size(p->out_dtype);
+  const int64_t in_strides[6] = {p->q_stride_tok, p->q_stride_head, p->k_stride_tok,
+                                 p->k_stride_head, p->v_stride_tok, p->v_stride_head};
+  for (int64_t s : in_strides)
+    if (s < 0 || s % in_mult != 0)
+      return fail(MI_ATTN_ERR_INVALID_ARG,
+                  "q/k/v strides must be non-negative multiples of %lld elements (got %lld)",
+                  (long long)in_mult, (long long)s);
+  if (p->out_stride_tok < 0 || p->out_stride_head < 0 || p->out_stride_tok % out_mult != 0 ||
+      p->out_stride_head % out_mult != 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "out strides must be non-negative multiples of %lld",
+                (long long)out_mult);
+  const bool has_bias = p->bias != nullptr;
+  if (has_bias) {
+    if (p->bias_heads != 1 && p->bias_heads != p->hq)
+      return fail(MI_ATTN_ERR_UNSUPPORTED, "bias_heads must be 1 or hq (got %d)", p->bias_heads);
+    if (!aligned16(p->bias) || p->bias_stride_tok < 0 || p->bias_stride_head < 0 ||
+        p->bias_stride_tok % 4 != 0 || p->bias_stride_head % 4 != 0)
+      return fail(MI_ATTN_ERR_INVALID_ARG,
+                  "bias must be 16-byte aligned with strides that are multiples of 4");
+    if (p->bias_cols <= 0) return fail(MI_ATTN_ERR_INVALID_ARG, "bias_cols must be > 0");
+  }
+
+  int32_t bm = 0, bn = 0;
+  if (mi_attn_tile_shape(dt, p->d_qk, p->d_v, &bm, &bn) != MI_ATTN_OK) return MI_ATTN_ERR_UNSUPPORTED;
+  const int64_t n_qtiles = (p->max_seqlen_q + bm - 1) / bm;
+  const int64_t grid_x = (int64_t)p->hq * p->num_seqs;
+  if (grid_x > INT32_MAX || n_qtiles > 65535)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "problem too large for one launch (hq*num_seqs=%lld, "
+                "q tiles=%lld)", (long long)grid_x, (long long)n_qtiles);
+
+  if (env_flag("MI_ATTN_VALIDATE")) {
+    int rc = validate_cu(p->cu_seqlens_q, p->num_seqs, p->total_q, p->max_seqlen_q, "cu_seqlens_q");
+    if (rc != MI_ATTN_OK) return rc;
+    rc = validate_cu(p->cu_seqlens_kv, p->num_seqs, p->total_kv, has_bias ? p->bias_cols : -1,
+                     "cu_seqlens_kv");
+    if (rc != MI_ATTN_OK) return rc;
+  }
+
+  mi_attn::KernelArgs a{};
+  a.q = p->q;
+  a.k = p->k;
+  a.v = p->v;
+  a.out = p->out;
+  a.lse = p->lse;
+  a.cu_q = p->cu_seqlens_q;
+  a.cu_kv = p->cu_seqlens_kv;
+  a.bias = p->bias;
+  a.tile_counts = p->tile_counts;
+  a.q_st = p->q_stride_tok;
+  a.q_sh = p->q_stride_head;
+  a.k_st = p->k_stride_tok;
+  a.k_sh = p->k_stride_head;
+  a.v_st = p->v_stride_tok;
+  a.v_sh = p->v_stride_head;
+  a.o_st = p->out_stride_tok;
+  a.o_sh = p->out_stride_head;
+  a.b_st = has_bias ? p->bias_stride_tok : 0;
+  a.b_sh = has_bias ? p->bias_stride_head : 0;
+  a.total_q = p->total_q;
+  a.num_seqs = (int32_t)p->num_seqs;
+  a.hq = p->hq;
+  a.group = p->hq / p->hkv;
+  a.bias_heads = has_bias ? p->bias_heads : 1;
+  a.causal = p->causal;
+  a.window = p->window;
+  a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  a.split_keys = dt == MI_ATTN_BF16 ? kSplitKeysBf16 : (dt == MI_ATTN_F16 ? kSplitKeysF16 : 0);
+  a.split_bias = (has_bias && dt == MI_ATTN_BF16) ? 1 : 0;
+
+  const dim3 grid((unsigned)grid_x, (unsigned)n_qtiles);
+  hipError_t e = mi_attn::launch_attn_fwd(a, dt, p->out_dtype, p->d_qk, p->d_v, has_bias, grid,
+                                          reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return MI_ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+/*
+ * mi_attn — fused variable-length attention forward for AMD MI355X (gfx950).
+ *
+ * C ABI.  No HIP or PyTorch types appear in the signatures: device buffers
+ * are plain pointers, sizes and strides are integers, the stream is an
+ * opaque pointer (a hipStream_t, NULL for the default stream).
+ *
+ * The operation (mtlattn 0.3.0 project page, section "Use"):
+ *   packed ragged q [total_q, hq, d_qk], k [total_kv, hkv, d_qk],
+ *   v [total_kv, hkv, d_v]; sequence s owns q rows cu_seqlens_q[s] ..
+ *   cu_seqlens_q[s+1]-1 and kv rows cu_seqlens_kv[s] .. cu_seqlens_kv[s+1]-1;
+ *   query head h reads kv head h / (hq / hkv) (GQA / MQA);
+ *   logit(i, j) = scale * (q_i . k_j) + bias[global row of i][h or 0][j];
+ *   causal: local query i sees local key j iff j <= i + (Lk - Lq)
+ *   (end-aligned, so self-attention and cached decode both hold);
+ *   window W > 0 (with causal): additionally j > i + (Lk - Lq) - W, i.e. the
+ *   last W keys up to that diagonal;
+ *   out_i = sum_j softmax_j(logit(i, .)) v_j over the visible keys whose
+ *   logit is not -inf, and lse_i = ln sum_j exp(logit(i, j)) (natural log).
+ *   A row with no such key gets out = 0 and lse = -inf.
+ * The softmax is streamed over key tiles with fp32 running max and sum
+ * (triton-msl part-1 post, section "What works, and where the edges are";
+ * mtlattn page, section "Notes": fp32 accumulation for every input dtype);
+ * no Lq x Lk matrix is ever stored.
+ *
+ * Supported set (anything else is refused, nothing is launched):
+ *   (d_qk, d_v) in {(64,64), (128,128), (192,128)}; bf16 / fp16 inputs for
+ *   all three, fp32 inputs for (64,64) and (128,128);
+ *   out dtype = input dtype or fp32; hq % hkv == 0; window > 0 needs causal.
+ * The refusal follows the correct-or-refuse contract on the triton-msl
+ * part-1 post (section "Correct-or-refuse"): an unsupported request returns
+ * an error code and a reason, never a plausible wrong answer.
+ */
+#ifndef MI_ATTN_H
+#define MI_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MI_ATTN_VERSION 100 /* 1.0.0 */
+
+/* Return codes.  On any error nothing is launched and out / lse are untouched. */
+enum {
+  MI_ATTN_OK = 0,
+  MI_ATTN_ERR_INVALID_ARG = -1, /* malformed arguments (null pointer, bad size, misalignment) */
+  MI_ATTN_ERR_UNSUPPORTED = -2, /* well-formed but outside the supported set */
+  MI_ATTN_ERR_LAUNCH = -3,      /* the HIP runtime rejected the launch */
+  MI_ATTN_ERR_VALIDATION = -4   /* MI_ATTN_VALIDATE=1 found a bad cu_seqlens / size contract */
+};
+
+/* Element types. */
+enum { MI_ATTN_F32 = 0, MI_ATTN_F16 = 1, MI_ATTN_BF16 = 2 };
+
+/*
+ * Arguments of one forward call.  Set struct_size = sizeof(mi_attn_fwd_params)
+ * so the struct can grow without breaking callers.
+ *
+ * Pointers (all device memory, owned by the caller; the library keeps none
+ * of them after the call returns and allocates nothing):
+ *   q, k, v      input tensors, element type in_dtype, last dim contiguous,
+ *                16-byte aligned.
+ *   out          [total_q, hq, d_v] output, element type out_dtype, last dim
+ *                contiguous, 16-byte aligned.  Written for every row of every
+ *                sequence.
+ *   lse          [hq, total_q] fp32, row h contiguous (element h*total_q + t);
+ *                may be NULL.
+ *   cu_seqlens_q, cu_seqlens_kv   int32 [num_seqs + 1], cumulative lengths.
+ *   bias         optional fp32 additive bias [total_q, bias_heads, bias_cols]
+ *                addressed as bias[t*bias_stride_tok + hb*bias_stride_head + j]
+ *                with t the global query row, hb = 0 if bias_heads == 1 else
+ *                the query head, j the key position inside its sequence;
+ *                16-byte aligned, strides multiples of 4.  Values must be
+ *                finite or -inf.
+ *   tile_counts  optional int32 [hq * num_seqs * n_qtiles] (debug): for every
+ *                workgroup, the number of key tiles its loop visited, at
+ *                index (qtile * num_seqs + seq) * hq + head, where
+ *                n_qtiles = ceil(max_seqlen_q / BM) and BM, BN come from
+ *                mi_attn_tile_shape.  NULL in normal use.
+ *
+ * Sizes: num_seqs >= 0, max_seqlen_q >= every sequence's query length,
+ * total_q / total_kv = cu_seqlens_q[num_seqs] / cu_seqlens_kv[num_seqs],
+ * bias_cols >= every sequence's key length.
+ * Strides are in elements (not bytes); *_stride_tok between consecutive
+ * tokens, *_stride_head between consecutive heads; each must be a multiple
+ * of 8 elements for 16-bit types and of 4 for fp32.
+ *
+ * The device-side contracts (cu_seqlens non-decreasing from 0 to total,
+ * lengths within max_seqlen_q / bias_cols) are the caller's; with the
+ * environment variable MI_ATTN_VALIDATE=1 the library copies both
+ * cu_seqlens arrays to the host (synchronously) and refuses violations.
+ */
+typedef struct mi_attn_fwd_params {
+  size_t struct_size;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_kv;
+  const float* bias;
+  int32_t* tile_counts;
+  int64_t num_seqs;
+  int64_t max_seqlen_q;
+  int64_t total_q;
+  int64_t total_kv;
+  int32_t hq, hkv, d_qk, d_v;
+  int64_t q_stride_tok, q_stride_head;
+  int64_t k_stride_tok, k_stride_head;
+  int64_t v_stride_tok, v_stride_head;
+  int64_t out_stride_tok, out_stride_head;
+  int32_t bias_heads; /* 1 or hq; ignored when bias is NULL */
+  int64_t bias_cols;
+  int64_t bias_stride_tok, bias_stride_head;
+  int32_t in_dtype;  /* MI_ATTN_F32 / F16 / BF16 */
+  int32_t out_dtype; /* in_dtype or MI_ATTN_F32 */
+  float scale;       /* softmax scale, e.g. 1/sqrt(d_qk) */
+  int32_t causal;    /* 0 or 1 */
+  int32_t window;    /* 0 = none, else W >= 1 (requires causal) */
+} mi_attn_fwd_params;
+
+/*
+ * Enqueue the forward pass on `stream` (a hipStream_t; NULL = default
+ * stream) and return without waiting: results are visible in stream order,
+ * as the mtlattn page's section "Notes" describes for its own stream.
+ * Returns MI_ATTN_OK or a negative code; mi_attn_last_error() then says why.
+ * Re-entrant and thread-safe; the run is bitwise deterministic (fixed
+ * reduction order, no atomics).
+ */
+int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream);
+
+/* Reason for the last non-OK return on the calling thread ("" if none). */
+const char* mi_attn_last_error(void);
+
+/* MI_ATTN_VERSION of the built library. */
+int mi_attn_version(void);
+
+/*
+ * Tile shape the kernel uses for (in_dtype, d_qk, d_v): *bm query rows per
+ * workgroup and *bn keys per key tile.  Returns MI_ATTN_OK, or
+ * MI_ATTN_ERR_UNSUPPORTED for a combination outside the supported set.
+ */
+int mi_attn_tile_shape(int32_t in_dtype, int32_t d_qk, int32_t d_v, int32_t* bm, int32_t* bn);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI_ATTN_H */

@@ -1,0 +1,133 @@
+"""The C-ABI library loads, exports every symbol include/mi_attn.h declares,
+its params struct matches the ctypes mirror, and host-side validation refuses
+malformed or unsupported calls before touching the GPU (CPU only)."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import flash_attention_varlen_amd as fav
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mi_attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert names == ["mi_attn_last_error", "mi_attn_tile_shape", "mi_attn_varlen_fwd",
+                     "mi_attn_version"]
+    lib = fav.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fav.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (mi_attn_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_version_and_tile_shape():
+    assert fav.mi_attn_version() == 100
+    assert fav.mi_attn_tile_shape(fav.BF16, 128, 128) == (128, 64)
+    assert fav.mi_attn_tile_shape(fav.F16, 192, 128) == (128, 64)
+    assert fav.mi_attn_tile_shape(fav.F32, 64, 64) == (128, 32)
+    with pytest.raises(fav.MiAttnError):
+        fav.mi_attn_tile_shape(fav.F32, 192, 128)
+    with pytest.raises(fav.MiAttnError):
+        fav.mi_attn_tile_shape(fav.BF16, 96, 96)
+
+
+def test_struct_layout_matches_header():
+    fields = [f[0] for f in fav.MiAttnFwdParams._fields_]
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"mi_attn.h\"\nint main(void){\n"
+    src += 'printf("%zu\\n", sizeof(mi_attn_fwd_params));\n'
+    for f in fields:
+        src += f'printf("%zu\\n", offsetof(mi_attn_fwd_params, {f}));\n'
+    src += "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                               check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(fav.MiAttnFwdParams)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(fav.MiAttnFwdParams, f).offset == off, f
+
+
+def _valid_params():
+    p = fav.MiAttnFwdParams()
+    fake = 1 << 20  # aligned non-null addresses; never dereferenced by refused calls
+    p.q = p.k = p.v = p.out = fake
+    p.cu_seqlens_q = p.cu_seqlens_kv = fake
+    p.num_seqs, p.max_seqlen_q, p.total_q, p.total_kv = 2, 64, 100, 100
+    p.hq, p.hkv, p.d_qk, p.d_v = 8, 2, 128, 128
+    p.q_stride_tok, p.q_stride_head = 8 * 128, 128
+    p.k_stride_tok, p.k_stride_head = 2 * 128, 128
+    p.v_stride_tok, p.v_stride_head = 2 * 128, 128
+    p.out_stride_tok, p.out_stride_head = 8 * 128, 128
+    p.in_dtype = p.out_dtype = fav.BF16
+    p.scale = 0.088
+    return p
+
+
+REFUSALS = {
+    "bad_dtype": (dict(in_dtype=7), fav.ERR_UNSUPPORTED),
+    "bad_out_dtype": (dict(out_dtype=fav.F16), fav.ERR_UNSUPPORTED),
+    "head_dims": (dict(d_qk=96, d_v=96), fav.ERR_UNSUPPORTED),
+    "f32_latent": (dict(in_dtype=fav.F32, out_dtype=fav.F32, d_qk=192, d_v=128), fav.ERR_UNSUPPORTED),
+    "gqa_ratio": (dict(hq=6, hkv=4), fav.ERR_UNSUPPORTED),
+    "zero_heads": (dict(hkv=0), fav.ERR_INVALID_ARG),
+    "window_without_causal": (dict(window=16), fav.ERR_UNSUPPORTED),
+    "negative_window": (dict(window=-1, causal=1), fav.ERR_INVALID_ARG),
+    "bad_causal": (dict(causal=2), fav.ERR_INVALID_ARG),
+    "negative_size": (dict(total_q=-1), fav.ERR_INVALID_ARG),
+    "null_q": (dict(q=None), fav.ERR_INVALID_ARG),
+    "null_cu": (dict(cu_seqlens_kv=None), fav.ERR_INVALID_ARG),
+    "misaligned_q": (dict(q=(1 << 20) + 8), fav.ERR_INVALID_ARG),
+    "odd_stride": (dict(k_stride_tok=2 * 128 + 4), fav.ERR_INVALID_ARG),
+    "nan_scale": (dict(scale=float("nan")), fav.ERR_INVALID_ARG),
+    "zero_scale": (dict(scale=0.0), fav.ERR_UNSUPPORTED),
+    "bias_heads": (dict(bias=1 << 20, bias_heads=3, bias_cols=64, bias_stride_tok=8 * 64,
+                        bias_stride_head=64), fav.ERR_UNSUPPORTED),
+    "bias_stride": (dict(bias=1 << 20, bias_heads=1, bias_cols=64, bias_stride_tok=66,
+                         bias_stride_head=0), fav.ERR_INVALID_ARG),
+    "too_many_q_tiles": (dict(max_seqlen_q=128 * 65536), fav.ERR_UNSUPPORTED),
+}
+
+
+@pytest.mark.parametrize("name", sorted(REFUSALS))
+def test_host_validation_refuses(name):
+    changes, code = REFUSALS[name]
+    p = _valid_params()
+    for k, v in changes.items():
+        setattr(p, k, v)
+    with pytest.raises(fav.MiAttnError) as ei:
+        fav.mi_attn_varlen_fwd(p, 0)
+    assert ei.value.code == code, fav.mi_attn_last_error()
+    assert fav.mi_attn_last_error() != ""
+
+
+def test_short_struct_is_refused():
+    p = _valid_params()
+    lib = fav.load_library()
+    p.struct_size = 8
+    assert lib.mi_attn_varlen_fwd(ctypes.byref(p), None) == fav.ERR_INVALID_ARG
+
+
+def test_empty_problem_is_a_no_op():
+    p = _valid_params()
+    p.num_seqs = 0
+    fav.mi_attn_varlen_fwd(p, 0)
+    p = _valid_params()
+    p.total_q = 0
+    fav.mi_attn_varlen_fwd(p, 0)
