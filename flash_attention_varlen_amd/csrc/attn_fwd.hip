@@ -42,6 +42,12 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt in 6:4, lgkmcnt in 11:8): wait for vmcnt == 0 / lgkmcnt == 0 only.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -545,9 +551,421 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
   }
 }
 
+// ----------------------------------------------------------------------------
+// 16-bit kernel with direct HBM -> LDS staging.
+//
+// K and V tiles are copied by buffer_load ... lds: lane i of each wave-wide
+// load writes 16 bytes at LDS base + 16 i, so the tile layout in LDS is
+// chosen by which (key, 16-byte chunk) each lane fetches.  Loads past the
+// end of the sequence fall outside the buffer's byte range and come back as
+// zeros.  Chunks are XOR-swizzled per key so that the MFMA operand reads
+// (K as 16-byte rows, V through the transposing 8-byte read) hit 16
+// different 16-byte bank groups.
+// ----------------------------------------------------------------------------
+template <int D>
+struct KSwz {
+  // 16-byte-chunk swizzle of K rows: D=128 rows are 256 B (all 64 banks), so
+  // 16 consecutive keys take 16 distinct chunk slots; 128 B / 384 B rows
+  // alternate bank halves with key parity, so pairs of keys share a pattern.
+  __device__ static int f(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
+};
+template <int D>
+struct VSwz {
+  // V rows are read four keys at a time by the transposing read; the four
+  // keys must land in four different 4-chunk groups.
+  __device__ static int f(int key) { return D == 128 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2); }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // word 3 = 0x00020000: raw (untyped) dword access, no swizzle, no stride.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy one 64-key tile of K and V (rows [kb, kb + rows) of this sequence
+// and kv head) into LDS at kdst (this wave's 1 KB slice of the K tile; the
+// V tile follows K_BYTES later).  Device-only: the buffer-resource builtins
+// have no host form.
+template <int DQK, int DV, int KLOADS, int VLOADS>
+__device__ __forceinline__ void load_kv_tile(const char* kbase, const char* vbase, int64_t k_st_b,
+                                             int64_t v_st_b, int kb, int rows, lds_char* kdst,
+                                             int k_bytes, const uint32_t* koff,
+                                             const uint32_t* voff) {
+  const __amdgpu_buffer_rsrc_t kr =
+      make_rsrc(kbase + kb * k_st_b, (uint32_t)((rows - 1) * k_st_b + DQK * 2));
+  const __amdgpu_buffer_rsrc_t vr =
+      make_rsrc(vbase + kb * v_st_b, (uint32_t)((rows - 1) * v_st_b + DV * 2));
+  lds_char* vdst = kdst + k_bytes;
+#pragma unroll
+  for (int i = 0; i < KLOADS; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + i * kThreads * 16), 16, koff[i],
+                                             0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < VLOADS; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + i * kThreads * 16), 16, voff[i],
+                                             0, 0, 0);
+}
+
+template <typename T, int DQK, int DV, bool BIAS, typename OutT>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(const KernelArgs a) {
+  using E = Elem<T>;
+  constexpr int BN = 64;            // keys per tile
+  constexpr int KRB = DQK * 2;      // K row bytes in LDS
+  constexpr int VRB = DV * 2;       // V row bytes in LDS (row-major, keys x d)
+  constexpr int KCPR = DQK / 8;     // 16-byte chunks per K row
+  constexpr int VCPR = DV / 8;
+  constexpr int K_BYTES = BN * KRB;
+  constexpr int V_BYTES = BN * VRB;
+  constexpr int STAGE = K_BYTES + V_BYTES;
+  constexpr int KLOADS = K_BYTES / (kThreads * 16);  // direct loads per thread per tile
+  constexpr int VLOADS = V_BYTES / (kThreads * 16);
+  constexpr int KSTEPS = DQK / 16;  // MFMA k-steps of S^T = K Q^T
+  constexpr int NDB = DV / 32;      // 32-row blocks of O^T
+  constexpr int OUT_RB = DV * (int)sizeof(OutT);  // epilogue row bytes
+  constexpr int OUT_CPR = OUT_RB / 16;
+  static_assert(K_BYTES % (kThreads * 16) == 0 && V_BYTES % (kThreads * 16) == 0, "tile loads");
+  static_assert(4 * 32 * OUT_RB <= 2 * STAGE, "epilogue staging must fit in the K/V buffers");
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // Scalar wave index: every per-wave condition below is a uniform scalar
+  // branch.  MFMA writes all 64 lanes whatever EXEC holds, so an MFMA must
+  // never sit in a branch the compiler could run with a partial EXEC mask.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5;
+  const int l32 = lane & 31;
+
+  // ---- work decode.  blockIdx.y counts query tiles from the end of each
+  // sequence (longest causal rows first).  Within one (sequence, tile) slab
+  // the query heads are ordered so that the heads dispatched to one XCD
+  // (consecutive workgroups go round-robin over 8 XCDs) are neighbours, i.e.
+  // mostly share their kv head and hit the same L2.
+  const int hx = blockIdx.x % a.hq;
+  const int seq = blockIdx.x / a.hq;
+  int head = hx;
+  if ((a.hq & 7) == 0) {
+    const int per_xcd = a.hq >> 3;
+    head = (hx & 7) * per_xcd + (hx >> 3);
+  }
+  const int cq0 = a.cu_q[seq];
+  const int lq = a.cu_q[seq + 1] - cq0;
+  const int ck0 = a.cu_kv[seq];
+  const int lk = a.cu_kv[seq + 1] - ck0;
+  const int n_qtiles = (lq + kBM - 1) / kBM;
+  const int qtile = n_qtiles - 1 - (int)blockIdx.y;
+  if (qtile < 0) return;
+
+  const int r0 = qtile * kBM;
+  const int r1 = min(lq, r0 + kBM);
+  const int off = lk - lq;
+  const int g = head / a.group;
+  const bool causal = a.causal != 0;
+  const int W = a.window;
+
+  int kv_hi = lk;
+  if (causal) kv_hi = min(lk, r1 - 1 + off + 1);
+  int kv_lo = 0;
+  if (W > 0) kv_lo = max(0, r0 + off - W + 1);
+  const int t_begin = kv_lo / BN;
+  int t_end = kv_hi > 0 ? (kv_hi + BN - 1) / BN : 0;
+  if (t_end < t_begin) t_end = t_begin;
+
+  if (a.tile_counts != nullptr && tid == 0 && qtile < (int)gridDim.y)
+    a.tile_counts[((int64_t)qtile * a.num_seqs + seq) * a.hq + head] = t_end - t_begin;
+
+  const int w0 = r0 + wave * 32;
+  const int w1 = min(lq, w0 + 32);
+  const bool wave_active = w0 < lq;
+  const int my_row = w0 + l32;
+  const bool row_ok = my_row < lq;
+  int wkv_hi = lk;
+  if (causal) wkv_hi = min(lk, w1 - 1 + off + 1);
+  int wkv_lo = 0;
+  if (W > 0) wkv_lo = max(0, w0 + off - W + 1);
+  bool split;
+  {
+    const int nvis = (causal ? min(lk, w0 + off + 1) : lk) - wkv_lo;
+    split = (nvis < a.split_keys) || (BIAS && a.split_bias != 0);
+  }
+
+  const int64_t k_st_b = a.k_st * 2;
+  const int64_t v_st_b = a.v_st * 2;
+  const char* kbase = reinterpret_cast<const char*>(a.k) + ((int64_t)ck0 * a.k_st + (int64_t)g * a.k_sh) * 2;
+  const char* vbase = reinterpret_cast<const char*>(a.v) + ((int64_t)ck0 * a.v_st + (int64_t)g * a.v_sh) * 2;
+
+  // Per-lane byte offsets (within a tile, from its first key) of the chunks
+  // this lane copies; the same for every tile.
+  uint32_t koff[KLOADS];
+  uint32_t voff[VLOADS];
+#pragma unroll
+  for (int i = 0; i < KLOADS; ++i) {
+    const int pos = i * kThreads + tid;  // 16-byte slot in the LDS tile
+    const int key = pos / KCPR;
+    const int c = (pos % KCPR) ^ KSwz<DQK>::f(key);
+    koff[i] = (uint32_t)(key * k_st_b + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < VLOADS; ++i) {
+    const int pos = i * kThreads + tid;
+    const int key = pos / VCPR;
+    const int c = (pos % VCPR) ^ VSwz<DV>::f(key);
+    voff[i] = (uint32_t)(key * v_st_b + c * 16);
+  }
+
+  auto load_tile = [&](int t, int buf) __attribute__((device)) {
+    load_kv_tile<DQK, DV, KLOADS, VLOADS>(kbase, vbase, k_st_b, v_st_b, t * BN, min(lk - t * BN, BN),
+                                         (lds_char*)smem + buf * STAGE + wave * 1024, K_BYTES, koff,
+                                         voff);
+  };
+
+  // ---- Q fragments (B operand of S^T = K Q^T), loaded once.
+  u32x4_t qf[KSTEPS];
+  {
+    const T* qp = reinterpret_cast<const T*>(a.q) + (int64_t)(cq0 + my_row) * a.q_st +
+                  (int64_t)head * a.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qf[ks] = row_ok ? *reinterpret_cast<const u32x4_t*>(qp + 16 * ks + 8 * hf)
+                      : (u32x4_t){0u, 0u, 0u, 0u};
+  }
+
+  // LDS byte offsets of this lane's operand reads (tile-relative).
+  // K: key 32 mb + l32, chunk 2 ks + hf.
+  // V (transposing read r of k-step kk, d-block db): key 16 kk + 8 r + 4 hf +
+  // (lane % 16) / 4, head dims 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4) .. +3.
+  const int vkey_lane = 4 * hf + ((lane & 15) >> 2);
+  const int vchunk_lane = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vbyte_lane = (lane & 1) * 8;
+
+  f32x16_t o[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
+  float m_run = kNegInf;
+  float l_run = 0.0f;
+  const float c_scale = a.scale_log2;
+  const float* brow = nullptr;
+  if constexpr (BIAS) {
+    brow = a.bias + (int64_t)(cq0 + (row_ok ? my_row : 0)) * a.b_st +
+           (int64_t)(a.bias_heads == 1 ? 0 : head) * a.b_sh;
+  }
+
+  if (t_begin < t_end) load_tile(t_begin, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = (t - t_begin) & 1;
+    if (t + 1 < t_end) load_tile(t + 1, buf ^ 1);
+
+    const int kb = t * BN;
+    const bool wave_tile = wave_active && kb < wkv_hi && kb + BN > wkv_lo;
+    if (wave_tile) {
+      const lds_char* ks = (const lds_char*)smem + buf * STAGE;
+      const lds_char* vs = ks + K_BYTES;
+
+      f32x16_t s[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[mb][e] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int key = 32 * mb + l32;
+          const int c = (2 * kk + hf) ^ KSwz<DQK>::f(key);
+          const u32x4_t kf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+              ks + key * KRB + c * 16);
+          s[mb] = E::mma(kf, qf[kk], s[mb]);
+        }
+      }
+
+      const bool need_mask = (kb + BN > lk) || (causal && kb + BN - 1 > w0 + off) ||
+                             (W > 0 && kb <= w1 - 1 + off - W);
+      if (need_mask) {
+        const int lim_hi = causal ? my_row + off : lk - 1;
+        const int lim_lo = W > 0 ? my_row + off - W : -1;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kb + 32 * mb + 8 * (e >> 2) + 4 * hf + (e & 3);
+            const bool ok = key < lk && key <= lim_hi && key > lim_lo;
+            s[mb][e] = ok ? s[mb][e] : kNegInf;
+          }
+      }
+
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int key0 = kb + 32 * mb + 8 * qd + 4 * hf;
+            f32x4_t bv;
+            if (row_ok && key0 + 3 < lk) {
+              bv = *reinterpret_cast<const f32x4_t*>(brow + key0);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) bv[e] = (row_ok && key0 + e < lk) ? brow[key0 + e] : 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              s[mb][4 * qd + e] = __builtin_fmaf(s[mb][4 * qd + e], c_scale, bv[e] * kLog2e);
+          }
+      }
+
+      float mx = kNegInf;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_tile = BIAS ? mx : mx * c_scale;
+
+      // Per-row lazy rescale (alpha = 1 for rows whose max stayed within the
+      // threshold: exact, so a row never depends on its wave neighbours).
+      const bool grow = m_tile > m_run + kRescaleThreshold;
+      if (__ballot(grow) != 0ull) {
+        const float m_new = grow ? m_tile : m_run;
+        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+
+      float lsum = 0.0f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float x = BIAS ? s[mb][e] - m_use : __builtin_fmaf(s[mb][e], c_scale, -m_use);
+          const float p = fast_exp2(x);
+          s[mb][e] = p;
+          lsum += p;
+        }
+      l_run += lsum;
+
+      // P as the B operand: k-step kk takes S^T entries 8 (kk % 2) .. +7 of
+      // block kk / 2, i.e. keys 16 kk + {0..3, 8..11} + 4 hf; the transposing
+      // V reads fetch the same keys in the same order.
+      u32x4_t ph[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int mb = kk >> 1, b8 = 8 * (kk & 1);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ph[kk][w] = E::pack(s[mb][b8 + 2 * w], s[mb][b8 + 2 * w + 1]);
+      }
+      auto vfrag = [&](int kk, int db) -> u32x4_t {
+        u32x4_t r;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int key = 16 * kk + 8 * h + vkey_lane;
+          const int c = (4 * db + vchunk_lane) ^ VSwz<DV>::f(key);
+          const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16_t*)(vs + key * VRB + c * 16 + vbyte_lane));
+          const u32x2_t xw = __builtin_bit_cast(u32x2_t, x);
+          r[2 * h] = xw[0];
+          r[2 * h + 1] = xw[1];
+        }
+        return r;
+      };
+      if (split) {
+        u32x4_t pl[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int mb = kk >> 1, b8 = 8 * (kk & 1);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float x0 = s[mb][b8 + 2 * w], x1 = s[mb][b8 + 2 * w + 1];
+            pl[kk][w] = E::pack(x0 - E::round_trip(x0), x1 - E::round_trip(x1));
+          }
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const u32x4_t vf = vfrag(kk, db);
+            o[db] = E::mma(vf, ph[kk], o[db]);
+            o[db] = E::mma(vf, pl[kk], o[db]);
+          }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) o[db] = E::mma(vfrag(kk, db), ph[kk], o[db]);
+      }
+    }
+
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of tile t+1 have landed
+    __syncthreads();
+  }
+
+  // ---- epilogue: O / l staged through LDS (the K/V buffers are free after
+  // the loop's last barrier) so that every output row is written as
+  // contiguous 16-byte stores.
+  if (!wave_active) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  lds_char* ostage = (lds_char*)smem + wave * 32 * OUT_RB;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int d0 = 32 * db + 8 * qd + 4 * hf;
+      const float v0 = o[db][4 * qd] * inv, v1 = o[db][4 * qd + 1] * inv;
+      const float v2 = o[db][4 * qd + 2] * inv, v3 = o[db][4 * qd + 3] * inv;
+      const int byte = d0 * (int)sizeof(OutT);
+      const int c = (byte >> 4) ^ (l32 & (OUT_CPR - 1));
+      lds_char* dst = ostage + l32 * OUT_RB + c * 16 + (byte & 15);
+      if constexpr (sizeof(OutT) == 4) {
+        *(__attribute__((address_space(3))) f32x4_t*)dst = (f32x4_t){v0, v1, v2, v3};
+      } else {
+        *(__attribute__((address_space(3))) u32x2_t*)dst =
+            (u32x2_t){Elem<OutT>::pack(v0, v1), Elem<OutT>::pack(v2, v3)};
+      }
+    }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_wave_barrier();
+  {
+    constexpr int RPI = 64 / OUT_CPR;  // rows per wave-wide pass
+    const int cc = lane % OUT_CPR;
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int q = it * RPI + lane / OUT_CPR;
+      const int c = cc ^ (q & (OUT_CPR - 1));
+      const u32x4_t val = *(const __attribute__((address_space(3))) u32x4_t*)(ostage + q * OUT_RB + c * 16);
+      if (w0 + q < lq) {
+        char* dst = reinterpret_cast<char*>(a.out) +
+                    ((int64_t)(cq0 + w0 + q) * a.o_st + (int64_t)head * a.o_sh) * (int64_t)sizeof(OutT) +
+                    cc * 16;
+        *reinterpret_cast<u32x4_t*>(dst) = val;
+      }
+    }
+  }
+  if (a.lse != nullptr && hf == 0 && row_ok) {
+    const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+    a.lse[(int64_t)head * a.total_q + cq0 + my_row] =
+        l_tot > 0.0f ? (m_use + fast_log2(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
 template <typename T, int DQK, int DV, bool BIAS, typename OutT>
 hipError_t launch_one(const KernelArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, BIAS, OutT>), grid, dim3(kThreads), 0, stream, a);
+  if constexpr (Elem<T>::kWide) {
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, BIAS, OutT>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_fwd16_kernel<T, DQK, DV, BIAS, OutT>), grid, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -144,6 +144,15 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
       return fail(MI_ATTN_ERR_INVALID_ARG,
                   "q/k/v strides must be non-negative multiples of %lld elements (got %lld)",
                   (long long)in_mult, (long long)s);
+  if (p->k_stride_tok < p->d_qk || p->v_stride_tok < p->d_v)
+    return fail(MI_ATTN_ERR_UNSUPPORTED,
+                "k/v token strides must cover a full head row (k_stride_tok >= d_qk, "
+                "v_stride_tok >= d_v)");
+  // 16-bit K/V tiles are fetched through 32-bit buffer offsets spanning one
+  // 64-key tile.
+  if (dt != MI_ATTN_F32 &&
+      (p->k_stride_tok * elem_size(dt) * 64 > INT32_MAX || p->v_stride_tok * elem_size(dt) * 64 > INT32_MAX))
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "k/v token strides too large (more than 32 MiB per token)");
   if (p->out_stride_tok < 0 || p->out_stride_head < 0 || p->out_stride_tok % out_mult != 0 ||
       p->out_stride_head % out_mult != 0)
     return fail(MI_ATTN_ERR_INVALID_ARG, "out strides must be non-negative multiples of %lld",
