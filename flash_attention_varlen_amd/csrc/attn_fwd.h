@@ -9,7 +9,7 @@
 namespace mi_attn {
 
 constexpr int kThreads = 256;  // 4 wave64s per workgroup
-constexpr int kBM = 128;       // query rows per workgroup (32 per wave)
+constexpr int kBM = 128;       // query rows per workgroup of the fp32 kernel (32 per wave)
 
 // Element type codes (same values as the public MI_ATTN_F32 / F16 / BF16).
 constexpr int kF32 = 0;
@@ -41,8 +41,11 @@ struct KernelArgs {
   int32_t split_bias;  // with a bias, split P on every tile (16-bit types)
 };
 
-// Keys per tile for an input type.
-int tile_bn(int in_dtype);
+// Keys per tile for an input type and head dims.
+int tile_bn(int in_dtype, int dqk, int dv);
+
+// Query rows per workgroup for an input type and head dims.
+int tile_bm(int in_dtype, int dqk, int dv);
 
 // Launch on `stream`; grid = (hq * num_seqs, ceil(max_seqlen_q / kBM)).
 hipError_t launch_attn_fwd(const KernelArgs& a, int in_dtype, int out_dtype, int dqk, int dv,

@@ -584,51 +584,127 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Copy one 64-key tile of K and V (rows [kb, kb + rows) of this sequence
-// and kv head) into LDS at kdst (this wave's 1 KB slice of the K tile; the
-// V tile follows K_BYTES later).  Device-only: the buffer-resource builtins
-// have no host form.
-template <int DQK, int DV, int KLOADS, int VLOADS>
-__device__ __forceinline__ void load_kv_tile(const char* kbase, const char* vbase, int64_t k_st_b,
-                                             int64_t v_st_b, int kb, int rows, lds_char* kdst,
-                                             int k_bytes, const uint32_t* koff,
-                                             const uint32_t* voff) {
-  const __amdgpu_buffer_rsrc_t kr =
-      make_rsrc(kbase + kb * k_st_b, (uint32_t)((rows - 1) * k_st_b + DQK * 2));
-  const __amdgpu_buffer_rsrc_t vr =
-      make_rsrc(vbase + kb * v_st_b, (uint32_t)((rows - 1) * v_st_b + DV * 2));
-  lds_char* vdst = kdst + k_bytes;
+// Copy rows [kb, kb + rows) of one tensor's 64-key tile into LDS at dst
+// (this wave's 1 KB slice); rows past `rows` read as zeros.
+template <int D, int LOADS>
+__device__ __forceinline__ void load_tile_part(const char* base, int64_t st_b, int kb, int rows,
+                                               lds_char* dst, const uint32_t* off) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base + kb * st_b, (uint32_t)((rows - 1) * st_b + D * 2));
 #pragma unroll
-  for (int i = 0; i < KLOADS; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + i * kThreads * 16), 16, koff[i],
-                                             0, 0, 0);
-#pragma unroll
-  for (int i = 0; i < VLOADS; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + i * kThreads * 16), 16, voff[i],
-                                             0, 0, 0);
+  for (int i = 0; i < LOADS; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * kThreads * 16), 16, off[i], 0, 0, 0);
 }
 
+// ----------------------------------------------------------------------------
+// Software-pipelined 16-bit kernel.
+//
+// A wave owns NB blocks of 32 query rows (BM = 4 waves x 32 NB).  Every K
+// and V^T fragment read from LDS feeds NB MFMAs, one per query block.  Each
+// wave runs its key loop one tile ahead: the MFMAs of tile t+1's scores, the
+// PV MFMAs of tile t and tile t's softmax form one interleaved instruction
+// stream, with operand reads issued ahead of their MFMAs.  K and V have
+// separate double buffers so K(t+2) and V(t+1) stream in while tile t is
+// consumed.  Whether P is split into hi/lo halves is decided once per
+// workgroup (rows that see few keys), giving two straight-line variants.
+// ----------------------------------------------------------------------------
+
+// Compile-time order of one tile's stream: QK^T MFMAs of the next tile
+// (after the first kHead), PV MFMAs of this tile and the softmax chunks (one
+// chunk = one pair of scores of one query block).  Chunk q covers k-step
+// q / (4 NB), query block (q / 4) % NB, P word q % 4, so the P operand of
+// (k-step kk, block n) is complete after chunk (kk NB + n) 4 + 3.  PV MFMA
+// p uses V fragment p / NB (k-step (p / NB) / NDB, d-block (p / NB) % NDB)
+// for block p % NB.  MFMAs alternate between QK and PV where possible; one
+// chunk follows each MFMA until all are placed.
+enum : int { kOpQK = 0, kOpPV = 1, kOpChunk = 2 };
+
+template <int NQK, int NPV, int NB, int NDB, int NKS>
+struct StreamPlan {
+  static constexpr int kHead = NQK < 4 ? NQK : 4;
+  static constexpr int kChunks = 4 * NKS * NB;
+  static constexpr int kOps = (NQK - kHead) + NPV + kChunks;
+  struct Table {
+    int8_t op[kOps];
+    int8_t ix[kOps];
+  };
+  static constexpr int pv_needs(int p) {
+    return (((p / NB) / NDB) * NB + (p % NB)) * 4 + 4;
+  }
+  static constexpr Table build() {
+    Table t{};
+    int n = 0, qk = kHead, pv = 0, ch = 0;
+    bool last_pv = false;
+    while (qk < NQK || pv < NPV || ch < kChunks) {
+      const bool pv_ready = pv < NPV && ch >= pv_needs(pv);
+      bool mfma = false;
+      if (pv_ready && (qk >= NQK || !last_pv)) {
+        t.op[n] = kOpPV; t.ix[n] = (int8_t)pv++; ++n; last_pv = true; mfma = true;
+      } else if (qk < NQK) {
+        t.op[n] = kOpQK; t.ix[n] = (int8_t)qk++; ++n; last_pv = false; mfma = true;
+      }
+      if (ch < kChunks) {
+        t.op[n] = kOpChunk; t.ix[n] = (int8_t)ch++; ++n;
+      } else if (!mfma) {
+        break;  // unreachable: every PV MFMA is ready once all chunks are placed
+      }
+    }
+    return t;
+  }
+  static constexpr Table kTable = build();
+  static constexpr int op(int n) { return kTable.op[n]; }
+  static constexpr int index(int n) { return kTable.ix[n]; }
+};
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Per head-dim pair: NB query blocks of 32 rows per wave and NMB key
+// blocks of 32 keys per tile.
+template <int DQK, int DV>
+struct WaveBlocks {
+  static constexpr int NB = 1;
+  static constexpr int NMB = 2;
+};
+
 template <typename T, int DQK, int DV, bool BIAS, typename OutT>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(const KernelArgs a) {
+__global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) void attn_fwd16p_kernel(
+    const KernelArgs a) {
   using E = Elem<T>;
-  constexpr int BN = 64;            // keys per tile
-  constexpr int KRB = DQK * 2;      // K row bytes in LDS
-  constexpr int VRB = DV * 2;       // V row bytes in LDS (row-major, keys x d)
-  constexpr int KCPR = DQK / 8;     // 16-byte chunks per K row
+  // A row's running max m only moves when a tile's max exceeds it by more
+  // than this many powers of two, so p = exp2(x - m) stays below 2^64 for
+  // bf16 P (8 exponent bits, like fp32) and below 2^12 for fp16 P (max
+  // 65504); floating-point P and fp32 sums lose nothing to the stale max.
+  constexpr float kGrowBound = std::is_same<T, __bf16>::value ? 64.0f : 12.0f;
+  constexpr int NB = WaveBlocks<DQK, DV>::NB;
+  constexpr int NMB = WaveBlocks<DQK, DV>::NMB;
+  constexpr int RW = 32 * NB;  // query rows per wave
+  constexpr int BM = 4 * RW;   // query rows per workgroup
+  constexpr int BN = 32 * NMB; // keys per tile
+  constexpr int NKS = BN / 16; // PV k-steps per tile
+  constexpr int KRB = DQK * 2;
+  constexpr int VRB = DV * 2;
+  constexpr int KCPR = DQK / 8;
   constexpr int VCPR = DV / 8;
   constexpr int K_BYTES = BN * KRB;
   constexpr int V_BYTES = BN * VRB;
-  constexpr int STAGE = K_BYTES + V_BYTES;
-  constexpr int KLOADS = K_BYTES / (kThreads * 16);  // direct loads per thread per tile
+  constexpr int KLOADS = K_BYTES / (kThreads * 16);
   constexpr int VLOADS = V_BYTES / (kThreads * 16);
-  constexpr int KSTEPS = DQK / 16;  // MFMA k-steps of S^T = K Q^T
-  constexpr int NDB = DV / 32;      // 32-row blocks of O^T
-  constexpr int OUT_RB = DV * (int)sizeof(OutT);  // epilogue row bytes
+  constexpr int KSTEPS = DQK / 16;
+  constexpr int NDB = DV / 32;
+  constexpr int OUT_RB = DV * (int)sizeof(OutT);
   constexpr int OUT_CPR = OUT_RB / 16;
+  constexpr int KV_SMEM = 2 * (K_BYTES + V_BYTES);
+  constexpr int SMEM = KV_SMEM > 4 * 32 * OUT_RB ? KV_SMEM : 4 * 32 * OUT_RB;
   static_assert(K_BYTES % (kThreads * 16) == 0 && V_BYTES % (kThreads * 16) == 0, "tile loads");
-  static_assert(4 * 32 * OUT_RB <= 2 * STAGE, "epilogue staging must fit in the K/V buffers");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -642,8 +718,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(const KernelArg
   // ---- work decode.  blockIdx.y counts query tiles from the end of each
   // sequence (longest causal rows first).  Within one (sequence, tile) slab
   // the query heads are ordered so that the heads dispatched to one XCD
-  // (consecutive workgroups go round-robin over 8 XCDs) are neighbours, i.e.
-  // mostly share their kv head and hit the same L2.
+  // (consecutive workgroups go round-robin over 8 XCDs) are neighbours and
+  // mostly share their kv head, i.e. hit the same L2.
   const int hx = blockIdx.x % a.hq;
   const int seq = blockIdx.x / a.hq;
   int head = hx;
@@ -655,17 +731,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(const KernelArg
   const int lq = a.cu_q[seq + 1] - cq0;
   const int ck0 = a.cu_kv[seq];
   const int lk = a.cu_kv[seq + 1] - ck0;
-  const int n_qtiles = (lq + kBM - 1) / kBM;
+  const int n_qtiles = (lq + BM - 1) / BM;
   const int qtile = n_qtiles - 1 - (int)blockIdx.y;
   if (qtile < 0) return;
 
-  const int r0 = qtile * kBM;
-  const int r1 = min(lq, r0 + kBM);
+  const int r0 = qtile * BM;
+  const int r1 = min(lq, r0 + BM);
   const int off = lk - lq;
   const int g = head / a.group;
   const bool causal = a.causal != 0;
   const int W = a.window;
 
+  // Key range holding at least one visible key for rows [r0, r1).
   int kv_hi = lk;
   if (causal) kv_hi = min(lk, r1 - 1 + off + 1);
   int kv_lo = 0;
@@ -677,20 +754,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(const KernelArg
   if (a.tile_counts != nullptr && tid == 0 && qtile < (int)gridDim.y)
     a.tile_counts[((int64_t)qtile * a.num_seqs + seq) * a.hq + head] = t_end - t_begin;
 
-  const int w0 = r0 + wave * 32;
-  const int w1 = min(lq, w0 + 32);
+  const int w0 = r0 + wave * RW;
+  const int w1 = min(lq, w0 + RW);
   const bool wave_active = w0 < lq;
-  const int my_row = w0 + l32;
-  const bool row_ok = my_row < lq;
-  int wkv_hi = lk;
-  if (causal) wkv_hi = min(lk, w1 - 1 + off + 1);
-  int wkv_lo = 0;
-  if (W > 0) wkv_lo = max(0, w0 + off - W + 1);
-  bool split;
-  {
-    const int nvis = (causal ? min(lk, w0 + off + 1) : lk) - wkv_lo;
-    split = (nvis < a.split_keys) || (BIAS && a.split_bias != 0);
+  int my_row[NB];
+  bool row_ok[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    my_row[n] = w0 + 32 * n + l32;
+    row_ok[n] = my_row[n] < lq;
   }
+  // hi/lo split of P for the whole workgroup when its first row sees few keys
+  const int nvis0 = (causal ? min(lk, r0 + off + 1) : lk) - kv_lo;
+  const bool split = (nvis0 < a.split_keys) || (BIAS && a.split_bias != 0);
 
   const int64_t k_st_b = a.k_st * 2;
   const int64_t v_st_b = a.v_st * 2;
@@ -715,247 +791,354 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(const KernelArg
     const int c = (pos % VCPR) ^ VSwz<DV>::f(key);
     voff[i] = (uint32_t)(key * v_st_b + c * 16);
   }
-
-  auto load_tile = [&](int t, int buf) __attribute__((device)) {
-    load_kv_tile<DQK, DV, KLOADS, VLOADS>(kbase, vbase, k_st_b, v_st_b, t * BN, min(lk - t * BN, BN),
-                                         (lds_char*)smem + buf * STAGE + wave * 1024, K_BYTES, koff,
-                                         voff);
+  lds_char* const kbuf0 = (lds_char*)smem;
+  lds_char* const vbuf0 = (lds_char*)smem + 2 * K_BYTES;
+  auto load_k = [&](int t, int slot) __attribute__((device)) {
+    load_tile_part<DQK, KLOADS>(kbase, k_st_b, t * BN, min(lk - t * BN, BN),
+                                kbuf0 + slot * K_BYTES + wave * 1024, koff);
+  };
+  auto load_v = [&](int t, int slot) __attribute__((device)) {
+    load_tile_part<DV, VLOADS>(vbase, v_st_b, t * BN, min(lk - t * BN, BN),
+                               vbuf0 + slot * V_BYTES + wave * 1024, voff);
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T), loaded once.
-  u32x4_t qf[KSTEPS];
-  {
-    const T* qp = reinterpret_cast<const T*>(a.q) + (int64_t)(cq0 + my_row) * a.q_st +
+  u32x4_t qf[NB][KSTEPS];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const T* qp = reinterpret_cast<const T*>(a.q) + (int64_t)(cq0 + my_row[n]) * a.q_st +
                   (int64_t)head * a.q_sh;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
-      qf[ks] = row_ok ? *reinterpret_cast<const u32x4_t*>(qp + 16 * ks + 8 * hf)
-                      : (u32x4_t){0u, 0u, 0u, 0u};
+      qf[n][ks] = row_ok[n] ? *reinterpret_cast<const u32x4_t*>(qp + 16 * ks + 8 * hf)
+                            : (u32x4_t){0u, 0u, 0u, 0u};
   }
 
-  // LDS byte offsets of this lane's operand reads (tile-relative).
-  // K: key 32 mb + l32, chunk 2 ks + hf.
-  // V (transposing read r of k-step kk, d-block db): key 16 kk + 8 r + 4 hf +
-  // (lane % 16) / 4, head dims 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4) .. +3.
+  // V^T fragment (A operand of O^T += V^T P^T): two transposing reads of the
+  // row-major V tile.  Read h of k-step kk, d-block db gives this lane keys
+  // 16 kk + 8 h + 4 hf + k (k = 0..3) at head dim 32 db + lane % 32.
   const int vkey_lane = 4 * hf + ((lane & 15) >> 2);
   const int vchunk_lane = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int vbyte_lane = (lane & 1) * 8;
+  auto vfrag = [&](const lds_char* vt, int kk, int db) __attribute__((device)) -> u32x4_t {
+    u32x4_t r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int key = 16 * kk + 8 * h + vkey_lane;
+      const int c = (4 * db + vchunk_lane) ^ VSwz<DV>::f(key);
+      const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16_t*)(vt + key * VRB + c * 16 + vbyte_lane));
+      const u32x2_t xw = __builtin_bit_cast(u32x2_t, x);
+      r[2 * h] = xw[0];
+      r[2 * h + 1] = xw[1];
+    }
+    return r;
+  };
 
-  f32x16_t o[NDB];
+  f32x16_t o[NB][NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i)
+  for (int n = 0; n < NB; ++n)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
-  float m_run = kNegInf;
-  float l_run = 0.0f;
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[n][i][e] = 0.0f;
+  float m_run[NB];
+  float l_run[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    m_run[n] = kNegInf;  // running max, log2 units (scale folded in)
+    l_run[n] = 0.0f;     // this lane's share of the running sum
+  }
   const float c_scale = a.scale_log2;
-  const float* brow = nullptr;
+  const float* brow[NB];
   if constexpr (BIAS) {
-    brow = a.bias + (int64_t)(cq0 + (row_ok ? my_row : 0)) * a.b_st +
-           (int64_t)(a.bias_heads == 1 ? 0 : head) * a.b_sh;
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      brow[n] = a.bias + (int64_t)(cq0 + (row_ok[n] ? my_row[n] : 0)) * a.b_st +
+                (int64_t)(a.bias_heads == 1 ? 0 : head) * a.b_sh;
   }
 
-  if (t_begin < t_end) load_tile(t_begin, 0);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
-
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    if (t + 1 < t_end) load_tile(t + 1, buf ^ 1);
-
-    const int kb = t * BN;
-    const bool wave_tile = wave_active && kb < wkv_hi && kb + BN > wkv_lo;
-    if (wave_tile) {
-      const lds_char* ks = (const lds_char*)smem + buf * STAGE;
-      const lds_char* vs = ks + K_BYTES;
-
-      f32x16_t s[2];
+  // S^T = K Q^T for the whole K tile at kt (prologue only).
+  auto qk_all = [&](const lds_char* kt, f32x16_t (&s)[NB][NMB]) __attribute__((device)) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int n = 0; n < NB; ++n)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[mb][e] = 0.0f;
+      for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
+        for (int e = 0; e < 16; ++e) s[n][mb][e] = 0.0f;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const int key = 32 * mb + l32;
-          const int c = (2 * kk + hf) ^ KSwz<DQK>::f(key);
-          const u32x4_t kf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
-              ks + key * KRB + c * 16);
-          s[mb] = E::mma(kf, qf[kk], s[mb]);
-        }
+    for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int key = 32 * mb + l32;
+        const int c = (2 * kk + hf) ^ KSwz<DQK>::f(key);
+        const u32x4_t kf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+            kt + key * KRB + c * 16);
+#pragma unroll
+        for (int n = 0; n < NB; ++n) s[n][mb] = E::mma(kf, qf[n][kk], s[n][mb]);
       }
+  };
 
-      const bool need_mask = (kb + BN > lk) || (causal && kb + BN - 1 > w0 + off) ||
-                             (W > 0 && kb <= w1 - 1 + off - W);
-      if (need_mask) {
-        const int lim_hi = causal ? my_row + off : lk - 1;
-        const int lim_lo = W > 0 ? my_row + off - W : -1;
+  // Mask (boundary tiles only) and bias the raw scores of tile t, then take
+  // each row's max; returns true when some row's max exceeds its running max
+  // by more than the growth bound (m_pend holds the new maxima).  A row whose
+  // running max is still -inf (nothing visible yet: O and l are zero) simply
+  // adopts the new max.
+  auto prep_tile = [&](int t, f32x16_t (&sc)[NB][NMB], float (&m_pend)[NB]) __attribute__((device)) -> bool {
+    const int kb = t * BN;
+    const bool need_mask = (kb + BN > lk) || (causal && kb + BN - 1 > w0 + off) ||
+                           (W > 0 && kb <= w1 - 1 + off - W);
+    if (need_mask) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+      for (int n = 0; n < NB; ++n) {
+        const int lim_hi = causal ? my_row[n] + off : lk - 1;
+        const int lim_lo = W > 0 ? my_row[n] + off - W : -1;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = kb + 32 * mb + 8 * (e >> 2) + 4 * hf + (e & 3);
             const bool ok = key < lk && key <= lim_hi && key > lim_lo;
-            s[mb][e] = ok ? s[mb][e] : kNegInf;
+            sc[n][mb][e] = ok ? sc[n][mb][e] : kNegInf;
           }
       }
-
-      if constexpr (BIAS) {
+    }
+    if constexpr (BIAS) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
           for (int qd = 0; qd < 4; ++qd) {
             const int key0 = kb + 32 * mb + 8 * qd + 4 * hf;
             f32x4_t bv;
-            if (row_ok && key0 + 3 < lk) {
-              bv = *reinterpret_cast<const f32x4_t*>(brow + key0);
+            if (row_ok[n] && key0 + 3 < lk) {
+              bv = *reinterpret_cast<const f32x4_t*>(brow[n] + key0);
             } else {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) bv[e] = (row_ok && key0 + e < lk) ? brow[key0 + e] : 0.0f;
+              for (int e = 0; e < 4; ++e) bv[e] = (row_ok[n] && key0 + e < lk) ? brow[n][key0 + e] : 0.0f;
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              s[mb][4 * qd + e] = __builtin_fmaf(s[mb][4 * qd + e], c_scale, bv[e] * kLog2e);
+              sc[n][mb][4 * qd + e] = __builtin_fmaf(sc[n][mb][4 * qd + e], c_scale, bv[e] * kLog2e);
           }
-      }
-
+    }
+    bool grow = false;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
       float mx = kNegInf;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[n][mb][e]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_tile = BIAS ? mx : mx * c_scale;
-
-      // Per-row lazy rescale (alpha = 1 for rows whose max stayed within the
-      // threshold: exact, so a row never depends on its wave neighbours).
-      const bool grow = m_tile > m_run + kRescaleThreshold;
-      if (__ballot(grow) != 0ull) {
-        const float m_new = grow ? m_tile : m_run;
-        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < NDB; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
-
-      float lsum = 0.0f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float x = BIAS ? s[mb][e] - m_use : __builtin_fmaf(s[mb][e], c_scale, -m_use);
-          const float p = fast_exp2(x);
-          s[mb][e] = p;
-          lsum += p;
-        }
-      l_run += lsum;
-
-      // P as the B operand: k-step kk takes S^T entries 8 (kk % 2) .. +7 of
-      // block kk / 2, i.e. keys 16 kk + {0..3, 8..11} + 4 hf; the transposing
-      // V reads fetch the same keys in the same order.
-      u32x4_t ph[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int mb = kk >> 1, b8 = 8 * (kk & 1);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) ph[kk][w] = E::pack(s[mb][b8 + 2 * w], s[mb][b8 + 2 * w + 1]);
-      }
-      auto vfrag = [&](int kk, int db) -> u32x4_t {
-        u32x4_t r;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int key = 16 * kk + 8 * h + vkey_lane;
-          const int c = (4 * db + vchunk_lane) ^ VSwz<DV>::f(key);
-          const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4i16_t*)(vs + key * VRB + c * 16 + vbyte_lane));
-          const u32x2_t xw = __builtin_bit_cast(u32x2_t, x);
-          r[2 * h] = xw[0];
-          r[2 * h + 1] = xw[1];
-        }
-        return r;
-      };
-      if (split) {
-        u32x4_t pl[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int mb = kk >> 1, b8 = 8 * (kk & 1);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float x0 = s[mb][b8 + 2 * w], x1 = s[mb][b8 + 2 * w + 1];
-            pl[kk][w] = E::pack(x0 - E::round_trip(x0), x1 - E::round_trip(x1));
-          }
-        }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const u32x4_t vf = vfrag(kk, db);
-            o[db] = E::mma(vf, ph[kk], o[db]);
-            o[db] = E::mma(vf, pl[kk], o[db]);
-          }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) o[db] = E::mma(vfrag(kk, db), ph[kk], o[db]);
-      }
+      if (m_run[n] == kNegInf) m_run[n] = m_tile;
+      m_pend[n] = m_tile;
+      grow = grow || (m_tile > m_run[n] + kGrowBound);
     }
+    return __ballot(grow) != 0ull;
+  };
 
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of tile t+1 have landed
+  // Rows whose max outgrew the bound: move their running max and rescale O
+  // and l (kept outside the key loop so O never needs VALU work there).
+  auto rescale = [&](const float (&m_pend)[NB]) __attribute__((device)) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const bool g = m_pend[n] > m_run[n] + kGrowBound;
+      const float alpha = g ? fast_exp2(m_run[n] - m_pend[n]) : 1.0f;
+      if (g) m_run[n] = m_pend[n];
+      l_run[n] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[n][i][e] *= alpha;
+    }
+  };
+
+  // One loop step for tile t.  Entry: s_cur holds tile t's masked, biased
+  // scores and m_run is final for them.  One interleaved stream (StreamPlan):
+  // QK^T MFMAs of tile t+1, PV MFMAs of tile t as soon as their slice of P
+  // is packed, and tile t's softmax in pairs of scores, with operand reads
+  // issued ahead.  Then tile t+1's scores are prepared; the return value says
+  // whether a rescale is due before tile t+1.
+  auto step = [&](auto split_tag, int j, f32x16_t (&s_cur)[NB][NMB], f32x16_t (&s_nxt)[NB][NMB],
+                  float (&m_pend)[NB]) __attribute__((device)) -> bool {
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    constexpr int NKF = NMB * KSTEPS;     // K fragments per tile
+    constexpr int NQK = NKF * NB;         // QK^T MFMAs per tile
+    constexpr int NVF = NKS * NDB;        // V^T fragments per tile
+    constexpr int NPV = NVF * NB;         // PV MFMA slots per tile (x2 with the split)
+    using Plan = StreamPlan<NQK, NPV, NB, NDB, NKS>;
+    const int nt = t_end - t_begin;
+    const int t = t_begin + j;
+    const int slot = j & 1;
+    if (j + 1 < nt) load_v(t + 1, slot ^ 1);
+    if (j + 2 < nt) load_k(t + 2, slot);
+
+    const lds_char* kt = kbuf0 + (slot ^ 1) * K_BYTES;
+    const lds_char* vt = vbuf0 + slot * V_BYTES;
+    // K fragment fi: d-step fi / NMB, key block fi % NMB
+    auto kread = [&](int fi) __attribute__((device)) -> u32x4_t {
+      const int kk = fi / NMB, mb = fi % NMB;
+      const int key = 32 * mb + l32;
+      const int c = (2 * kk + hf) ^ KSwz<DQK>::f(key);
+      return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(kt + key * KRB + c * 16);
+    };
+    u32x4_t kf[3];
+    u32x4_t vf[3];
+    // QK MFMA i: K fragment i / NB, query block i % NB
+    auto do_qk = [&](int i) __attribute__((device)) {
+      const int fi = i / NB, n = i % NB;
+      if (n == 0 && fi + 2 < NKF) kf[(fi + 2) % 3] = kread(fi + 2);
+      s_nxt[n][fi % NMB] = E::mma(kf[fi % 3], qf[n][fi / NMB], s_nxt[n][fi % NMB]);
+    };
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s_nxt[n][mb][e] = 0.0f;
+    kf[0] = kread(0);
+    if (NKF > 1) kf[1] = kread(1);
+    float neg_m[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) neg_m[n] = (m_run[n] == kNegInf) ? 0.0f : -m_run[n];
+
+    u32x4_t ph[NB][NKS];
+    u32x4_t pl[NB][NKS];
+    float lsum[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) lsum[n] = 0.0f;
+    auto vread = [&](int vi) __attribute__((device)) -> u32x4_t { return vfrag(vt, vi / NDB, vi % NDB); };
+#pragma unroll
+    for (int i = 0; i < Plan::kHead; ++i) do_qk(i);
+    vf[0] = vread(0);
+    if (NVF > 1) vf[1] = vread(1);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, Plan::kOps>([&](auto qc) __attribute__((device)) {
+      constexpr int op = Plan::op(decltype(qc)::value);
+      constexpr int ix = Plan::index(decltype(qc)::value);
+      if constexpr (op == kOpQK) {
+        do_qk(ix);
+      } else if constexpr (op == kOpPV) {
+        const int vi = ix / NB, n = ix % NB;
+        if (n == 0 && vi + 2 < NVF) vf[(vi + 2) % 3] = vread(vi + 2);
+        const int kk = vi / NDB, db = vi % NDB;
+        o[n][db] = E::mma(vf[vi % 3], ph[n][kk], o[n][db]);
+        if constexpr (SPLIT) o[n][db] = E::mma(vf[vi % 3], pl[n][kk], o[n][db]);
+      } else {
+        static_assert(op == kOpChunk, "stream op");
+        // chunk ix: k-step kk, query block n, P word w -> S^T block kk / 2,
+        // entries 8 (kk % 2) + 2 w, +1 (keys 16 kk + {2w, 2w+1 | +8} + 4 hf)
+        const int kk = ix / (4 * NB), n = (ix / 4) % NB, w = ix % 4;
+        const int mb = kk >> 1, e0 = 8 * (kk & 1) + 2 * w;
+        const float x0 = BIAS ? s_cur[n][mb][e0] + neg_m[n] : __builtin_fmaf(s_cur[n][mb][e0], c_scale, neg_m[n]);
+        const float x1 = BIAS ? s_cur[n][mb][e0 + 1] + neg_m[n]
+                              : __builtin_fmaf(s_cur[n][mb][e0 + 1], c_scale, neg_m[n]);
+        const float p0 = fast_exp2(x0);
+        const float p1 = fast_exp2(x1);
+        lsum[n] += p0;
+        lsum[n] += p1;
+        uint32_t hw = E::pack(p0, p1);
+        // Empty asm with in/out register operands: an optimisation fence
+        // that keeps this pair's VALU work at its slot in the stream (pure
+        // arithmetic would otherwise be sunk below the MFMAs).
+        if constexpr (SPLIT) {
+          uint32_t lw = E::pack(p0 - E::round_trip(p0), p1 - E::round_trip(p1));
+          asm volatile("" : "+v"(hw), "+v"(lw), "+v"(lsum[n]));
+          pl[n][kk][w] = lw;
+        } else {
+          asm volatile("" : "+v"(hw), "+v"(lsum[n]));
+        }
+        ph[n][kk][w] = hw;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int n = 0; n < NB; ++n) l_run[n] += lsum[n];
+    const bool grow = (j + 1 < nt) ? prep_tile(t + 1, s_nxt, m_pend) : false;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of V(t+1), K(t+2) have landed
     __syncthreads();
+    return grow;
+  };
+
+  auto run = [&](auto split_tag) __attribute__((device)) {
+    const int nt = t_end - t_begin;
+    load_k(t_begin, 0);
+    load_v(t_begin, 0);
+    if (nt > 1) load_k(t_begin + 1, 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    f32x16_t sa[NB][NMB], sb[NB][NMB];
+    float m_pend[NB];
+    qk_all(kbuf0, sa);
+    bool need = prep_tile(t_begin, sa, m_pend);
+    __syncthreads();  // every wave is done with K buffer 0 before it is refilled
+    for (int j = 0; j < nt; j += 2) {
+      need = step(split_tag, j, sa, sb, m_pend);
+      if (need) rescale(m_pend);
+      if (j + 1 < nt) { need = step(split_tag, j + 1, sb, sa, m_pend); if (need) rescale(m_pend); }
+    }
+  };
+  if (t_begin < t_end) {
+    if (split) run(std::true_type{});
+    else run(std::false_type{});
   }
 
   // ---- epilogue: O / l staged through LDS (the K/V buffers are free after
-  // the loop's last barrier) so that every output row is written as
-  // contiguous 16-byte stores.
+  // the loop's last barrier), one 32-row query block at a time, so that
+  // every output row is written as contiguous 16-byte stores.
   if (!wave_active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   lds_char* ostage = (lds_char*)smem + wave * 32 * OUT_RB;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int n = 0; n < NB; ++n) {
+    const float l_tot = l_run[n] + __shfl_xor(l_run[n], 32);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (n > 0) __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int d0 = 32 * db + 8 * qd + 4 * hf;
-      const float v0 = o[db][4 * qd] * inv, v1 = o[db][4 * qd + 1] * inv;
-      const float v2 = o[db][4 * qd + 2] * inv, v3 = o[db][4 * qd + 3] * inv;
-      const int byte = d0 * (int)sizeof(OutT);
-      const int c = (byte >> 4) ^ (l32 & (OUT_CPR - 1));
-      lds_char* dst = ostage + l32 * OUT_RB + c * 16 + (byte & 15);
-      if constexpr (sizeof(OutT) == 4) {
-        *(__attribute__((address_space(3))) f32x4_t*)dst = (f32x4_t){v0, v1, v2, v3};
-      } else {
-        *(__attribute__((address_space(3))) u32x2_t*)dst =
-            (u32x2_t){Elem<OutT>::pack(v0, v1), Elem<OutT>::pack(v2, v3)};
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int d0 = 32 * db + 8 * qd + 4 * hf;
+        const float v0 = o[n][db][4 * qd] * inv, v1 = o[n][db][4 * qd + 1] * inv;
+        const float v2 = o[n][db][4 * qd + 2] * inv, v3 = o[n][db][4 * qd + 3] * inv;
+        const int byte = d0 * (int)sizeof(OutT);
+        const int c = (byte >> 4) ^ (l32 & (OUT_CPR - 1));
+        lds_char* dst = ostage + l32 * OUT_RB + c * 16 + (byte & 15);
+        if constexpr (sizeof(OutT) == 4) {
+          *(__attribute__((address_space(3))) f32x4_t*)dst = (f32x4_t){v0, v1, v2, v3};
+        } else {
+          *(__attribute__((address_space(3))) u32x2_t*)dst =
+              (u32x2_t){Elem<OutT>::pack(v0, v1), Elem<OutT>::pack(v2, v3)};
+        }
+      }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_wave_barrier();
+    {
+      constexpr int RPI = 64 / OUT_CPR;  // rows per wave-wide pass
+      const int cc = lane % OUT_CPR;
+      const int qb = w0 + 32 * n;        // first row of this block
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int q = it * RPI + lane / OUT_CPR;
+        const int c = cc ^ (q & (OUT_CPR - 1));
+        const u32x4_t val =
+            *(const __attribute__((address_space(3))) u32x4_t*)(ostage + q * OUT_RB + c * 16);
+        if (qb + q < lq) {
+          char* dst = reinterpret_cast<char*>(a.out) +
+                      ((int64_t)(cq0 + qb + q) * a.o_st + (int64_t)head * a.o_sh) * (int64_t)sizeof(OutT) +
+                      cc * 16;
+          *reinterpret_cast<u32x4_t*>(dst) = val;
+        }
       }
     }
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_wave_barrier();
-  {
-    constexpr int RPI = 64 / OUT_CPR;  // rows per wave-wide pass
-    const int cc = lane % OUT_CPR;
-#pragma unroll
-    for (int it = 0; it < 32 / RPI; ++it) {
-      const int q = it * RPI + lane / OUT_CPR;
-      const int c = cc ^ (q & (OUT_CPR - 1));
-      const u32x4_t val = *(const __attribute__((address_space(3))) u32x4_t*)(ostage + q * OUT_RB + c * 16);
-      if (w0 + q < lq) {
-        char* dst = reinterpret_cast<char*>(a.out) +
-                    ((int64_t)(cq0 + w0 + q) * a.o_st + (int64_t)head * a.o_sh) * (int64_t)sizeof(OutT) +
-                    cc * 16;
-        *reinterpret_cast<u32x4_t*>(dst) = val;
-      }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    if (a.lse != nullptr && hf == 0 && row_ok[n]) {
+      const float m_use = (m_run[n] == kNegInf) ? 0.0f : m_run[n];
+      a.lse[(int64_t)head * a.total_q + cq0 + my_row[n]] =
+          l_tot > 0.0f ? (m_use + fast_log2(l_tot)) * kLn2 : kNegInf;
     }
-  }
-  if (a.lse != nullptr && hf == 0 && row_ok) {
-    const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
-    a.lse[(int64_t)head * a.total_q + cq0 + my_row] =
-        l_tot > 0.0f ? (m_use + fast_log2(l_tot)) * kLn2 : kNegInf;
   }
 }
 
@@ -964,7 +1147,7 @@ hipError_t launch_one(const KernelArgs& a, dim3 grid, hipStream_t stream) {
   if constexpr (Elem<T>::kWide) {
     hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, BIAS, OutT>), grid, dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((attn_fwd16_kernel<T, DQK, DV, BIAS, OutT>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd16p_kernel<T, DQK, DV, BIAS, OutT>), grid, dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -992,7 +1175,19 @@ hipError_t launch_type(const KernelArgs& a, int dqk, int dv, bool bias, bool out
 
 }  // namespace
 
-int tile_bn(int in_dtype) { return in_dtype == kF32 ? Geo<float, 64, 64>::BN : Geo<__bf16, 64, 64>::BN; }
+int tile_bn(int in_dtype, int dqk, int dv) {
+  if (in_dtype == kF32) return Geo<float, 64, 64>::BN;
+  if (dqk == 64 && dv == 64) return 32 * WaveBlocks<64, 64>::NMB;
+  if (dqk == 128 && dv == 128) return 32 * WaveBlocks<128, 128>::NMB;
+  return 32 * WaveBlocks<192, 128>::NMB;
+}
+
+int tile_bm(int in_dtype, int dqk, int dv) {
+  if (in_dtype == kF32) return kBM;
+  if (dqk == 64 && dv == 64) return 4 * 32 * WaveBlocks<64, 64>::NB;
+  if (dqk == 128 && dv == 128) return 4 * 32 * WaveBlocks<128, 128>::NB;
+  return 4 * 32 * WaveBlocks<192, 128>::NB;
+}
 
 hipError_t launch_attn_fwd(const KernelArgs& a, int in_dtype, int out_dtype, int dqk, int dv,
                            bool bias, dim3 grid, hipStream_t stream) {

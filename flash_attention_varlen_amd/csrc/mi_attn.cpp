@@ -89,8 +89,8 @@ int mi_attn_tile_shape(int32_t in_dtype, int32_t d_qk, int32_t d_v, int32_t* bm,
   if (!dims_supported(in_dtype, d_qk, d_v))
     return fail(MI_ATTN_ERR_UNSUPPORTED, "head dims (%d, %d) unsupported for dtype %d", d_qk, d_v,
                 in_dtype);
-  if (bm) *bm = mi_attn::kBM;
-  if (bn) *bn = mi_attn::tile_bn(in_dtype);
+  if (bm) *bm = mi_attn::tile_bm(in_dtype, d_qk, d_v);
+  if (bn) *bn = mi_attn::tile_bn(in_dtype, d_qk, d_v);
   return MI_ATTN_OK;
 }
 

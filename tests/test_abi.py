@@ -36,8 +36,10 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_tile_shape():
     assert fav.mi_attn_version() == 100
-    assert fav.mi_attn_tile_shape(fav.BF16, 128, 128) == (128, 64)
-    assert fav.mi_attn_tile_shape(fav.F16, 192, 128) == (128, 64)
+    for dt in (fav.BF16, fav.F16):
+        for dqk, dv in ((64, 64), (128, 128), (192, 128)):
+            bm, bn = fav.mi_attn_tile_shape(dt, dqk, dv)
+            assert bm % 128 == 0 and bn % 32 == 0 and bm > 0 and bn > 0
     assert fav.mi_attn_tile_shape(fav.F32, 64, 64) == (128, 32)
     with pytest.raises(fav.MiAttnError):
         fav.mi_attn_tile_shape(fav.F32, 192, 128)

@@ -178,7 +178,7 @@ def test_window_cost_scales_with_window():
         w = W(name="swa_tiles", seqlens_q=(16384,), seqlens_kv=(16384,), hq=1, hkv=1, d_qk=128,
               d_v=128, dtype="bf16", causal=True, window=win, seed=41)
         bm, bn = fav.mi_attn_tile_shape(fav.BF16, 128, 128)
-        nqt = 16384 // bm
+        nqt = (16384 + bm - 1) // bm
         counts = torch.full((nqt,), -1, dtype=torch.int32, device="cuda")
         inp = workloads.make_inputs(w)
         run_gpu(inp, out_dtype=torch.bfloat16, tile_counts=counts)
@@ -187,8 +187,8 @@ def test_window_cost_scales_with_window():
         expect = [((t + 1) * bm + bn - 1) // bn - max(0, t * bm - win + 1) // bn for t in range(nqt)]
         assert c.tolist() == expect
         totals[win] = int(c.sum())
-    # 2232 vs 7392 tiles: cost follows W (full causal would be 16512)
-    assert totals == {1024: 2232, 4096: 7392}
+    # cost follows W: at BM=128, BN=64 this is 2232 vs 7392 tiles (full causal: 16512)
+    assert 3.0 < totals[4096] / totals[1024] < 3.6
 
 
 def test_bitwise_deterministic():
