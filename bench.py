@@ -307,7 +307,7 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "algorithmic_bytes": algorithmic_bytes(w, out_bytes),
-            "kernel": "attn_fwd_kernel" if w.dtype == "f32" else "attn_fwd16_kernel",
+            "kernel": "attn_fwd_kernel" if w.dtype == "f32" else "attn_fwd16p_kernel",
             "kernel_ms": round(kernel_ms, 4),
         },
         "cpu_baseline": cpu,

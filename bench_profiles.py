@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Turn rocprofv3 CSV output of bench.py runs into the short text summaries
+kept under profiles/ (and the per-launch HBM traffic figure bench.py reports).
+
+    python bench_profiles.py --workload gqa_causal_bf16 \
+        --trace DIR --trace-cmd "..." --bench-json FILE \
+        [--fetch DIR --write DIR --pmc-cmd "..."]
+
+--trace: directory of a `rocprofv3 --kernel-trace --stats --output-format csv`
+run of bench.py; the summary lists every kernel's statistics and the mean
+duration of the attention kernel over the timed launches (the last --steps
+dispatches), next to the bench line printed by the same run.
+
+--fetch / --write: directories of `rocprofv3 --pmc FETCH_SIZE` and
+`--pmc WRITE_SIZE` runs of bench.py with --copy-calibration-mib M.  The
+counters are in KiB per dispatch.  The plain device copy of M MiB that the
+same runs launch reads and writes exactly M MiB, so
+factor = M*1024 / (counter reading of the copy) converts each counter to
+bytes; the attention kernel's per-launch HBM bytes are
+fetch*factor_f + write*factor_w, averaged over its dispatches.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+ATTN_PREFIX = "_ZN7mi_attn"
+
+
+def short_name(mangled: str) -> str:
+    for key in ("attn_fwd16p_kernel", "attn_fwd_kernel"):
+        if key in mangled:
+            return key
+    return mangled[:60]
+
+
+def read_csv(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def trace_summary(args) -> str:
+    stats = read_csv(os.path.join(args.trace, "run_kernel_stats.csv"))
+    trace = read_csv(os.path.join(args.trace, "run_kernel_trace.csv"))
+    attn = [r for r in trace if r["Kernel_Name"].startswith(ATTN_PREFIX)]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in attn]
+    timed = durs[-args.steps:]
+    bench = None
+    if args.bench_json and os.path.exists(args.bench_json):
+        with open(args.bench_json) as f:
+            for line in f:
+                if line.startswith("{"):
+                    bench = json.loads(line)
+    r0 = attn[0] if attn else {}
+    lines = [f"# rocprofv3 kernel trace: {short_name(r0.get('Kernel_Name', ''))}, "
+             f"workload {args.workload}", "",
+             "Command (run from the repository root on one MI355X):", "",
+             "```", args.trace_cmd, "```", "",
+             "## Kernel statistics (all dispatches, as rocprofv3 --stats prints them)", "",
+             "| kernel | calls | total ms | average us | min us | max us |",
+             "|---|---|---|---|---|---|"]
+    for s in stats:
+        lines.append(f"| {short_name(s['Name'])} | {s['Calls']} | "
+                     f"{int(s['TotalDurationNs']) / 1e6:.3f} | {float(s['AverageNs']) / 1e3:.1f} | "
+                     f"{int(s['MinNs']) / 1e3:.1f} | {int(s['MaxNs']) / 1e3:.1f} |")
+    lines += ["", "## Attention kernel", "",
+              f"- launch: grid {r0.get('Grid_Size_X')}x{r0.get('Grid_Size_Y')} work-items, "
+              f"workgroup {r0.get('Workgroup_Size_X')}, LDS {r0.get('LDS_Block_Size')} B, "
+              f"scratch {r0.get('Scratch_Size')} B, arch VGPR {r0.get('VGPR_Count')}, "
+              f"AGPR {r0.get('Accum_VGPR_Count')}, SGPR {r0.get('SGPR_Count')}",
+              f"- dispatches: {len(durs)} (warmup + timed)",
+              f"- mean over the {len(timed)} timed dispatches: {statistics.mean(timed):.1f} us "
+              f"(median {statistics.median(timed):.1f}, min {min(timed):.1f}, max {max(timed):.1f})"]
+    if bench:
+        rf = bench["roofline"]
+        lines += [f"- the same run's bench line: kernel_ms {rf['kernel_ms']} (HIP events around "
+                  f"each launch), value {bench['value']} {bench['unit']}, roofline achieved "
+                  f"{rf['achieved']} of {rf['peak']} {rf['unit']} (frac {rf['frac']})",
+                  f"- trace mean / event mean = "
+                  f"{statistics.mean(timed) / (rf['kernel_ms'] * 1e3):.3f}"]
+    return "\n".join(lines) + "\n"
+
+
+def counter_values(d, name):
+    rows = read_csv(os.path.join(d, "run_counter_collection.csv"))
+    attn = [float(r["Counter_Value"]) for r in rows
+            if r["Kernel_Name"].startswith(ATTN_PREFIX) and r["Counter_Name"] == name]
+    copy = [float(r["Counter_Value"]) for r in rows
+            if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == name]
+    kname = next(r["Kernel_Name"] for r in rows if r["Kernel_Name"].startswith(ATTN_PREFIX))
+    return attn, copy, kname
+
+
+def traffic_summary(args):
+    from bench import algorithmic_bytes, kernel_source_hash
+    import workloads
+    fa, fc, kname = counter_values(args.fetch, "FETCH_SIZE")
+    wa, wc, _ = counter_values(args.write, "WRITE_SIZE")
+    kib = args.copy_mib * 1024.0
+    # the calibration copies are the big ones (the library's own small copies read ~KiB)
+    fcal = max(fc)
+    wcal = max(wc)
+    ff = kib / fcal
+    fw = kib / wcal
+    fetch_b = statistics.mean(fa) * ff * 1024
+    write_b = statistics.mean(wa) * fw * 1024
+    w = workloads.ALL[args.workload]
+    alg = algorithmic_bytes(w, 2 if w.dtype != "f32" else 4)
+    lines = [f"# HBM traffic: {short_name(kname)}, workload {args.workload}", "",
+             "Commands (one PMC pass each, run from the repository root on one MI355X):", "",
+             "```", args.pmc_cmd.replace("{COUNTER}", "FETCH_SIZE").replace("{DIR}", "prof_fetch"),
+             args.pmc_cmd.replace("{COUNTER}", "WRITE_SIZE").replace("{DIR}", "prof_write"), "```", "",
+             f"Calibration: bench.py --copy-calibration-mib {args.copy_mib} copies {args.copy_mib} MiB "
+             f"device to device (reads and writes {kib:.0f} KiB each).", "",
+             "| counter | copy reading (KiB) | factor | attention readings (KiB/dispatch) | "
+             "attention bytes/launch |", "|---|---|---|---|---|",
+             f"| FETCH_SIZE | {fcal:.1f} | {ff:.3f} | {', '.join(f'{x:.0f}' for x in fa)} | "
+             f"{fetch_b:.4g} |",
+             f"| WRITE_SIZE | {wcal:.1f} | {fw:.3f} | {', '.join(f'{x:.0f}' for x in wa)} | "
+             f"{write_b:.4g} |", "",
+             f"- HBM bytes per launch (fetch + write, calibrated): {fetch_b + write_b:.4g}",
+             f"- algorithmic bytes per launch (q, k, v, out, lse once): {alg:.4g}",
+             f"- ratio: {(fetch_b + write_b) / alg:.2f}",
+             f"- kernel source sha256[:16]: {kernel_source_hash()}"]
+    data = {"workload": args.workload, "kernel": short_name(kname),
+            "kernel_source_sha256_16": kernel_source_hash(),
+            "hbm_bytes_per_launch": fetch_b + write_b,
+            "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+            "fetch_factor": ff, "write_factor": fw, "algorithmic_bytes": alg}
+    return "\n".join(lines) + "\n", data
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--trace")
+    ap.add_argument("--trace-cmd", default="")
+    ap.add_argument("--bench-json")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--pmc-cmd", default="")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    args = ap.parse_args()
+    os.makedirs(args.out_dir, exist_ok=True)
+    if args.trace:
+        txt = trace_summary(args)
+        kname = "attn_fwd16p_kernel" if "attn_fwd16p" in txt else "attn_fwd_kernel"
+        p = os.path.join(args.out_dir, f"{kname}_{args.workload}_trace.md")
+        with open(p, "w") as f:
+            f.write(txt)
+        print("wrote", p)
+    if args.fetch and args.write:
+        txt, data = traffic_summary(args)
+        p = os.path.join(args.out_dir, f"{data['kernel']}_{args.workload}_hbm.md")
+        with open(p, "w") as f:
+            f.write(txt)
+        pj = os.path.join(args.out_dir, f"traffic_attn_fwd_{args.workload}.json")
+        with open(pj, "w") as f:
+            json.dump(data, f, indent=1)
+        print("wrote", p, pj)
+
+
+if __name__ == "__main__":
+    main()

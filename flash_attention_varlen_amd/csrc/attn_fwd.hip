@@ -58,6 +58,31 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleThreshold = 8.0f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max(x, x of the lane 32 away).  v_permlane32_swap exchanges lanes 32-63 of
+// its first operand with lanes 0-31 of its second; given two copies of x it
+// leaves (low half of x in both halves, high half of x in both halves), whose
+// elementwise max is the pairwise max on every lane.  It is written as
+// inline assembly (with the two wait states a VALU write needs before the
+// swap reads it): the compiler builtin's second result was dropped from the
+// max by the optimiser.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  float lo = x, hi = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+  return __builtin_fmaxf(lo, hi);
+}
+
+// Max of the 16 entries of one accumulator block as a tree (depth 3).
+__device__ __forceinline__ float max16(const f32x16_t& v) {
+  const float a0 = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
+  const float a1 = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
+  const float a2 = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
+  const float a3 = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), v[11]);
+  const float a4 = __builtin_fmaxf(__builtin_fmaxf(v[12], v[13]), v[14]);
+  const float b0 = __builtin_fmaxf(__builtin_fmaxf(a0, a1), a2);
+  const float b1 = __builtin_fmaxf(__builtin_fmaxf(a3, a4), v[15]);
+  return __builtin_fmaxf(b0, b1);
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 template <typename T>
@@ -609,20 +634,25 @@ __device__ __forceinline__ void load_tile_part(const char* base, int64_t st_b, i
 // ----------------------------------------------------------------------------
 
 // Compile-time order of one tile's stream: QK^T MFMAs of the next tile
-// (after the first kHead), PV MFMAs of this tile and the softmax chunks (one
-// chunk = one pair of scores of one query block).  Chunk q covers k-step
-// q / (4 NB), query block (q / 4) % NB, P word q % 4, so the P operand of
-// (k-step kk, block n) is complete after chunk (kk NB + n) 4 + 3.  PV MFMA
-// p uses V fragment p / NB (k-step (p / NB) / NDB, d-block (p / NB) % NDB)
-// for block p % NB.  MFMAs alternate between QK and PV where possible; one
-// chunk follows each MFMA until all are placed.
-enum : int { kOpQK = 0, kOpPV = 1, kOpChunk = 2 };
+// (after the first kHead), PV MFMAs of this tile, the softmax chunks (one
+// chunk = one pair of scores of one query block) and, when MAXOPS, the next
+// tile's masking and row max: one op per (query block, key block) once that
+// block's last QK^T MFMA is two MFMAs old, then one op that combines them.
+// Chunk q covers k-step q / (4 NB), query block (q / 4) % NB, P word q % 4,
+// so the P operand of (k-step kk, block n) is complete after chunk
+// (kk NB + n) 4 + 3.  PV MFMA p uses V fragment p / NB (k-step (p / NB) /
+// NDB, d-block (p / NB) % NDB) for block p % NB; QK MFMA i uses K fragment
+// i / NB (d-step (i / NB) / NMB, key block (i / NB) % NMB) for block i % NB.
+// MFMAs alternate between QK and PV where possible; one chunk (else one max
+// op) follows each MFMA.
+enum : int { kOpQK = 0, kOpPV = 1, kOpChunk = 2, kOpMax = 3, kOpMaxEnd = 4 };
 
-template <int NQK, int NPV, int NB, int NDB, int NKS>
+template <int NQK, int NPV, int NB, int NDB, int NKS, int NMB, bool MAXOPS>
 struct StreamPlan {
   static constexpr int kHead = NQK < 4 ? NQK : 4;
   static constexpr int kChunks = 4 * NKS * NB;
-  static constexpr int kOps = (NQK - kHead) + NPV + kChunks;
+  static constexpr int kMaxOps = MAXOPS ? NB * NMB + 1 : 0;
+  static constexpr int kOps = (NQK - kHead) + NPV + kChunks + kMaxOps;
   struct Table {
     int8_t op[kOps];
     int8_t ix[kOps];
@@ -630,22 +660,36 @@ struct StreamPlan {
   static constexpr int pv_needs(int p) {
     return (((p / NB) / NDB) * NB + (p % NB)) * 4 + 4;
   }
+  // QK MFMA index after which block (n, mb) of the next tile's scores is final
+  static constexpr int qk_last(int n, int mb) {
+    return ((NQK / NB / NMB - 1) * NMB + mb) * NB + n;
+  }
   static constexpr Table build() {
     Table t{};
-    int n = 0, qk = kHead, pv = 0, ch = 0;
+    int n = 0, qk = kHead, pv = 0, ch = 0, mx = 0, mfmas = 0;
+    int qk_pos[NQK > 0 ? NQK : 1] = {};  // MFMA ordinal of each QK MFMA
+    for (int i = 0; i < kHead; ++i) qk_pos[i] = i - kHead;
     bool last_pv = false;
-    while (qk < NQK || pv < NPV || ch < kChunks) {
+    auto max_ready = [&](int m) {
+      if (m == NB * NMB) return true;  // combine op: after all block ops
+      const int i = qk_last(m / NMB, m % NMB);
+      return i < qk && mfmas - qk_pos[i] >= 3;
+    };
+    while (qk < NQK || pv < NPV || ch < kChunks || mx < kMaxOps) {
       const bool pv_ready = pv < NPV && ch >= pv_needs(pv);
       bool mfma = false;
       if (pv_ready && (qk >= NQK || !last_pv)) {
-        t.op[n] = kOpPV; t.ix[n] = (int8_t)pv++; ++n; last_pv = true; mfma = true;
+        t.op[n] = kOpPV; t.ix[n] = (int8_t)pv++; ++n; last_pv = true; mfma = true; ++mfmas;
       } else if (qk < NQK) {
-        t.op[n] = kOpQK; t.ix[n] = (int8_t)qk++; ++n; last_pv = false; mfma = true;
+        qk_pos[qk] = mfmas;
+        t.op[n] = kOpQK; t.ix[n] = (int8_t)qk++; ++n; last_pv = false; mfma = true; ++mfmas;
       }
       if (ch < kChunks) {
         t.op[n] = kOpChunk; t.ix[n] = (int8_t)ch++; ++n;
-      } else if (!mfma) {
-        break;  // unreachable: every PV MFMA is ready once all chunks are placed
+      } else if (mx < kMaxOps && (max_ready(mx) || (!mfma && qk >= NQK))) {
+        t.op[n] = mx == NB * NMB ? kOpMaxEnd : kOpMax; t.ix[n] = (int8_t)mx++; ++n;
+      } else if (!mfma && qk >= NQK && pv >= NPV && mx >= kMaxOps) {
+        break;
       }
     }
     return t;
@@ -884,24 +928,50 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
   // by more than the growth bound (m_pend holds the new maxima).  A row whose
   // running max is still -inf (nothing visible yet: O and l are zero) simply
   // adopts the new max.
+  // Tile t holds keys that some row of this wave must not see (sequence
+  // end, causal diagonal, window start).
+  auto tile_needs_mask = [&](int t) __attribute__((device)) -> bool {
+    const int kb = t * BN;
+    return (kb + BN > lk) || (causal && kb + BN - 1 > w0 + off) || (W > 0 && kb <= w1 - 1 + off - W);
+  };
+  // Masks key block mb of query block n of tile t: entry e of the lane holds
+  // key kb + 32 mb + 8 (e / 4) + 4 hf + e % 4, visible iff lo < key <= hi
+  // (one unsigned compare per entry).
+  auto mask_block = [&](int t, f32x16_t& sc, int n, int mb) __attribute__((device)) {
+    const int key0 = t * BN + 32 * mb + 4 * hf;
+    const int hi = min(lk - 1, causal ? my_row[n] + off : lk - 1);
+    const int lo = W > 0 ? my_row[n] + off - W : -1;
+    const int base = lo + 1 - key0;         // first visible entry offset
+    const uint32_t span = (uint32_t)max(hi - lo, 0);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 8 * (e >> 2) + (e & 3);
+      sc[e] = (uint32_t)(c - base) < span ? sc[e] : kNegInf;
+    }
+  };
+  // Given the row max of tile t's (masked) scores for each query block, set
+  // the pending max; returns true when some row's max exceeds its running
+  // max by more than the growth bound.  A row whose running max is still
+  // -inf (nothing visible yet: O and l are zero) adopts the new max.
+  auto finish_max = [&](float (&mx)[NB], float (&m_pend)[NB]) __attribute__((device)) -> bool {
+    bool grow = false;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const float m_all = max_with_other_half(mx[n]);
+      const float m_tile = BIAS ? m_all : m_all * c_scale;
+      if (m_run[n] == kNegInf) m_run[n] = m_tile;
+      m_pend[n] = m_tile;
+      grow = grow || (m_tile > m_run[n] + kGrowBound);
+    }
+    return __ballot(grow) != 0ull;
+  };
   auto prep_tile = [&](int t, f32x16_t (&sc)[NB][NMB], float (&m_pend)[NB]) __attribute__((device)) -> bool {
     const int kb = t * BN;
-    const bool need_mask = (kb + BN > lk) || (causal && kb + BN - 1 > w0 + off) ||
-                           (W > 0 && kb <= w1 - 1 + off - W);
-    if (need_mask) {
+    if (tile_needs_mask(t)) {
 #pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const int lim_hi = causal ? my_row[n] + off : lk - 1;
-        const int lim_lo = W > 0 ? my_row[n] + off - W : -1;
+      for (int n = 0; n < NB; ++n)
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = kb + 32 * mb + 8 * (e >> 2) + 4 * hf + (e & 3);
-            const bool ok = key < lk && key <= lim_hi && key > lim_lo;
-            sc[n][mb][e] = ok ? sc[n][mb][e] : kNegInf;
-          }
-      }
+        for (int mb = 0; mb < NMB; ++mb) mask_block(t, sc[n][mb], n, mb);
     }
     if constexpr (BIAS) {
 #pragma unroll
@@ -923,21 +993,14 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
               sc[n][mb][4 * qd + e] = __builtin_fmaf(sc[n][mb][4 * qd + e], c_scale, bv[e] * kLog2e);
           }
     }
-    bool grow = false;
+    float mx[NB];
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      float mx = kNegInf;
+      mx[n] = max16(sc[n][0]);
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[n][mb][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_tile = BIAS ? mx : mx * c_scale;
-      if (m_run[n] == kNegInf) m_run[n] = m_tile;
-      m_pend[n] = m_tile;
-      grow = grow || (m_tile > m_run[n] + kGrowBound);
+      for (int mb = 1; mb < NMB; ++mb) mx[n] = __builtin_fmaxf(mx[n], max16(sc[n][mb]));
     }
-    return __ballot(grow) != 0ull;
+    return finish_max(mx, m_pend);
   };
 
   // Rows whose max outgrew the bound: move their running max and rescale O
@@ -969,7 +1032,10 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
     constexpr int NQK = NKF * NB;         // QK^T MFMAs per tile
     constexpr int NVF = NKS * NDB;        // V^T fragments per tile
     constexpr int NPV = NVF * NB;         // PV MFMA slots per tile (x2 with the split)
-    using Plan = StreamPlan<NQK, NPV, NB, NDB, NKS>;
+    // Without a bias the next tile's masking and row max run inside the
+    // stream (after its last QK^T MFMAs); with one they follow the stream.
+    constexpr bool MAXOPS = !BIAS;
+    using Plan = StreamPlan<NQK, NPV, NB, NDB, NKS, NMB, MAXOPS>;
     const int nt = t_end - t_begin;
     const int t = t_begin + j;
     const int slot = j & 1;
@@ -1010,6 +1076,10 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
     float lsum[NB];
 #pragma unroll
     for (int n = 0; n < NB; ++n) lsum[n] = 0.0f;
+    const bool has_next = j + 1 < nt;
+    const bool mask_next = has_next && tile_needs_mask(t + 1);
+    float mxp[NB];
+    bool grow = false;
     auto vread = [&](int vi) __attribute__((device)) -> u32x4_t { return vfrag(vt, vi / NDB, vi % NDB); };
 #pragma unroll
     for (int i = 0; i < Plan::kHead; ++i) do_qk(i);
@@ -1027,6 +1097,16 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
         const int kk = vi / NDB, db = vi % NDB;
         o[n][db] = E::mma(vf[vi % 3], ph[n][kk], o[n][db]);
         if constexpr (SPLIT) o[n][db] = E::mma(vf[vi % 3], pl[n][kk], o[n][db]);
+      } else if constexpr (op == kOpMax) {
+        // next tile, query block n, key block mb: mask, then fold into the max
+        const int n = ix / NMB, mb = ix % NMB;
+        if (has_next) {
+          if (mask_next) mask_block(t + 1, s_nxt[n][mb], n, mb);
+          const float m = max16(s_nxt[n][mb]);
+          mxp[n] = mb == 0 ? m : __builtin_fmaxf(mxp[n], m);
+        }
+      } else if constexpr (op == kOpMaxEnd) {
+        if (has_next) grow = finish_max(mxp, m_pend);
       } else {
         static_assert(op == kOpChunk, "stream op");
         // chunk ix: k-step kk, query block n, P word w -> S^T block kk / 2,
@@ -1057,7 +1137,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
     });
 #pragma unroll
     for (int n = 0; n < NB; ++n) l_run[n] += lsum[n];
-    const bool grow = (j + 1 < nt) ? prep_tile(t + 1, s_nxt, m_pend) : false;
+    if constexpr (!MAXOPS) grow = has_next ? prep_tile(t + 1, s_nxt, m_pend) : false;
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of V(t+1), K(t+2) have landed
     __syncthreads();
     return grow;
