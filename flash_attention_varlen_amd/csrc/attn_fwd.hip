@@ -743,12 +743,17 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
   constexpr int NDB = DV / 32;
   constexpr int OUT_RB = DV * (int)sizeof(OutT);
   constexpr int OUT_CPR = OUT_RB / 16;
-  constexpr int KV_SMEM = 2 * (K_BYTES + V_BYTES);
-  constexpr int SMEM = KV_SMEM > 4 * 32 * OUT_RB ? KV_SMEM : 4 * 32 * OUT_RB;
   static_assert(K_BYTES % (kThreads * 16) == 0 && V_BYTES % (kThreads * 16) == 0, "tile loads");
+  static_assert(32 * OUT_RB <= K_BYTES && 32 * OUT_RB <= V_BYTES, "output staging fits a buffer");
 
-  // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
-  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  // K and V double buffers as four separate LDS objects.  Each access names
+  // its buffer at compile time, so the compiler can tell that reads of the
+  // current tiles do not overlap the copies in flight into the other buffers
+  // and does not wait for those copies before reading.
+  __shared__ __attribute__((aligned(1024))) char kbuf_0[K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf_1[K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf_0[V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf_1[V_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -835,15 +840,20 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
     const int c = (pos % VCPR) ^ VSwz<DV>::f(key);
     voff[i] = (uint32_t)(key * v_st_b + c * 16);
   }
-  lds_char* const kbuf0 = (lds_char*)smem;
-  lds_char* const vbuf0 = (lds_char*)smem + 2 * K_BYTES;
-  auto load_k = [&](int t, int slot) __attribute__((device)) {
-    load_tile_part<DQK, KLOADS>(kbase, k_st_b, t * BN, min(lk - t * BN, BN),
-                                kbuf0 + slot * K_BYTES + wave * 1024, koff);
+  // buffer of compile-time slot S
+  auto kbuf = [&](auto S) __attribute__((device)) -> lds_char* {
+    if constexpr (decltype(S)::value == 0) return (lds_char*)kbuf_0;
+    else return (lds_char*)kbuf_1;
   };
-  auto load_v = [&](int t, int slot) __attribute__((device)) {
-    load_tile_part<DV, VLOADS>(vbase, v_st_b, t * BN, min(lk - t * BN, BN),
-                               vbuf0 + slot * V_BYTES + wave * 1024, voff);
+  auto vbuf = [&](auto S) __attribute__((device)) -> lds_char* {
+    if constexpr (decltype(S)::value == 0) return (lds_char*)vbuf_0;
+    else return (lds_char*)vbuf_1;
+  };
+  auto load_k = [&](int t, auto S) __attribute__((device)) {
+    load_tile_part<DQK, KLOADS>(kbase, k_st_b, t * BN, min(lk - t * BN, BN), kbuf(S) + wave * 1024, koff);
+  };
+  auto load_v = [&](int t, auto S) __attribute__((device)) {
+    load_tile_part<DV, VLOADS>(vbase, v_st_b, t * BN, min(lk - t * BN, BN), vbuf(S) + wave * 1024, voff);
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T), loaded once.
@@ -1025,8 +1035,8 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
   // is packed, and tile t's softmax in pairs of scores, with operand reads
   // issued ahead.  Then tile t+1's scores are prepared; the return value says
   // whether a rescale is due before tile t+1.
-  auto step = [&](auto split_tag, int j, f32x16_t (&s_cur)[NB][NMB], f32x16_t (&s_nxt)[NB][NMB],
-                  float (&m_pend)[NB]) __attribute__((device)) -> bool {
+  auto step = [&](auto split_tag, auto slot_tag, int j, f32x16_t (&s_cur)[NB][NMB],
+                  f32x16_t (&s_nxt)[NB][NMB], float (&m_pend)[NB]) __attribute__((device)) -> bool {
     constexpr bool SPLIT = decltype(split_tag)::value;
     constexpr int NKF = NMB * KSTEPS;     // K fragments per tile
     constexpr int NQK = NKF * NB;         // QK^T MFMAs per tile
@@ -1038,12 +1048,15 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
     using Plan = StreamPlan<NQK, NPV, NB, NDB, NKS, NMB, MAXOPS>;
     const int nt = t_end - t_begin;
     const int t = t_begin + j;
-    const int slot = j & 1;
-    if (j + 1 < nt) load_v(t + 1, slot ^ 1);
-    if (j + 2 < nt) load_k(t + 2, slot);
+    // slot = j & 1 (j runs even, odd, even, ... in the caller's unrolled loop)
+    constexpr int slot = decltype(slot_tag)::value;
+    using Cur = std::integral_constant<int, slot>;
+    using Oth = std::integral_constant<int, slot ^ 1>;
+    if (j + 1 < nt) load_v(t + 1, Oth{});
+    if (j + 2 < nt) load_k(t + 2, Cur{});
 
-    const lds_char* kt = kbuf0 + (slot ^ 1) * K_BYTES;
-    const lds_char* vt = vbuf0 + slot * V_BYTES;
+    const lds_char* kt = kbuf(Oth{});
+    const lds_char* vt = vbuf(Cur{});
     // K fragment fi: d-step fi / NMB, key block fi % NMB
     auto kread = [&](int fi) __attribute__((device)) -> u32x4_t {
       const int kk = fi / NMB, mb = fi % NMB;
@@ -1145,20 +1158,25 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
 
   auto run = [&](auto split_tag) __attribute__((device)) {
     const int nt = t_end - t_begin;
-    load_k(t_begin, 0);
-    load_v(t_begin, 0);
-    if (nt > 1) load_k(t_begin + 1, 1);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    load_k(t_begin, S0{});
+    load_v(t_begin, S0{});
+    if (nt > 1) load_k(t_begin + 1, S1{});
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     f32x16_t sa[NB][NMB], sb[NB][NMB];
     float m_pend[NB];
-    qk_all(kbuf0, sa);
+    qk_all(kbuf(S0{}), sa);
     bool need = prep_tile(t_begin, sa, m_pend);
     __syncthreads();  // every wave is done with K buffer 0 before it is refilled
     for (int j = 0; j < nt; j += 2) {
-      need = step(split_tag, j, sa, sb, m_pend);
+      need = step(split_tag, S0{}, j, sa, sb, m_pend);
       if (need) rescale(m_pend);
-      if (j + 1 < nt) { need = step(split_tag, j + 1, sb, sa, m_pend); if (need) rescale(m_pend); }
+      if (j + 1 < nt) {
+        need = step(split_tag, S1{}, j + 1, sb, sa, m_pend);
+        if (need) rescale(m_pend);
+      }
     }
   };
   if (t_begin < t_end) {
@@ -1170,7 +1188,9 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
   // the loop's last barrier), one 32-row query block at a time, so that
   // every output row is written as contiguous 16-byte stores.
   if (!wave_active) return;
-  lds_char* ostage = (lds_char*)smem + wave * 32 * OUT_RB;
+  // each wave stages its rows in one of the four (now free) buffers
+  lds_char* ostage = wave == 0 ? (lds_char*)kbuf_0 : wave == 1 ? (lds_char*)kbuf_1
+                   : wave == 2 ? (lds_char*)vbuf_0 : (lds_char*)vbuf_1;
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
     const float l_tot = l_run[n] + __shfl_xor(l_run[n], 32);
