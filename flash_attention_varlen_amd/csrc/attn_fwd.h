@@ -39,6 +39,7 @@ struct KernelArgs {
   float scale_log2;    // softmax scale * log2(e)
   int32_t split_keys;  // rows seeing fewer keys get a hi/lo split of P
   int32_t split_bias;  // with a bias, split P on every tile (16-bit types)
+  int32_t n_qtiles;    // grid.y: query tiles of the longest sequence
 };
 
 // Keys per tile for an input type and head dims.

@@ -601,6 +601,15 @@ struct VSwz {
   __device__ static int f(int key) { return D == 128 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2); }
 };
 
+// A pointer the compiler cannot prove wave-uniform, made uniform (every lane
+// must hold the same value): keeps buffer descriptors in scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // word 3 = 0x00020000: raw (untyped) dword access, no swizzle, no stride.
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
@@ -764,8 +773,11 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
   const int hf = lane >> 5;
   const int l32 = lane & 31;
 
-  // ---- work decode.  blockIdx.y counts query tiles from the end of each
-  // sequence (longest causal rows first).  Within one (sequence, tile) slab
+  // ---- work decode.  blockIdx.y counts query tiles down from the last tile
+  // of the longest sequence: tile index gridDim.y - 1 - blockIdx.y from the
+  // start of every sequence, so workgroups are dispatched roughly by
+  // decreasing row position, i.e. (for causal rows) decreasing work, and
+  // the last ones to start are the lightest.  Within one (sequence, tile) slab
   // the query heads are ordered so that the heads dispatched to one XCD
   // (consecutive workgroups go round-robin over 8 XCDs) are neighbours and
   // mostly share their kv head, i.e. hit the same L2.
@@ -776,13 +788,19 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
     const int per_xcd = a.hq >> 3;
     head = (hx & 7) * per_xcd + (hx >> 3);
   }
-  const int cq0 = a.cu_q[seq];
-  const int lq = a.cu_q[seq + 1] - cq0;
-  const int ck0 = a.cu_kv[seq];
-  const int lk = a.cu_kv[seq + 1] - ck0;
+  // The sequence bounds and the arguments the set-up needs are fetched in
+  // one round trip: the empty asm keeps the compiler from deferring loads
+  // past the early exit, one dependent wait at a time.
+  int cq0 = a.cu_q[seq], cq1 = a.cu_q[seq + 1];
+  int ck0 = a.cu_kv[seq], ck1 = a.cu_kv[seq + 1];
+  asm volatile("" : "+s"(cq0), "+s"(cq1), "+s"(ck0), "+s"(ck1)
+               : "s"(a.q_st), "s"(a.q_sh), "s"(a.k_st), "s"(a.k_sh), "s"(a.v_st), "s"(a.v_sh),
+                 "s"(a.group), "s"(a.causal), "s"(a.window), "s"(a.split_keys), "s"(a.n_qtiles));
+  const int lq = cq1 - cq0;
+  const int lk = ck1 - ck0;
   const int n_qtiles = (lq + BM - 1) / BM;
-  const int qtile = n_qtiles - 1 - (int)blockIdx.y;
-  if (qtile < 0) return;
+  const int qtile = a.n_qtiles - 1 - (int)blockIdx.y;
+  if (qtile >= n_qtiles) return;
 
   const int r0 = qtile * BM;
   const int r1 = min(lq, r0 + BM);
@@ -800,7 +818,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
   int t_end = kv_hi > 0 ? (kv_hi + BN - 1) / BN : 0;
   if (t_end < t_begin) t_end = t_begin;
 
-  if (a.tile_counts != nullptr && tid == 0 && qtile < (int)gridDim.y)
+  if (a.tile_counts != nullptr && tid == 0)
     a.tile_counts[((int64_t)qtile * a.num_seqs + seq) * a.hq + head] = t_end - t_begin;
 
   const int w0 = r0 + wave * RW;
@@ -857,15 +875,20 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T), loaded once.
+  // Rows past the sequence end fall outside the buffer window and read as 0.
   u32x4_t qf[NB][KSTEPS];
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
-    const T* qp = reinterpret_cast<const T*>(a.q) + (int64_t)(cq0 + my_row[n]) * a.q_st +
-                  (int64_t)head * a.q_sh;
+    const int64_t q_st_b = a.q_st * 2;
+    const int rows = min(32, lq - (w0 + 32 * n));  // valid rows of this block (may be <= 0)
+    const char* qb = uniform_ptr(reinterpret_cast<const char*>(a.q) +
+                                 ((int64_t)(cq0 + w0 + 32 * n) * a.q_st + (int64_t)head * a.q_sh) * 2);
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(qb, rows > 0 ? (uint32_t)((rows - 1) * q_st_b + DQK * 2) : 0u);
+    const int qoff = (int)(l32 * q_st_b) + 16 * hf;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
-      qf[n][ks] = row_ok[n] ? *reinterpret_cast<const u32x4_t*>(qp + 16 * ks + 8 * hf)
-                            : (u32x4_t){0u, 0u, 0u, 0u};
+      qf[n][ks] = __builtin_amdgcn_raw_buffer_load_b128(r, qoff + 32 * ks, 0, 0);
   }
 
   // V^T fragment (A operand of O^T += V^T P^T): two transposing reads of the

@@ -144,15 +144,16 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
       return fail(MI_ATTN_ERR_INVALID_ARG,
                   "q/k/v strides must be non-negative multiples of %lld elements (got %lld)",
                   (long long)in_mult, (long long)s);
-  if (p->k_stride_tok < p->d_qk || p->v_stride_tok < p->d_v)
+  if (p->q_stride_tok < p->d_qk || p->k_stride_tok < p->d_qk || p->v_stride_tok < p->d_v)
     return fail(MI_ATTN_ERR_UNSUPPORTED,
-                "k/v token strides must cover a full head row (k_stride_tok >= d_qk, "
+                "q/k/v token strides must cover a full head row (q_stride_tok, k_stride_tok >= d_qk, "
                 "v_stride_tok >= d_v)");
-  // 16-bit K/V tiles are fetched through 32-bit buffer offsets spanning one
-  // 64-key tile.
+  // 16-bit Q rows and K/V tiles are fetched through 32-bit buffer offsets
+  // spanning at most 64 tokens.
   if (dt != MI_ATTN_F32 &&
-      (p->k_stride_tok * elem_size(dt) * 64 > INT32_MAX || p->v_stride_tok * elem_size(dt) * 64 > INT32_MAX))
-    return fail(MI_ATTN_ERR_UNSUPPORTED, "k/v token strides too large (more than 32 MiB per token)");
+      (p->q_stride_tok * elem_size(dt) * 64 > INT32_MAX || p->k_stride_tok * elem_size(dt) * 64 > INT32_MAX ||
+       p->v_stride_tok * elem_size(dt) * 64 > INT32_MAX))
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "q/k/v token strides too large (more than 32 MiB per token)");
   if (p->out_stride_tok < 0 || p->out_stride_head < 0 || p->out_stride_tok % out_mult != 0 ||
       p->out_stride_head % out_mult != 0)
     return fail(MI_ATTN_ERR_INVALID_ARG, "out strides must be non-negative multiples of %lld",
@@ -215,6 +216,7 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
   a.split_keys = dt == MI_ATTN_BF16 ? kSplitKeysBf16 : (dt == MI_ATTN_F16 ? kSplitKeysF16 : 0);
   a.split_bias = (has_bias && dt == MI_ATTN_BF16) ? 1 : 0;
 
+  a.n_qtiles = (int32_t)n_qtiles;
   const dim3 grid((unsigned)grid_x, (unsigned)n_qtiles);
   hipError_t e = mi_attn::launch_attn_fwd(a, dt, p->out_dtype, p->d_qk, p->d_v, has_bias, grid,
                                           reinterpret_cast<hipStream_t>(stream));
