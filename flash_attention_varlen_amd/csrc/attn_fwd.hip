@@ -72,6 +72,10 @@ __device__ __forceinline__ float max_with_other_half(float x) {
   return __builtin_fmaxf(lo, hi);
 }
 
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+}
+
 // Max of the 16 entries of one accumulator block as a tree (depth 3).
 __device__ __forceinline__ float max16(const f32x16_t& v) {
   const float a0 = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
@@ -645,8 +649,9 @@ __device__ __forceinline__ void load_tile_part(const char* base, int64_t st_b, i
 // Compile-time order of one tile's stream: QK^T MFMAs of the next tile
 // (after the first kHead), PV MFMAs of this tile, the softmax chunks (one
 // chunk = one pair of scores of one query block) and, when MAXOPS, the next
-// tile's masking and row max: one op per (query block, key block) once that
-// block's last QK^T MFMA is two MFMAs old, then one op that combines them.
+// tile's masking and row max in small pieces: kMaxPieces per (query block,
+// key block) once that block's last QK^T MFMA is two MFMAs old, then two
+// that combine the blocks and exchange with the other half of the wave.
 // Chunk q covers k-step q / (4 NB), query block (q / 4) % NB, P word q % 4,
 // so the P operand of (k-step kk, block n) is complete after chunk
 // (kk NB + n) 4 + 3.  PV MFMA p uses V fragment p / NB (k-step (p / NB) /
@@ -655,12 +660,15 @@ __device__ __forceinline__ void load_tile_part(const char* base, int64_t st_b, i
 // MFMAs alternate between QK and PV where possible; one chunk (else one max
 // op) follows each MFMA.
 enum : int { kOpQK = 0, kOpPV = 1, kOpChunk = 2, kOpMax = 3, kOpMaxEnd = 4 };
+constexpr int kMaxPieces = 3;  // max-tree pieces per 16-entry accumulator block
+constexpr int kMaxEndPieces = 2;
 
 template <int NQK, int NPV, int NB, int NDB, int NKS, int NMB, bool MAXOPS>
 struct StreamPlan {
   static constexpr int kHead = NQK < 4 ? NQK : 4;
   static constexpr int kChunks = 4 * NKS * NB;
-  static constexpr int kMaxOps = MAXOPS ? NB * NMB + 1 : 0;
+  static constexpr int kBlockMaxOps = NB * NMB * kMaxPieces;
+  static constexpr int kMaxOps = MAXOPS ? kBlockMaxOps + kMaxEndPieces : 0;
   static constexpr int kOps = (NQK - kHead) + NPV + kChunks + kMaxOps;
   struct Table {
     int8_t op[kOps];
@@ -680,8 +688,9 @@ struct StreamPlan {
     for (int i = 0; i < kHead; ++i) qk_pos[i] = i - kHead;
     bool last_pv = false;
     auto max_ready = [&](int m) {
-      if (m == NB * NMB) return true;  // combine op: after all block ops
-      const int i = qk_last(m / NMB, m % NMB);
+      if (m >= kBlockMaxOps) return true;  // combine ops: after all block ops
+      const int b = m / kMaxPieces;
+      const int i = qk_last(b / NMB, b % NMB);
       return i < qk && mfmas - qk_pos[i] >= 3;
     };
     while (qk < NQK || pv < NPV || ch < kChunks || mx < kMaxOps) {
@@ -696,7 +705,9 @@ struct StreamPlan {
       if (ch < kChunks) {
         t.op[n] = kOpChunk; t.ix[n] = (int8_t)ch++; ++n;
       } else if (mx < kMaxOps && (max_ready(mx) || (!mfma && qk >= NQK))) {
-        t.op[n] = mx == NB * NMB ? kOpMaxEnd : kOpMax; t.ix[n] = (int8_t)mx++; ++n;
+        t.op[n] = mx >= kBlockMaxOps ? kOpMaxEnd : kOpMax;
+        t.ix[n] = (int8_t)(mx >= kBlockMaxOps ? mx - kBlockMaxOps : mx);
+        ++mx; ++n;
       } else if (!mfma && qk >= NQK && pv >= NPV && mx >= kMaxOps) {
         break;
       }
@@ -986,11 +997,12 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
   // the pending max; returns true when some row's max exceeds its running
   // max by more than the growth bound.  A row whose running max is still
   // -inf (nothing visible yet: O and l are zero) adopts the new max.
+  // mx holds the maxima over both halves of the wave (max_with_other_half).
   auto finish_max = [&](float (&mx)[NB], float (&m_pend)[NB]) __attribute__((device)) -> bool {
     bool grow = false;
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const float m_all = max_with_other_half(mx[n]);
+      const float m_all = mx[n];
       const float m_tile = BIAS ? m_all : m_all * c_scale;
       if (m_run[n] == kNegInf) m_run[n] = m_tile;
       m_pend[n] = m_tile;
@@ -1032,6 +1044,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
       mx[n] = max16(sc[n][0]);
 #pragma unroll
       for (int mb = 1; mb < NMB; ++mb) mx[n] = __builtin_fmaxf(mx[n], max16(sc[n][mb]));
+      mx[n] = max_with_other_half(mx[n]);
     }
     return finish_max(mx, m_pend);
   };
@@ -1115,6 +1128,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
     const bool has_next = j + 1 < nt;
     const bool mask_next = has_next && tile_needs_mask(t + 1);
     float mxp[NB];
+    float mpart[NB][NMB][5];  // leaf maxima of the max tree of each block
     bool grow = false;
     auto vread = [&](int vi) __attribute__((device)) -> u32x4_t { return vfrag(vt, vi / NDB, vi % NDB); };
 #pragma unroll
@@ -1134,15 +1148,32 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
         o[n][db] = E::mma(vf[vi % 3], ph[n][kk], o[n][db]);
         if constexpr (SPLIT) o[n][db] = E::mma(vf[vi % 3], pl[n][kk], o[n][db]);
       } else if constexpr (op == kOpMax) {
-        // next tile, query block n, key block mb: mask, then fold into the max
-        const int n = ix / NMB, mb = ix % NMB;
-        if (has_next) {
-          if (mask_next) mask_block(t + 1, s_nxt[n][mb], n, mb);
-          const float m = max16(s_nxt[n][mb]);
+        // next tile, query block n, key block mb: masking, then the max tree
+        // (leaves of three entries, then two levels), in kMaxPieces pieces.
+        // On the last tile the scores are stale and the result is unused.
+        constexpr int b = ix / kMaxPieces, piece = ix % kMaxPieces;
+        constexpr int n = b / NMB, mb = b % NMB;
+        f32x16_t& v = s_nxt[n][mb];
+        float* mp = mpart[n][mb];
+        if constexpr (piece == 0) {
+          if (mask_next) mask_block(t + 1, v, n, mb);
+          mp[0] = max3f(v[0], v[1], v[2]);
+          mp[1] = max3f(v[3], v[4], v[5]);
+        } else if constexpr (piece == 1) {
+          mp[2] = max3f(v[6], v[7], v[8]);
+          mp[3] = max3f(v[9], v[10], v[11]);
+          mp[4] = max3f(v[12], v[13], v[14]);
+        } else {
+          const float m = __builtin_fmaxf(max3f(mp[0], mp[1], mp[2]), max3f(mp[3], mp[4], v[15]));
           mxp[n] = mb == 0 ? m : __builtin_fmaxf(mxp[n], m);
         }
       } else if constexpr (op == kOpMaxEnd) {
-        if (has_next) grow = finish_max(mxp, m_pend);
+        if constexpr (ix == 0) {
+#pragma unroll
+          for (int n = 0; n < NB; ++n) mxp[n] = max_with_other_half(mxp[n]);
+        } else {
+          if (has_next) grow = finish_max(mxp, m_pend);
+        }
       } else {
         static_assert(op == kOpChunk, "stream op");
         // chunk ix: k-step kk, query block n, P word w -> S^T block kk / 2,
