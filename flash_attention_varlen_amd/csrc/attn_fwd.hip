@@ -1155,22 +1155,29 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
         constexpr int n = b / NMB, mb = b % NMB;
         f32x16_t& v = s_nxt[n][mb];
         float* mp = mpart[n][mb];
+        // (empty asm fences keep each piece at its slot, as in the chunks)
         if constexpr (piece == 0) {
           if (mask_next) mask_block(t + 1, v, n, mb);
           mp[0] = max3f(v[0], v[1], v[2]);
           mp[1] = max3f(v[3], v[4], v[5]);
+          asm volatile("" : "+v"(mp[0]), "+v"(mp[1]));
         } else if constexpr (piece == 1) {
           mp[2] = max3f(v[6], v[7], v[8]);
           mp[3] = max3f(v[9], v[10], v[11]);
           mp[4] = max3f(v[12], v[13], v[14]);
+          asm volatile("" : "+v"(mp[2]), "+v"(mp[3]), "+v"(mp[4]));
         } else {
           const float m = __builtin_fmaxf(max3f(mp[0], mp[1], mp[2]), max3f(mp[3], mp[4], v[15]));
           mxp[n] = mb == 0 ? m : __builtin_fmaxf(mxp[n], m);
+          asm volatile("" : "+v"(mxp[n]));
         }
       } else if constexpr (op == kOpMaxEnd) {
         if constexpr (ix == 0) {
 #pragma unroll
-          for (int n = 0; n < NB; ++n) mxp[n] = max_with_other_half(mxp[n]);
+          for (int n = 0; n < NB; ++n) {
+            mxp[n] = max_with_other_half(mxp[n]);
+            asm volatile("" : "+v"(mxp[n]));
+          }
         } else {
           if (has_next) grow = finish_max(mxp, m_pend);
         }
