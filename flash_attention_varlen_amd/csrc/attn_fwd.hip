@@ -842,6 +842,13 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
     my_row[n] = w0 + 32 * n + l32;
     row_ok[n] = my_row[n] < lq;
   }
+  // Tiles from wt_end on hold no key visible to any row of this wave (causal
+  // rows that end before the workgroup's last diagonal; no rows at all past
+  // the sequence end): the wave skips their work but still does its share of
+  // the copies and the barriers.
+  const int wt_end = !wave_active ? t_begin
+                     : causal    ? (min(lk, w1 - 1 + off + 1) + BN - 1) / BN
+                                 : t_end;
   // hi/lo split of P for the whole workgroup when its first row sees few keys
   const int nvis0 = (causal ? min(lk, r0 + off + 1) : lk) - kv_lo;
   const bool split = (nvis0 < a.split_keys) || (BIAS && a.split_bias != 0);
@@ -1090,6 +1097,11 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
     using Oth = std::integral_constant<int, slot ^ 1>;
     if (j + 1 < nt) load_v(t + 1, Oth{});
     if (j + 2 < nt) load_k(t + 2, Cur{});
+    if (t >= wt_end) {  // nothing visible to this wave from here on
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      return false;
+    }
 
     const lds_char* kt = kbuf(Oth{});
     const lds_char* vt = vbuf(Cur{});
