@@ -728,16 +728,19 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Per head-dim pair: NB query blocks of 32 rows per wave and NMB key
-// blocks of 32 keys per tile.
+// Per head-dim pair: NB query blocks of 32 rows per wave, NMB key blocks
+// of 32 keys per tile, OCC workgroups per CU (the register budget).  The
+// 192-wide contraction keeps 32-key tiles: its Q fragments need 48
+// registers, and 64-key tiles would push two workgroups per CU into spills.
 template <int DQK, int DV>
 struct WaveBlocks {
   static constexpr int NB = 1;
-  static constexpr int NMB = 2;
+  static constexpr int NMB = DQK > 128 ? 1 : 2;
+  static constexpr int OCC = 2;
 };
 
 template <typename T, int DQK, int DV, bool BIAS, typename OutT>
-__global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) void attn_fwd16p_kernel(
+__global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::OCC)) void attn_fwd16p_kernel(
     const KernelArgs a) {
   using E = Elem<T>;
   // A row's running max m only moves when a tile's max exceeds it by more
@@ -764,7 +767,10 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
   constexpr int OUT_RB = DV * (int)sizeof(OutT);
   constexpr int OUT_CPR = OUT_RB / 16;
   static_assert(K_BYTES % (kThreads * 16) == 0 && V_BYTES % (kThreads * 16) == 0, "tile loads");
-  static_assert(32 * OUT_RB <= K_BYTES && 32 * OUT_RB <= V_BYTES, "output staging fits a buffer");
+  // output rows staged per pass (a wave stages in one K or V buffer)
+  constexpr int STAGE_BYTES = K_BYTES < V_BYTES ? K_BYTES : V_BYTES;
+  constexpr int STAGE_ROWS = 32 * OUT_RB <= STAGE_BYTES ? 32 : STAGE_BYTES / OUT_RB;
+  static_assert(STAGE_ROWS >= 1 && 32 % STAGE_ROWS == 0, "output staging");
 
   // K and V double buffers as four separate LDS objects.  Each access names
   // its buffer at compile time, so the compiler can tell that reads of the
@@ -1258,8 +1264,8 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
   }
 
   // ---- epilogue: O / l staged through LDS (the K/V buffers are free after
-  // the loop's last barrier), one 32-row query block at a time, so that
-  // every output row is written as contiguous 16-byte stores.
+  // the loop's last barrier), STAGE_ROWS rows of a 32-row query block at a
+  // time, so that every output row is written as contiguous 16-byte stores.
   if (!wave_active) return;
   // each wave stages its rows in one of the four (now free) buffers
   lds_char* ostage = wave == 0 ? (lds_char*)kbuf_0 : wave == 1 ? (lds_char*)kbuf_1
@@ -1268,45 +1274,51 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::NB == 1 ? 2 : 1)) v
   for (int n = 0; n < NB; ++n) {
     const float l_tot = l_run[n] + __shfl_xor(l_run[n], 32);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    if (n > 0) __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int pass = 0; pass < 32 / STAGE_ROWS; ++pass) {
+      if (n > 0 || pass > 0) __builtin_amdgcn_wave_barrier();
+      const int sr = l32 - pass * STAGE_ROWS;  // this lane's row within the pass
+      if (sr >= 0 && sr < STAGE_ROWS) {
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int d0 = 32 * db + 8 * qd + 4 * hf;
-        const float v0 = o[n][db][4 * qd] * inv, v1 = o[n][db][4 * qd + 1] * inv;
-        const float v2 = o[n][db][4 * qd + 2] * inv, v3 = o[n][db][4 * qd + 3] * inv;
-        const int byte = d0 * (int)sizeof(OutT);
-        const int c = (byte >> 4) ^ (l32 & (OUT_CPR - 1));
-        lds_char* dst = ostage + l32 * OUT_RB + c * 16 + (byte & 15);
-        if constexpr (sizeof(OutT) == 4) {
-          *(__attribute__((address_space(3))) f32x4_t*)dst = (f32x4_t){v0, v1, v2, v3};
-        } else {
-          *(__attribute__((address_space(3))) u32x2_t*)dst =
-              (u32x2_t){Elem<OutT>::pack(v0, v1), Elem<OutT>::pack(v2, v3)};
-        }
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int d0 = 32 * db + 8 * qd + 4 * hf;
+            const float v0 = o[n][db][4 * qd] * inv, v1 = o[n][db][4 * qd + 1] * inv;
+            const float v2 = o[n][db][4 * qd + 2] * inv, v3 = o[n][db][4 * qd + 3] * inv;
+            const int byte = d0 * (int)sizeof(OutT);
+            const int c = (byte >> 4) ^ (sr & (OUT_CPR - 1));
+            lds_char* dst = ostage + sr * OUT_RB + c * 16 + (byte & 15);
+            if constexpr (sizeof(OutT) == 4) {
+              *(__attribute__((address_space(3))) f32x4_t*)dst = (f32x4_t){v0, v1, v2, v3};
+            } else {
+              *(__attribute__((address_space(3))) u32x2_t*)dst =
+                  (u32x2_t){Elem<OutT>::pack(v0, v1), Elem<OutT>::pack(v2, v3)};
+            }
+          }
       }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_wave_barrier();
-    {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();
       constexpr int RPI = 64 / OUT_CPR;  // rows per wave-wide pass
       const int cc = lane % OUT_CPR;
-      const int qb = w0 + 32 * n;        // first row of this block
+      const int qb = w0 + 32 * n + pass * STAGE_ROWS;  // first row of this pass
 #pragma unroll
-      for (int it = 0; it < 32 / RPI; ++it) {
+      for (int it = 0; it < (STAGE_ROWS + RPI - 1) / RPI; ++it) {
         const int q = it * RPI + lane / OUT_CPR;
         const int c = cc ^ (q & (OUT_CPR - 1));
-        const u32x4_t val =
-            *(const __attribute__((address_space(3))) u32x4_t*)(ostage + q * OUT_RB + c * 16);
-        if (qb + q < lq) {
-          char* dst = reinterpret_cast<char*>(a.out) +
-                      ((int64_t)(cq0 + qb + q) * a.o_st + (int64_t)head * a.o_sh) * (int64_t)sizeof(OutT) +
-                      cc * 16;
-          *reinterpret_cast<u32x4_t*>(dst) = val;
+        if (q < STAGE_ROWS) {
+          const u32x4_t val =
+              *(const __attribute__((address_space(3))) u32x4_t*)(ostage + q * OUT_RB + c * 16);
+          if (qb + q < lq) {
+            char* dst = reinterpret_cast<char*>(a.out) +
+                        ((int64_t)(cq0 + qb + q) * a.o_st + (int64_t)head * a.o_sh) * (int64_t)sizeof(OutT) +
+                        cc * 16;
+            *reinterpret_cast<u32x4_t*>(dst) = val;
+          }
         }
       }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     if (a.lse != nullptr && hf == 0 && row_ok[n]) {
       const float m_use = (m_run[n] == kNegInf) ? 0.0f : m_run[n];
       a.lse[(int64_t)head * a.total_q + cq0 + my_row[n]] =
