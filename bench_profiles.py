@@ -11,6 +11,12 @@ run of bench.py; the summary lists every kernel's statistics and the mean
 duration of the attention kernel over the timed launches (the last --steps
 dispatches), next to the bench line printed by the same run.
 
+--counters: directory of a `rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_MFMA SQ_INSTS_VALU
+SQ_INSTS_LDS GRBM_GUI_ACTIVE` run; the summary gives MFMA busy % (MFMA busy
+cycles over 1024 SIMDs x the GPU-active cycles of one XCD), the LDS
+bank-conflict share of LDS-active cycles and instruction counts per wave.
+
 --fetch / --write: directories of `rocprofv3 --pmc FETCH_SIZE` and
 `--pmc WRITE_SIZE` runs of bench.py with --copy-calibration-mib M.  The
 counters are in KiB per dispatch.  The plain device copy of M MiB that the
@@ -32,7 +38,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-ATTN_PREFIX = "_ZN7mi_attn"
+def is_attn(name: str) -> bool:
+    """The library's attention kernels (rocprofv3 prints some names mangled,
+    some demangled)."""
+    return "attn_fwd" in name and "mi_attn" in name
 
 
 def short_name(mangled: str) -> str:
@@ -50,7 +59,7 @@ def read_csv(path):
 def trace_summary(args) -> str:
     stats = read_csv(os.path.join(args.trace, "run_kernel_stats.csv"))
     trace = read_csv(os.path.join(args.trace, "run_kernel_trace.csv"))
-    attn = [r for r in trace if r["Kernel_Name"].startswith(ATTN_PREFIX)]
+    attn = [r for r in trace if is_attn(r["Kernel_Name"])]
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in attn]
     timed = durs[-args.steps:]
     bench = None
@@ -92,11 +101,43 @@ def trace_summary(args) -> str:
 def counter_values(d, name):
     rows = read_csv(os.path.join(d, "run_counter_collection.csv"))
     attn = [float(r["Counter_Value"]) for r in rows
-            if r["Kernel_Name"].startswith(ATTN_PREFIX) and r["Counter_Name"] == name]
+            if is_attn(r["Kernel_Name"]) and r["Counter_Name"] == name]
     copy = [float(r["Counter_Value"]) for r in rows
             if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == name]
-    kname = next(r["Kernel_Name"] for r in rows if r["Kernel_Name"].startswith(ATTN_PREFIX))
+    kname = next(r["Kernel_Name"] for r in rows if is_attn(r["Kernel_Name"]))
     return attn, copy, kname
+
+
+def counters_summary(args) -> str:
+    rows = read_csv(os.path.join(args.counters, "run_counter_collection.csv"))
+    by = {}
+    for r in rows:
+        if not is_attn(r["Kernel_Name"]):
+            continue
+        d = by.setdefault(int(r["Dispatch_Id"]), {"kname": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
+                                                  "wg": int(r["Workgroup_Size"]),
+                                                  "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    ds = list(by.values())
+    mean = lambda k: statistics.mean(d[k] for d in ds)
+    n_simd, n_xcd = 1024, 8
+    gui = mean("GRBM_GUI_ACTIVE") / n_xcd  # the counter sums the XCDs
+    busy = mean("SQ_VALU_MFMA_BUSY_CYCLES") / (n_simd * gui)
+    waves = ds[0]["grid"] / 64
+    conf = mean("SQ_LDS_BANK_CONFLICT") / mean("SQ_LDS_IDX_ACTIVE")
+    ns = statistics.mean(d["ns"] for d in ds)
+    lines = [f"# Counters: {short_name(ds[0]['kname'])}, workload {args.workload}", "",
+             "Command (run from the repository root on one MI355X):", "", "```", args.counters_cmd, "```", "",
+             f"- dispatches: {len(ds)}, mean duration {ns / 1e3:.1f} us, GPU-active {gui:.4g} cycles per XCD"
+             + (f" (shader clock {gui / ns:.2f} GHz)" if ns > 1e5 else
+                " (too short for a clock estimate: the GPU-active window is mostly launch)"),
+             f"- MFMA busy: {100 * busy:.1f}% (SQ_VALU_MFMA_BUSY_CYCLES {mean('SQ_VALU_MFMA_BUSY_CYCLES'):.4g} "
+             f"over {n_simd} SIMDs x {gui:.4g} cycles)",
+             f"- LDS bank conflicts: {100 * conf:.2f}% of LDS-active cycles (SQ_LDS_BANK_CONFLICT "
+             f"{mean('SQ_LDS_BANK_CONFLICT'):.4g}, SQ_LDS_IDX_ACTIVE {mean('SQ_LDS_IDX_ACTIVE'):.4g})",
+             f"- per wave ({waves:.0f} waves): MFMA {mean('SQ_INSTS_MFMA') / waves:.0f}, VALU "
+             f"{mean('SQ_INSTS_VALU') / waves:.0f}, LDS {mean('SQ_INSTS_LDS') / waves:.0f} instructions"]
+    return "\n".join(lines) + "\n"
 
 
 def traffic_summary(args):
@@ -104,6 +145,11 @@ def traffic_summary(args):
     import workloads
     fa, fc, kname = counter_values(args.fetch, "FETCH_SIZE")
     wa, wc, _ = counter_values(args.write, "WRITE_SIZE")
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            for d in (args.fetch, args.write)
+            for r in read_csv(os.path.join(d, "run_counter_collection.csv"))
+            if is_attn(r["Kernel_Name"])]
+    dur_ns = statistics.mean(durs)
     kib = args.copy_mib * 1024.0
     # the calibration copies are the big ones (the library's own small copies read ~KiB)
     fcal = max(fc)
@@ -129,12 +175,15 @@ def traffic_summary(args):
              f"- HBM bytes per launch (fetch + write, calibrated): {fetch_b + write_b:.4g}",
              f"- algorithmic bytes per launch (q, k, v, out, lse once): {alg:.4g}",
              f"- ratio: {(fetch_b + write_b) / alg:.2f}",
+             f"- HBM rate in these runs: {(fetch_b + write_b) / dur_ns:.1f} GB/s over a mean dispatch of "
+             f"{dur_ns / 1e3:.1f} us ({100 * (fetch_b + write_b) / dur_ns / 8000:.1f}% of 8 TB/s)",
              f"- kernel source sha256[:16]: {kernel_source_hash()}"]
     data = {"workload": args.workload, "kernel": short_name(kname),
             "kernel_source_sha256_16": kernel_source_hash(),
             "hbm_bytes_per_launch": fetch_b + write_b,
             "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
-            "fetch_factor": ff, "write_factor": fw, "algorithmic_bytes": alg}
+            "fetch_factor": ff, "write_factor": fw, "algorithmic_bytes": alg,
+            "pmc_mean_dispatch_ns": dur_ns}
     return "\n".join(lines) + "\n", data
 
 
@@ -151,12 +200,21 @@ def main():
     ap.add_argument("--write")
     ap.add_argument("--pmc-cmd", default="")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--counters")
+    ap.add_argument("--counters-cmd", default="")
     args = ap.parse_args()
     os.makedirs(args.out_dir, exist_ok=True)
     if args.trace:
         txt = trace_summary(args)
         kname = "attn_fwd16p_kernel" if "attn_fwd16p" in txt else "attn_fwd_kernel"
         p = os.path.join(args.out_dir, f"{kname}_{args.workload}_trace.md")
+        with open(p, "w") as f:
+            f.write(txt)
+        print("wrote", p)
+    if args.counters:
+        txt = counters_summary(args)
+        kname = "attn_fwd16p_kernel" if "attn_fwd16p" in txt else "attn_fwd_kernel"
+        p = os.path.join(args.out_dir, f"{kname}_{args.workload}_counters.md")
         with open(p, "w") as f:
             f.write(txt)
         print("wrote", p)
