@@ -39,7 +39,8 @@ struct KernelArgs {
   float scale_log2;    // softmax scale * log2(e)
   int32_t split_keys;  // rows seeing fewer keys get a hi/lo split of P
   int32_t split_bias;  // with a bias, split P on every tile (16-bit types)
-  int32_t n_qtiles;    // grid.y: query tiles of the longest sequence
+  int32_t n_qtiles;    // query tiles of the longest sequence (grid.y unless head_major)
+  int32_t head_major;  // 16-bit kernels: 1-D grid, all heads of a (sequence, tile) on one XCD
 };
 
 // Keys per tile for an input type and head dims.
@@ -48,7 +49,8 @@ int tile_bn(int in_dtype, int dqk, int dv);
 // Query rows per workgroup for an input type and head dims.
 int tile_bm(int in_dtype, int dqk, int dv);
 
-// Launch on `stream`; grid = (hq * num_seqs, ceil(max_seqlen_q / kBM)).
+// Launch on `stream`; grid = (hq * num_seqs, n_qtiles), or with head_major
+// (hq * (num_seqs * n_qtiles rounded up to a multiple of 8), 1).
 hipError_t launch_attn_fwd(const KernelArgs& a, int in_dtype, int out_dtype, int dqk, int dv,
                            bool bias, dim3 grid, hipStream_t stream);
 

@@ -798,12 +798,33 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::OCC)) void attn_fwd
   // the query heads are ordered so that the heads dispatched to one XCD
   // (consecutive workgroups go round-robin over 8 XCDs) are neighbours and
   // mostly share their kv head, i.e. hit the same L2.
-  const int hx = blockIdx.x % a.hq;
-  const int seq = blockIdx.x / a.hq;
-  int head = hx;
-  if ((a.hq & 7) == 0) {
-    const int per_xcd = a.hq >> 3;
-    head = (hx & 7) * per_xcd + (hx >> 3);
+  //
+  // With a bias shared by all query heads (head_major, one-dimensional
+  // grid) the order is different: XCD c (workgroups c, c + 8, ...) takes the
+  // (sequence, tile) groups c, c + 8, c + 16, ... in turn, all query heads of
+  // a group back to back, so that the group's bias rows are fetched from HBM
+  // into that XCD's L2 once and read there by every head.  Groups are
+  // numbered tile-major (sequence fastest), counting tiles down from the
+  // last as above; with a few sequences the groups an XCD holds at one time
+  // are tiles of the same sequence and share its K/V.
+  int seq, head, by;
+  if (a.head_major) {
+    const int k = (int)(blockIdx.x >> 3);
+    const int kg = k / a.hq;
+    head = k - kg * a.hq;
+    const int gb = kg * 8 + (int)(blockIdx.x & 7);
+    by = gb / a.num_seqs;
+    seq = gb - by * a.num_seqs;
+    if (by >= a.n_qtiles) return;  // padding of the last round of 8 groups
+  } else {
+    const int hx = blockIdx.x % a.hq;
+    seq = blockIdx.x / a.hq;
+    by = blockIdx.y;
+    head = hx;
+    if ((a.hq & 7) == 0) {
+      const int per_xcd = a.hq >> 3;
+      head = (hx & 7) * per_xcd + (hx >> 3);
+    }
   }
   // The sequence bounds and the arguments the set-up needs are fetched in
   // one round trip: the empty asm keeps the compiler from deferring loads
@@ -816,7 +837,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::OCC)) void attn_fwd
   const int lq = cq1 - cq0;
   const int lk = ck1 - ck0;
   const int n_qtiles = (lq + BM - 1) / BM;
-  const int qtile = a.n_qtiles - 1 - (int)blockIdx.y;
+  const int qtile = a.n_qtiles - 1 - by;
   if (qtile >= n_qtiles) return;
 
   const int r0 = qtile * BM;

@@ -217,7 +217,15 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
   a.split_bias = (has_bias && dt == MI_ATTN_BF16) ? 1 : 0;
 
   a.n_qtiles = (int32_t)n_qtiles;
-  const dim3 grid((unsigned)grid_x, (unsigned)n_qtiles);
+  // A bias shared by all query heads (16-bit kernels): every head of one
+  // (sequence, query tile) runs on one XCD so that its bias rows are read
+  // from HBM once, not once per head.  One-dimensional grid, kept well
+  // below 2^32 work-items.
+  const int64_t groups8 = ((int64_t)p->num_seqs * n_qtiles + 7) / 8 * 8;
+  const int64_t hm_wgs = (int64_t)p->hq * groups8;
+  a.head_major = (dt != MI_ATTN_F32 && has_bias && p->bias_heads == 1 && p->hq > 1 &&
+                  hm_wgs <= (int64_t)INT32_MAX / 256) ? 1 : 0;
+  const dim3 grid = a.head_major ? dim3((unsigned)hm_wgs, 1u) : dim3((unsigned)grid_x, (unsigned)n_qtiles);
   hipError_t e = mi_attn::launch_attn_fwd(a, dt, p->out_dtype, p->d_qk, p->d_v, has_bias, grid,
                                           reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));

@@ -97,6 +97,23 @@ def test_random_bias_matches_oracle(dtype, bias_heads):
     check(w.name, out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, w.dtype)
 
 
+@pytest.mark.parametrize("dims", [(64, 64), (192, 128)])
+def test_broadcast_bias_mixed_lengths(dims):
+    """A bias shared by all query heads is scheduled head-major (all heads of
+    a (sequence, tile) back to back); odd head and sequence counts leave a
+    partial last round of groups and sequences with fewer tiles than the
+    longest."""
+    dqk, dv = dims
+    w = W(name=f"bcast_bias_d{dqk}", seqlens_q=(400, 1, 257), seqlens_kv=(420, 9, 257), hq=6,
+          hkv=3, d_qk=dqk, d_v=dv, dtype="bf16", causal=True, seed=34)
+    say(f"[bias] {w.name} broadcast")
+    inp = workloads.make_inputs(w)
+    inp.bias = workloads.random_bias(w.seqlens_q, 1, 432, seed=35, neg_inf_frac=0.1)
+    out, lse = run_gpu(inp, out_dtype=torch.float32)
+    ref_out, ref_lse = run_oracle(inp)
+    check(w.name, out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, w.dtype)
+
+
 def test_outlier_channels_fp32_accumulation():
     """A few channels of magnitude 1e2..1e3: 16-bit accumulation would
     overflow; fp32 accumulation must keep the result finite and correct."""
