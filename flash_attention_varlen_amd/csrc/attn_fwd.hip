@@ -732,15 +732,21 @@ __device__ __forceinline__ void static_for(F&& f) {
 // of 32 keys per tile, OCC workgroups per CU (the register budget).  The
 // 192-wide contraction keeps 32-key tiles: its Q fragments need 48
 // registers, and 64-key tiles would push two workgroups per CU into spills.
-template <int DQK, int DV>
+template <int DQK, int DV, bool BIAS = false>
 struct WaveBlocks {
   static constexpr int NB = 1;
-  static constexpr int NMB = DQK > 128 ? 1 : 2;
+  // 32-key tiles where 64 would not fit the registers: the 192-wide head,
+  // and the 128-wide head with a bias (whose next tile's bias values are
+  // held in registers through a step).
+  static constexpr int NMB = (DQK > 128 || (BIAS && DQK == 128)) ? 1 : 2;
   static constexpr int OCC = 2;
+  // keys per tile as reported by mi_attn_tile_shape (tile counts are given
+  // in these units): the bias-free tile
+  static constexpr int kReportBN = 32 * (DQK > 128 ? 1 : 2);
 };
 
 template <typename T, int DQK, int DV, bool BIAS, typename OutT>
-__global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::OCC)) void attn_fwd16p_kernel(
+__global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void attn_fwd16p_kernel(
     const KernelArgs a) {
   using E = Elem<T>;
   // A row's running max m only moves when a tile's max exceeds it by more
@@ -748,8 +754,8 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::OCC)) void attn_fwd
   // bf16 P (8 exponent bits, like fp32) and below 2^12 for fp16 P (max
   // 65504); floating-point P and fp32 sums lose nothing to the stale max.
   constexpr float kGrowBound = std::is_same<T, __bf16>::value ? 64.0f : 12.0f;
-  constexpr int NB = WaveBlocks<DQK, DV>::NB;
-  constexpr int NMB = WaveBlocks<DQK, DV>::NMB;
+  constexpr int NB = WaveBlocks<DQK, DV, BIAS>::NB;
+  constexpr int NMB = WaveBlocks<DQK, DV, BIAS>::NMB;
   constexpr int RW = 32 * NB;  // query rows per wave
   constexpr int BM = 4 * RW;   // query rows per workgroup
   constexpr int BN = 32 * NMB; // keys per tile
@@ -856,8 +862,12 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::OCC)) void attn_fwd
   int t_end = kv_hi > 0 ? (kv_hi + BN - 1) / BN : 0;
   if (t_end < t_begin) t_end = t_begin;
 
-  if (a.tile_counts != nullptr && tid == 0)
-    a.tile_counts[((int64_t)qtile * a.num_seqs + seq) * a.hq + head] = t_end - t_begin;
+  if (a.tile_counts != nullptr && tid == 0) {
+    // in units of the reported tile width (a multiple of BN)
+    constexpr int RBN = WaveBlocks<DQK, DV, BIAS>::kReportBN;
+    a.tile_counts[((int64_t)qtile * a.num_seqs + seq) * a.hq + head] =
+        t_end > t_begin ? (t_end * BN + RBN - 1) / RBN - (t_begin * BN) / RBN : 0;
+  }
 
   const int w0 = r0 + wave * RW;
   const int w1 = min(lq, w0 + RW);
@@ -1044,8 +1054,30 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::OCC)) void attn_fwd
     }
     return __ballot(grow) != 0ull;
   };
-  auto prep_tile = [&](int t, f32x16_t (&sc)[NB][NMB], float (&m_pend)[NB]) __attribute__((device)) -> bool {
+  // This lane's bias values of tile t (the entries of its S^T registers);
+  // keys past the sequence end read as 0 (they are masked).  They are loaded
+  // at the start of the step whose end consumes them (prep_tile of the next
+  // tile), so the loads' latency is hidden behind that step's stream.
+  auto load_bias = [&](int t, f32x4_t (&bv)[NB][NMB][4]) __attribute__((device)) {
     const int kb = t * BN;
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int key0 = kb + 32 * mb + 8 * qd + 4 * hf;
+          if (row_ok[n] && key0 + 3 < lk) {
+            bv[n][mb][qd] = *reinterpret_cast<const f32x4_t*>(brow[n] + key0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              bv[n][mb][qd][e] = (row_ok[n] && key0 + e < lk) ? brow[n][key0 + e] : 0.0f;
+          }
+        }
+  };
+  auto prep_tile = [&](int t, f32x16_t (&sc)[NB][NMB], float (&m_pend)[NB],
+                       const f32x4_t (&bv)[NB][NMB][4]) __attribute__((device)) -> bool {
     if (tile_needs_mask(t)) {
 #pragma unroll
       for (int n = 0; n < NB; ++n)
@@ -1058,19 +1090,11 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::OCC)) void attn_fwd
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const int key0 = kb + 32 * mb + 8 * qd + 4 * hf;
-            f32x4_t bv;
-            if (row_ok[n] && key0 + 3 < lk) {
-              bv = *reinterpret_cast<const f32x4_t*>(brow[n] + key0);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) bv[e] = (row_ok[n] && key0 + e < lk) ? brow[n][key0 + e] : 0.0f;
-            }
+          for (int qd = 0; qd < 4; ++qd)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              sc[n][mb][4 * qd + e] = __builtin_fmaf(sc[n][mb][4 * qd + e], c_scale, bv[e] * kLog2e);
-          }
+              sc[n][mb][4 * qd + e] =
+                  __builtin_fmaf(sc[n][mb][4 * qd + e], c_scale, bv[n][mb][qd][e] * kLog2e);
     }
     float mx[NB];
 #pragma unroll
@@ -1106,7 +1130,8 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::OCC)) void attn_fwd
   // issued ahead.  Then tile t+1's scores are prepared; the return value says
   // whether a rescale is due before tile t+1.
   auto step = [&](auto split_tag, auto slot_tag, int j, f32x16_t (&s_cur)[NB][NMB],
-                  f32x16_t (&s_nxt)[NB][NMB], float (&m_pend)[NB]) __attribute__((device)) -> bool {
+                  f32x16_t (&s_nxt)[NB][NMB], float (&m_pend)[NB],
+                  f32x4_t (&bpre)[NB][NMB][4]) __attribute__((device)) -> bool {
     constexpr bool SPLIT = decltype(split_tag)::value;
     constexpr int NKF = NMB * KSTEPS;     // K fragments per tile
     constexpr int NQK = NKF * NB;         // QK^T MFMAs per tile
@@ -1128,6 +1153,9 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::OCC)) void attn_fwd
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       return false;
+    }
+    if constexpr (BIAS) {
+      if (j + 1 < nt) load_bias(t + 1, bpre);
     }
 
     const lds_char* kt = kbuf(Oth{});
@@ -1250,7 +1278,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::OCC)) void attn_fwd
     });
 #pragma unroll
     for (int n = 0; n < NB; ++n) l_run[n] += lsum[n];
-    if constexpr (!MAXOPS) grow = has_next ? prep_tile(t + 1, s_nxt, m_pend) : false;
+    if constexpr (!MAXOPS) grow = has_next ? prep_tile(t + 1, s_nxt, m_pend, bpre) : false;
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of V(t+1), K(t+2) have landed
     __syncthreads();
     return grow;
@@ -1263,18 +1291,21 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV>::OCC)) void attn_fwd
     load_k(t_begin, S0{});
     load_v(t_begin, S0{});
     if (nt > 1) load_k(t_begin + 1, S1{});
+    // bias of the first tile: in flight together with the first copies
+    f32x4_t bpre[NB][NMB][4];
+    if constexpr (BIAS) load_bias(t_begin, bpre);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     f32x16_t sa[NB][NMB], sb[NB][NMB];
     float m_pend[NB];
     qk_all(kbuf(S0{}), sa);
-    bool need = prep_tile(t_begin, sa, m_pend);
+    bool need = prep_tile(t_begin, sa, m_pend, bpre);
     __syncthreads();  // every wave is done with K buffer 0 before it is refilled
     for (int j = 0; j < nt; j += 2) {
-      need = step(split_tag, S0{}, j, sa, sb, m_pend);
+      need = step(split_tag, S0{}, j, sa, sb, m_pend, bpre);
       if (need) rescale(m_pend);
       if (j + 1 < nt) {
-        need = step(split_tag, S1{}, j + 1, sb, sa, m_pend);
+        need = step(split_tag, S1{}, j + 1, sb, sa, m_pend, bpre);
         if (need) rescale(m_pend);
       }
     }
@@ -1383,9 +1414,9 @@ hipError_t launch_type(const KernelArgs& a, int dqk, int dv, bool bias, bool out
 
 int tile_bn(int in_dtype, int dqk, int dv) {
   if (in_dtype == kF32) return Geo<float, 64, 64>::BN;
-  if (dqk == 64 && dv == 64) return 32 * WaveBlocks<64, 64>::NMB;
-  if (dqk == 128 && dv == 128) return 32 * WaveBlocks<128, 128>::NMB;
-  return 32 * WaveBlocks<192, 128>::NMB;
+  if (dqk == 64 && dv == 64) return WaveBlocks<64, 64>::kReportBN;
+  if (dqk == 128 && dv == 128) return WaveBlocks<128, 128>::kReportBN;
+  return WaveBlocks<192, 128>::kReportBN;
 }
 
 int tile_bm(int in_dtype, int dqk, int dv) {

@@ -76,10 +76,10 @@ enum { MI_ATTN_F32 = 0, MI_ATTN_F16 = 1, MI_ATTN_BF16 = 2 };
  *                16-byte aligned, strides multiples of 4.  Values must be
  *                finite or -inf.
  *   tile_counts  optional int32 [hq * num_seqs * n_qtiles] (debug): for every
- *                workgroup, the number of key tiles its loop visited, at
- *                index (qtile * num_seqs + seq) * hq + head, where
- *                n_qtiles = ceil(max_seqlen_q / BM) and BM, BN come from
- *                mi_attn_tile_shape.  NULL in normal use.
+ *                workgroup, the number of BN-key tiles spanned by the keys
+ *                its loop visited, at index (qtile * num_seqs + seq) * hq +
+ *                head, where n_qtiles = ceil(max_seqlen_q / BM) and BM, BN
+ *                come from mi_attn_tile_shape.  NULL in normal use.
  *
  * Sizes: num_seqs >= 0, max_seqlen_q >= every sequence's query length,
  * total_q / total_kv = cu_seqlens_q[num_seqs] / cu_seqlens_kv[num_seqs],
@@ -142,8 +142,10 @@ const char* mi_attn_last_error(void);
 int mi_attn_version(void);
 
 /*
- * Tile shape the kernel uses for (in_dtype, d_qk, d_v): *bm query rows per
- * workgroup and *bn keys per key tile.  Returns MI_ATTN_OK, or
+ * Tile shape the kernel uses for (in_dtype, d_qk, d_v) without a bias:
+ * *bm query rows per workgroup and *bn keys per key tile (with a bias the
+ * 16-bit kernel for d_qk = 128 steps through 32-key halves of these tiles;
+ * tile_counts are still given in *bn units).  Returns MI_ATTN_OK, or
  * MI_ATTN_ERR_UNSUPPORTED for a combination outside the supported set.
  */
 int mi_attn_tile_shape(int32_t in_dtype, int32_t d_qk, int32_t d_v, int32_t* bm, int32_t* bn);

@@ -171,6 +171,33 @@ def test_tile_schedule_visits_exactly_the_needed_tiles(shape, dtype):
             assert np.all(got[t, s, :] == -1)
 
 
+@pytest.mark.parametrize("shape", ["causal_self", "causal_kv_longer", "window_self", "window_cross"])
+def test_tile_schedule_with_bias_d128(shape):
+    """With a bias the 128-wide 16-bit kernel walks 32-key half tiles; the
+    debug counts are still reported in mi_attn_tile_shape's BN units and must
+    equal the BN-tiles spanned by the visible keys (a zero bias shared by
+    every head, so the head-major schedule is used too)."""
+    w = _probe_workload(MASK_SHAPES[shape], dtype="bf16", d=128)
+    say(f"[probe] tiles with bias {shape}")
+    bm, bn = fav.mi_attn_tile_shape(fav.BF16, 128, 128)
+    nqt = (w.max_seqlen_q + bm - 1) // bm
+    counts = torch.full((nqt * w.num_seqs * w.hq,), -1, dtype=torch.int32, device="cuda")
+    inp = workloads.make_inputs(w)
+    cols = (max(w.seqlens_kv) + 3) // 4 * 4  # row stride: a multiple of 4 elements
+    inp.bias = torch.zeros(w.total_q, 1, cols, dtype=torch.float32)
+    run_gpu(inp, out_dtype=torch.float32, tile_counts=counts)
+    got = counts.cpu().numpy().reshape(nqt, w.num_seqs, w.hq)
+    for s, vis in enumerate(_counts(w)):
+        lq = w.seqlens_q[s]
+        for t in range((lq + bm - 1) // bm):
+            rows = vis[t * bm:(t + 1) * bm]
+            keys = np.nonzero(rows.any(axis=0))[0]
+            expect = (int(keys.max()) // bn - int(keys.min()) // bn + 1) if len(keys) else 0
+            assert np.all(got[t, s, :] == expect), (s, t, got[t, s], expect)
+        for t in range((lq + bm - 1) // bm, nqt):
+            assert np.all(got[t, s, :] == -1)
+
+
 def test_window_cost_scales_with_window():
     """Visited tiles per query tile of a 16384-token sequence track W, not L."""
     totals = {}
