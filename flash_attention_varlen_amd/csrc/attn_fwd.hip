@@ -982,6 +982,9 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     l_run[n] = 0.0f;     // this lane's share of the running sum
   }
   const float c_scale = a.scale_log2;
+  // With a bias, logits stay in natural units (scale s + b, one fma) until
+  // the exponent's argument multiplies them by log2(e).
+  const float c_nat = a.scale_log2 * (1.0f / kLog2e);
   const float* brow[NB];
   if constexpr (BIAS) {
 #pragma unroll
@@ -1047,7 +1050,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const float m_all = mx[n];
-      const float m_tile = BIAS ? m_all : m_all * c_scale;
+      const float m_tile = BIAS ? m_all * kLog2e : m_all * c_scale;
       if (m_run[n] == kNegInf) m_run[n] = m_tile;
       m_pend[n] = m_tile;
       grow = grow || (m_tile > m_run[n] + kGrowBound);
@@ -1094,7 +1097,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               sc[n][mb][4 * qd + e] =
-                  __builtin_fmaf(sc[n][mb][4 * qd + e], c_scale, bv[n][mb][qd][e] * kLog2e);
+                  __builtin_fmaf(sc[n][mb][4 * qd + e], c_nat, bv[n][mb][qd][e]);
     }
     float mx[NB];
 #pragma unroll
@@ -1137,9 +1140,9 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     constexpr int NQK = NKF * NB;         // QK^T MFMAs per tile
     constexpr int NVF = NKS * NDB;        // V^T fragments per tile
     constexpr int NPV = NVF * NB;         // PV MFMA slots per tile (x2 with the split)
-    // Without a bias the next tile's masking and row max run inside the
-    // stream (after its last QK^T MFMAs); with one they follow the stream.
-    constexpr bool MAXOPS = !BIAS;
+    // The next tile's masking, bias and row max run inside the stream, in
+    // pieces after each key block's last QK^T MFMA.
+    constexpr bool MAXOPS = true;
     using Plan = StreamPlan<NQK, NPV, NB, NDB, NKS, NMB, MAXOPS>;
     const int nt = t_end - t_begin;
     const int t = t_begin + j;
@@ -1223,17 +1226,28 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
         f32x16_t& v = s_nxt[n][mb];
         float* mp = mpart[n][mb];
         // (empty asm fences keep each piece at its slot, as in the chunks)
+        // With a bias the entries become logits (natural units) first.
+        auto add_bias = [&](int e0, int e1) __attribute__((device)) {
+          if constexpr (BIAS) {
+#pragma unroll
+            for (int e = e0; e < e1; ++e)
+              v[e] = __builtin_fmaf(v[e], c_nat, bpre[n][mb][e / 4][e % 4]);
+          }
+        };
         if constexpr (piece == 0) {
           if (mask_next) mask_block(t + 1, v, n, mb);
+          add_bias(0, 6);
           mp[0] = max3f(v[0], v[1], v[2]);
           mp[1] = max3f(v[3], v[4], v[5]);
           asm volatile("" : "+v"(mp[0]), "+v"(mp[1]));
         } else if constexpr (piece == 1) {
+          add_bias(6, 15);
           mp[2] = max3f(v[6], v[7], v[8]);
           mp[3] = max3f(v[9], v[10], v[11]);
           mp[4] = max3f(v[12], v[13], v[14]);
           asm volatile("" : "+v"(mp[2]), "+v"(mp[3]), "+v"(mp[4]));
         } else {
+          add_bias(15, 16);
           const float m = __builtin_fmaxf(max3f(mp[0], mp[1], mp[2]), max3f(mp[3], mp[4], v[15]));
           mxp[n] = mb == 0 ? m : __builtin_fmaxf(mxp[n], m);
           asm volatile("" : "+v"(mxp[n]));
@@ -1254,9 +1268,9 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
         // entries 8 (kk % 2) + 2 w, +1 (keys 16 kk + {2w, 2w+1 | +8} + 4 hf)
         const int kk = ix / (4 * NB), n = (ix / 4) % NB, w = ix % 4;
         const int mb = kk >> 1, e0 = 8 * (kk & 1) + 2 * w;
-        const float x0 = BIAS ? s_cur[n][mb][e0] + neg_m[n] : __builtin_fmaf(s_cur[n][mb][e0], c_scale, neg_m[n]);
-        const float x1 = BIAS ? s_cur[n][mb][e0 + 1] + neg_m[n]
-                              : __builtin_fmaf(s_cur[n][mb][e0 + 1], c_scale, neg_m[n]);
+        const float cx = BIAS ? kLog2e : c_scale;
+        const float x0 = __builtin_fmaf(s_cur[n][mb][e0], cx, neg_m[n]);
+        const float x1 = __builtin_fmaf(s_cur[n][mb][e0 + 1], cx, neg_m[n]);
         const float p0 = fast_exp2(x0);
         const float p1 = fast_exp2(x1);
         lsum[n] += p0;
@@ -1278,7 +1292,6 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     });
 #pragma unroll
     for (int n = 0; n < NB; ++n) l_run[n] += lsum[n];
-    if constexpr (!MAXOPS) grow = has_next ? prep_tile(t + 1, s_nxt, m_pend, bpre) : false;
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of V(t+1), K(t+2) have landed
     __syncthreads();
     return grow;
