@@ -84,7 +84,7 @@ def test_small_case_matches_oracle(name):
 
 
 @pytest.mark.parametrize("bias_heads", [1, "hq"])
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_random_bias_matches_oracle(dtype, bias_heads):
     w = W(name=f"random_bias_{dtype}", seqlens_q=(190, 75), seqlens_kv=(260, 75), hq=4, hkv=2,
           d_qk=128, d_v=128, dtype=dtype, causal=True, seed=30)
