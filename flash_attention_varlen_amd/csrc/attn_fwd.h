@@ -41,6 +41,7 @@ struct KernelArgs {
   int32_t split_bias;  // with a bias, split P on every tile (16-bit types)
   int32_t n_qtiles;    // query tiles of the longest sequence (grid.y unless head_major)
   int32_t head_major;  // 16-bit kernels: 1-D grid, all heads of a (sequence, tile) on one XCD
+  int32_t kv_rows;     // 16-bit kernels: > 0 = 1-D grid, this many rows of one head run together
 };
 
 // Keys per tile for an input type and head dims.
@@ -50,7 +51,8 @@ int tile_bn(int in_dtype, int dqk, int dv);
 int tile_bm(int in_dtype, int dqk, int dv);
 
 // Launch on `stream`; grid = (hq * num_seqs, n_qtiles), or with head_major
-// (hq * (num_seqs * n_qtiles rounded up to a multiple of 8), 1).
+// (hq * (num_seqs * n_qtiles rounded up to a multiple of 8), 1), or with
+// kv_rows = R (hq * num_seqs * (n_qtiles rounded up to a multiple of R), 1).
 hipError_t launch_attn_fwd(const KernelArgs& a, int in_dtype, int out_dtype, int dqk, int dv,
                            bool bias, dim3 grid, hipStream_t stream);
 

@@ -813,8 +813,30 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   // numbered tile-major (sequence fastest), counting tiles down from the
   // last as above; with a few sequences the groups an XCD holds at one time
   // are tiles of the same sequence and share its K/V.
+  //
+  // With many heads and no kv sharing between them (kv_rows = R > 0, one-
+  // dimensional grid), one row holds more items per XCD than the XCD runs at
+  // once, so concurrent items would all read different K/V.  Instead XCD c
+  // takes its (sequence, head) slots R rows at a time: slot 0 for rows
+  // 0..R-1, slot 1 for rows 0..R-1, ..., then rows R..2R-1, so the R query
+  // tiles of one head that run together share their K/V through L2.  Rows
+  // still count down from the last tile, R at a time.
   int seq, head, by;
-  if (a.head_major) {
+  if (a.kv_rows > 0) {
+    const int R = a.kv_rows;
+    const int per_xcd = (a.hq * a.num_seqs) >> 3;  // (sequence, head) slots per XCD
+    const int k = (int)(blockIdx.x >> 3);
+    const int sr = k / (per_xcd * R);
+    const int rem = k - sr * (per_xcd * R);
+    const int slot = rem / R;
+    by = sr * R + (rem - slot * R);
+    if (by >= a.n_qtiles) return;  // padding rows of the last group of R
+    const int bx = slot * 8 + (int)(blockIdx.x & 7);
+    const int hx = bx % a.hq;
+    seq = bx / a.hq;
+    head = hx;
+    if ((a.hq & 7) == 0) head = (hx & 7) * (a.hq >> 3) + (hx >> 3);
+  } else if (a.head_major) {
     const int k = (int)(blockIdx.x >> 3);
     const int kg = k / a.hq;
     head = k - kg * a.hq;

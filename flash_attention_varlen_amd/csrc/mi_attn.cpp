@@ -225,7 +225,17 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
   const int64_t hm_wgs = (int64_t)p->hq * groups8;
   a.head_major = (dt != MI_ATTN_F32 && has_bias && p->bias_heads == 1 && p->hq > 1 &&
                   hm_wgs <= (int64_t)INT32_MAX / 256) ? 1 : 0;
-  const dim3 grid = a.head_major ? dim3((unsigned)hm_wgs, 1u) : dim3((unsigned)grid_x, (unsigned)n_qtiles);
+  // Many heads without kv sharing (16-bit kernels): more items per row and
+  // XCD (hq * num_seqs / 8) than the 64 an XCD holds at once means that the
+  // items running together would each stream different K/V; run kKvRows rows
+  // of one head together instead so that they share it through L2.
+  constexpr int64_t kKvRows = 4;
+  const int64_t kv_rows_wgs = grid_x * ((n_qtiles + kKvRows - 1) / kKvRows * kKvRows);
+  a.kv_rows = (!a.head_major && dt != MI_ATTN_F32 && p->hq == p->hkv && grid_x % 8 == 0 &&
+               grid_x / 8 >= 64 && kv_rows_wgs <= (int64_t)INT32_MAX / 256) ? (int32_t)kKvRows : 0;
+  const dim3 grid = a.head_major ? dim3((unsigned)hm_wgs, 1u)
+                    : a.kv_rows   ? dim3((unsigned)kv_rows_wgs, 1u)
+                                  : dim3((unsigned)grid_x, (unsigned)n_qtiles);
   hipError_t e = mi_attn::launch_attn_fwd(a, dt, p->out_dtype, p->d_qk, p->d_v, has_bias, grid,
                                           reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));

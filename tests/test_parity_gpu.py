@@ -114,6 +114,20 @@ def test_broadcast_bias_mixed_lengths(dims):
     check(w.name, out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, w.dtype)
 
 
+def test_many_heads_without_kv_sharing():
+    """hq = hkv with hq * num_seqs >= 512 takes the schedule that runs several
+    query tiles of one head together; varlen lengths leave empty items and a
+    partial last group of rows."""
+    w = W(name="mha_many_heads", seqlens_q=(300, 1, 129, 700, 64, 5, 257, 513),
+          seqlens_kv=(300, 1, 129, 700, 64, 5, 257, 513), hq=64, hkv=64, d_qk=64, d_v=64,
+          dtype="bf16", causal=True, seed=36)
+    say(f"[small] {w.name}")
+    inp = workloads.make_inputs(w)
+    out, lse = run_gpu(inp, out_dtype=torch.float32)
+    ref_out, ref_lse = run_oracle(inp)
+    check(w.name, out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, w.dtype)
+
+
 def test_outlier_channels_fp32_accumulation():
     """A few channels of magnitude 1e2..1e3: 16-bit accumulation would
     overflow; fp32 accumulation must keep the result finite and correct."""
