@@ -128,6 +128,33 @@ def test_many_heads_without_kv_sharing():
     check(w.name, out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, w.dtype)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_late_dominant_key(dtype, d):
+    """One key in a later tile dominates most rows (weight up to ~1) and its
+    value is large.  Its p must come out exactly 1 (running max up to date):
+    a stale running max leaves it at 2^f, f fractional, and its 16-bit
+    rounding then shows up at ~0.4% of |v| (bf16), above the tolerance."""
+    lens = (300, 190)
+    w = W(name=f"late_dominant_{dtype}_d{d}", seqlens_q=lens, seqlens_kv=lens, hq=2, hkv=2,
+          d_qk=d, d_v=d, dtype=dtype, causal=False, seed=37)
+    say(f"[small] {w.name}")
+    inp = workloads.make_inputs(w)
+    rng = np.random.default_rng(38)
+    u = np.ones(d) / math.sqrt(d)
+    q = inp.q.double().numpy() + 3.0 * u
+    k = inp.k.double().numpy()
+    v = inp.v.double().numpy()
+    for s0, key in ((0, 200), (300, 150)):  # a key in the fourth / third 64-key tile
+        k[s0 + key] = 2.2 * math.sqrt(d) * u + 0.3 * rng.standard_normal((w.hkv, d))
+        v[s0 + key] = 3.0
+    dt = inp.q.dtype
+    inp.q, inp.k, inp.v = (torch.from_numpy(x).to(dt) for x in (q, k, v))
+    out, lse = run_gpu(inp, out_dtype=torch.float32)
+    ref_out, ref_lse = run_oracle(inp)
+    check(w.name, out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, w.dtype)
+
+
 def test_outlier_channels_fp32_accumulation():
     """A few channels of magnitude 1e2..1e3: 16-bit accumulation would
     overflow; fp32 accumulation must keep the result finite and correct."""
