@@ -185,6 +185,8 @@ def main():
                     help="query heads per sequence the CPU oracle baseline covers")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
+    ap.add_argument("--window", type=int, default=None,
+                    help="override the window width of a sliding-window workload (cost vs W)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -195,6 +197,13 @@ def main():
         sys.exit(2)
 
     w = workloads.ALL[args.workload]
+    if args.window is not None:
+        if not w.window or args.window < 1:
+            print("--window applies to a sliding-window workload, with W >= 1", file=sys.stderr)
+            sys.exit(2)
+        base = w.name[:w.name.rfind("_w")] if "_w" in w.name else w.name
+        w = w.with_(name=f"{base}_w{args.window}", window=args.window,
+                    description=f"{w.description}, window overridden to {args.window}")
     print(f"# workload {w.name}: {w.description}", file=sys.stderr, flush=True)
     inp = workloads.make_inputs(w)
 
@@ -261,7 +270,8 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     out_bytes = out.element_size()
-    traffic = stored_traffic(args.workload)
+    # stored counter readings belong to the workload as defined (not to an overridden window)
+    traffic = stored_traffic(args.workload) if args.window is None else None
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
