@@ -1389,6 +1389,15 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
       constexpr int RPI = 64 / OUT_CPR;  // rows per wave-wide pass
       const int cc = lane % OUT_CPR;
       const int qb = w0 + 32 * n + pass * STAGE_ROWS;  // first row of this pass
+      // The pass's rows through one buffer window: rows past the sequence
+      // end fall outside it and their stores are dropped.
+      const int o_rows = min(max(lq - qb, 0), STAGE_ROWS);
+      const int64_t o_st_b = a.o_st * (int64_t)sizeof(OutT);
+      const char* obase = uniform_ptr(reinterpret_cast<const char*>(a.out) +
+                                      ((int64_t)(cq0 + qb) * a.o_st + (int64_t)head * a.o_sh) *
+                                          (int64_t)sizeof(OutT));
+      const __amdgpu_buffer_rsrc_t orsrc =
+          make_rsrc(obase, o_rows > 0 ? (uint32_t)((o_rows - 1) * o_st_b + OUT_RB) : 0u);
 #pragma unroll
       for (int it = 0; it < (STAGE_ROWS + RPI - 1) / RPI; ++it) {
         const int q = it * RPI + lane / OUT_CPR;
@@ -1396,12 +1405,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
         if (q < STAGE_ROWS) {
           const u32x4_t val =
               *(const __attribute__((address_space(3))) u32x4_t*)(ostage + q * OUT_RB + c * 16);
-          if (qb + q < lq) {
-            char* dst = reinterpret_cast<char*>(a.out) +
-                        ((int64_t)(cq0 + qb + q) * a.o_st + (int64_t)head * a.o_sh) * (int64_t)sizeof(OutT) +
-                        cc * 16;
-            *reinterpret_cast<u32x4_t*>(dst) = val;
-          }
+          __builtin_amdgcn_raw_buffer_store_b128(val, orsrc, (int)(q * o_st_b) + cc * 16, 0, 0);
         }
       }
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);

@@ -158,6 +158,12 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
       p->out_stride_head % out_mult != 0)
     return fail(MI_ATTN_ERR_INVALID_ARG, "out strides must be non-negative multiples of %lld",
                 (long long)out_mult);
+  // Output rows must not overlap; the 16-bit kernels store 32-row blocks
+  // through 32-bit buffer offsets.
+  if (p->out_stride_tok < p->d_v)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "out token stride must be >= d_v");
+  if (dt != MI_ATTN_F32 && p->out_stride_tok * elem_size(p->out_dtype) * 32 > INT32_MAX)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "out token stride too large (more than 64 MiB per token)");
   const bool has_bias = p->bias != nullptr;
   if (has_bias) {
     if (p->bias_heads != 1 && p->bias_heads != p->hq)

@@ -104,6 +104,8 @@ REFUSALS = {
     "bias_stride": (dict(bias=1 << 20, bias_heads=1, bias_cols=64, bias_stride_tok=66,
                          bias_stride_head=0), fav.ERR_INVALID_ARG),
     "too_many_q_tiles": (dict(max_seqlen_q=128 * 65536), fav.ERR_UNSUPPORTED),
+    "overlapping_out_rows": (dict(out_stride_tok=64, out_stride_head=8), fav.ERR_UNSUPPORTED),
+    "huge_out_stride": (dict(out_stride_tok=1 << 26), fav.ERR_UNSUPPORTED),
 }
 
 
