@@ -737,12 +737,14 @@ struct WaveBlocks {
   static constexpr int NB = 1;
   // 32-key tiles where 64 would not fit the registers: the 192-wide head,
   // and the 128-wide head with a bias (whose next tile's bias values are
-  // held in registers through a step).
-  static constexpr int NMB = (DQK > 128 || (BIAS && DQK == 128)) ? 1 : 2;
+  // held in registers through a step).  The 64-wide head without a bias
+  // has room for 128-key tiles, which halves its per-tile overheads (barrier,
+  // max exchange, copy issue) per key.
+  static constexpr int NMB = (DQK > 128 || (BIAS && DQK == 128)) ? 1 : (DQK == 64 && !BIAS) ? 4 : 2;
   static constexpr int OCC = 2;
   // keys per tile as reported by mi_attn_tile_shape (tile counts are given
   // in these units): the bias-free tile
-  static constexpr int kReportBN = 32 * (DQK > 128 ? 1 : 2);
+  static constexpr int kReportBN = 32 * (DQK > 128 ? 1 : DQK == 64 ? 4 : 2);
 };
 
 template <typename T, int DQK, int DV, bool BIAS, typename OutT>
