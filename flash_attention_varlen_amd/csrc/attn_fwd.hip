@@ -742,6 +742,10 @@ struct WaveBlocks {
   // max exchange, copy issue) per key.
   static constexpr int NMB = (DQK > 128 || (BIAS && DQK == 128)) ? 1 : (DQK == 64 && !BIAS) ? 4 : 2;
   static constexpr int OCC = 2;
+  // K/V buffer slots.  With 32-key tiles four of each fit the LDS of two
+  // workgroups per CU; then copies run one more step ahead and the
+  // workgroup synchronises every second step instead of every step.
+  static constexpr int NSLOT = NMB == 1 ? 4 : 2;
   // keys per tile as reported by mi_attn_tile_shape (tile counts are given
   // in these units): the bias-free tile
   static constexpr int kReportBN = 32 * (DQK > 128 ? 1 : DQK == 64 ? 4 : 2);
@@ -780,14 +784,21 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   constexpr int STAGE_ROWS = 32 * OUT_RB <= STAGE_BYTES ? 32 : STAGE_BYTES / OUT_RB;
   static_assert(STAGE_ROWS >= 1 && 32 % STAGE_ROWS == 0, "output staging");
 
-  // K and V double buffers as four separate LDS objects.  Each access names
-  // its buffer at compile time, so the compiler can tell that reads of the
-  // current tiles do not overlap the copies in flight into the other buffers
-  // and does not wait for those copies before reading.
+  // K and V buffers (NSLOT of each) as separate LDS objects.  Each access
+  // names its buffer at compile time, so the compiler can tell that reads of
+  // the current tiles do not overlap the copies in flight into the other
+  // buffers and does not wait for those copies before reading.
+  constexpr int NSLOT = WaveBlocks<DQK, DV, BIAS>::NSLOT;
+  constexpr int K_BYTES_HI = NSLOT == 4 ? K_BYTES : 16;  // slots 2 and 3
+  constexpr int V_BYTES_HI = NSLOT == 4 ? V_BYTES : 16;
   __shared__ __attribute__((aligned(1024))) char kbuf_0[K_BYTES];
   __shared__ __attribute__((aligned(1024))) char kbuf_1[K_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf_0[V_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf_1[V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf_2[K_BYTES_HI];
+  __shared__ __attribute__((aligned(1024))) char kbuf_3[K_BYTES_HI];
+  __shared__ __attribute__((aligned(1024))) char vbuf_2[V_BYTES_HI];
+  __shared__ __attribute__((aligned(1024))) char vbuf_3[V_BYTES_HI];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -939,12 +950,20 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   }
   // buffer of compile-time slot S
   auto kbuf = [&](auto S) __attribute__((device)) -> lds_char* {
-    if constexpr (decltype(S)::value == 0) return (lds_char*)kbuf_0;
-    else return (lds_char*)kbuf_1;
+    constexpr int i = decltype(S)::value;
+    static_assert(i < NSLOT, "K slot");
+    if constexpr (i == 0) return (lds_char*)kbuf_0;
+    else if constexpr (i == 1) return (lds_char*)kbuf_1;
+    else if constexpr (i == 2) return (lds_char*)kbuf_2;
+    else return (lds_char*)kbuf_3;
   };
   auto vbuf = [&](auto S) __attribute__((device)) -> lds_char* {
-    if constexpr (decltype(S)::value == 0) return (lds_char*)vbuf_0;
-    else return (lds_char*)vbuf_1;
+    constexpr int i = decltype(S)::value;
+    static_assert(i < NSLOT, "V slot");
+    if constexpr (i == 0) return (lds_char*)vbuf_0;
+    else if constexpr (i == 1) return (lds_char*)vbuf_1;
+    else if constexpr (i == 2) return (lds_char*)vbuf_2;
+    else return (lds_char*)vbuf_3;
   };
   auto load_k = [&](int t, auto S) __attribute__((device)) {
     load_tile_part<DQK, KLOADS>(kbase, k_st_b, t * BN, min(lk - t * BN, BN), kbuf(S) + wave * 1024, koff);
@@ -1170,23 +1189,36 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     using Plan = StreamPlan<NQK, NPV, NB, NDB, NKS, NMB, MAXOPS>;
     const int nt = t_end - t_begin;
     const int t = t_begin + j;
-    // slot = j & 1 (j runs even, odd, even, ... in the caller's unrolled loop)
+    // slot = j % NSLOT (the caller's loop is unrolled NSLOT times).  K(t+u)
+    // lives in K slot (slot + u) % NSLOT and V(t+u) in V slot
+    // (slot + u) % NSLOT.  This step reads K(t+1) and V(t) and starts the
+    // copies of K(t+LK) and V(t+LV), into the slots of the tiles read
+    // NSLOT - LK + 1 steps earlier.  With two slots every step ends with a
+    // barrier; with four, copies start one step further ahead and only odd
+    // steps end with one.  Either way a barrier separates the last read of a
+    // slot from the copy that refills it, and the end of a copy (each wave's
+    // vmcnt wait at its step's end) from the first read of its tile.
     constexpr int slot = decltype(slot_tag)::value;
-    using Cur = std::integral_constant<int, slot>;
-    using Oth = std::integral_constant<int, slot ^ 1>;
-    if (j + 1 < nt) load_v(t + 1, Oth{});
-    if (j + 2 < nt) load_k(t + 2, Cur{});
+    constexpr int LK = NSLOT == 4 ? 3 : 2;  // K copies run LK tiles ahead
+    constexpr int LV = LK - 1;              // V copies LV tiles ahead
+    using KR = std::integral_constant<int, (slot + 1) % NSLOT>;
+    using VR = std::integral_constant<int, slot>;
+    using KW = std::integral_constant<int, (slot + LK) % NSLOT>;
+    using VW = std::integral_constant<int, (slot + LV) % NSLOT>;
+    constexpr bool BAR = NSLOT == 2 || (slot & 1) != 0;
+    if (j + LV < nt) load_v(t + LV, VW{});
+    if (j + LK < nt) load_k(t + LK, KW{});
     if (t >= wt_end) {  // nothing visible to this wave from here on
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      __syncthreads();
+      if constexpr (BAR) __syncthreads();
       return false;
     }
     if constexpr (BIAS) {
       if (j + 1 < nt) load_bias(t + 1, bpre);
     }
 
-    const lds_char* kt = kbuf(Oth{});
-    const lds_char* vt = vbuf(Cur{});
+    const lds_char* kt = kbuf(KR{});
+    const lds_char* vt = vbuf(VR{});
     // K fragment fi: d-step fi / NMB, key block fi % NMB
     auto kread = [&](int fi) __attribute__((device)) -> u32x4_t {
       const int kk = fi / NMB, mb = fi % NMB;
@@ -1316,8 +1348,8 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     });
 #pragma unroll
     for (int n = 0; n < NB; ++n) l_run[n] += lsum[n];
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of V(t+1), K(t+2) have landed
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of V(t+LV), K(t+LK) have landed
+    if constexpr (BAR) __syncthreads();
     return grow;
   };
 
@@ -1328,6 +1360,11 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     load_k(t_begin, S0{});
     load_v(t_begin, S0{});
     if (nt > 1) load_k(t_begin + 1, S1{});
+    if constexpr (NSLOT == 4) {  // copies run a step further ahead
+      using S2 = std::integral_constant<int, 2>;
+      if (nt > 1) load_v(t_begin + 1, S1{});
+      if (nt > 2) load_k(t_begin + 2, S2{});
+    }
     // bias of the first tile: in flight together with the first copies
     f32x4_t bpre[NB][NMB][4];
     if constexpr (BIAS) load_bias(t_begin, bpre);
@@ -1338,13 +1375,37 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     qk_all(kbuf(S0{}), sa);
     bool need = prep_tile(t_begin, sa, m_pend, bpre);
     __syncthreads();  // every wave is done with K buffer 0 before it is refilled
-    for (int j = 0; j < nt; j += 2) {
-      need = step(split_tag, S0{}, j, sa, sb, m_pend, bpre);
-      if (need) rescale(m_pend);
-      if (j + 1 < nt) {
-        need = step(split_tag, S1{}, j + 1, sb, sa, m_pend, bpre);
+    if constexpr (NSLOT == 2) {
+      for (int j = 0; j < nt; j += 2) {
+        need = step(split_tag, S0{}, j, sa, sb, m_pend, bpre);
         if (need) rescale(m_pend);
+        if (j + 1 < nt) {
+          need = step(split_tag, S1{}, j + 1, sb, sa, m_pend, bpre);
+          if (need) rescale(m_pend);
+        }
       }
+    } else {
+      using S2 = std::integral_constant<int, 2>;
+      using S3 = std::integral_constant<int, 3>;
+      for (int j = 0; j < nt; j += 4) {
+        need = step(split_tag, S0{}, j, sa, sb, m_pend, bpre);
+        if (need) rescale(m_pend);
+        if (j + 1 < nt) {
+          need = step(split_tag, S1{}, j + 1, sb, sa, m_pend, bpre);
+          if (need) rescale(m_pend);
+        }
+        if (j + 2 < nt) {
+          need = step(split_tag, S2{}, j + 2, sa, sb, m_pend, bpre);
+          if (need) rescale(m_pend);
+        }
+        if (j + 3 < nt) {
+          need = step(split_tag, S3{}, j + 3, sb, sa, m_pend, bpre);
+          if (need) rescale(m_pend);
+        }
+      }
+      // the last step ended without a barrier when it was an even one: the
+      // epilogue reuses the buffers as staging
+      if (nt & 1) __syncthreads();
     }
   };
   if (t_begin < t_end) {
