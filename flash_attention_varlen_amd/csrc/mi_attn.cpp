@@ -235,7 +235,7 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
   // XCD (hq * num_seqs / 8) than the 64 an XCD holds at once means that the
   // items running together would each stream different K/V; run kKvRows rows
   // of one head together instead so that they share it through L2.
-  constexpr int64_t kKvRows = 4;
+  constexpr int64_t kKvRows = 8;
   const int64_t kv_rows_wgs = grid_x * ((n_qtiles + kKvRows - 1) / kKvRows * kKvRows);
   a.kv_rows = (!a.head_major && dt != MI_ATTN_F32 && p->hq == p->hkv && grid_x % 8 == 0 &&
                grid_x / 8 >= 64 && kv_rows_wgs <= (int64_t)INT32_MAX / 256) ? (int32_t)kKvRows : 0;
