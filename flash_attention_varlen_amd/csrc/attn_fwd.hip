@@ -742,10 +742,10 @@ struct WaveBlocks {
   // max exchange, copy issue) per key.
   static constexpr int NMB = (DQK > 128 || (BIAS && DQK == 128)) ? 1 : (DQK == 64 && !BIAS) ? 4 : 2;
   static constexpr int OCC = 2;
-  // K/V buffer slots.  With 32-key tiles four of each fit the LDS of two
-  // workgroups per CU; then copies run one more step ahead and the
-  // workgroup synchronises every second step instead of every step.
-  static constexpr int NSLOT = NMB == 1 ? 4 : 2;
+  // K/V buffer slots.  Where four of each fit the LDS of two workgroups per
+  // CU (80 KB each) copies run one more step ahead and the workgroup
+  // synchronises every second step instead of every step.
+  static constexpr int NSLOT = 4 * 32 * NMB * (DQK + DV) * 2 <= 80 * 1024 ? 4 : 2;
   // keys per tile as reported by mi_attn_tile_shape (tile counts are given
   // in these units): the bias-free tile
   static constexpr int kReportBN = 32 * (DQK > 128 ? 1 : DQK == 64 ? 4 : 2);
