@@ -155,6 +155,24 @@ def test_late_dominant_key(dtype, d):
     check(w.name, out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, w.dtype)
 
 
+@pytest.mark.parametrize("bias_heads", [1, "hq"])
+def test_many_heads_bias_window(bias_heads):
+    """Every schedule feature at once: 64 unshared heads over 8 varlen
+    sequences (row-grouped order, or head-major with a shared bias), a
+    sliding window, a bias with -inf entries, and the 128-wide head's
+    32-key four-slot tiles."""
+    lens = (300, 1, 129, 700, 64, 5, 257, 513)
+    w = W(name=f"mha_bias_window_{bias_heads}", seqlens_q=lens, seqlens_kv=lens, hq=64, hkv=64,
+          d_qk=128, d_v=128, dtype="bf16", causal=True, window=150, seed=39)
+    say(f"[bias] {w.name}")
+    inp = workloads.make_inputs(w)
+    nb = w.hq if bias_heads == "hq" else 1
+    inp.bias = workloads.random_bias(w.seqlens_q, nb, 704, seed=40, neg_inf_frac=0.05)
+    out, lse = run_gpu(inp, out_dtype=torch.float32)
+    ref_out, ref_lse = run_oracle(inp)
+    check(w.name, out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, w.dtype)
+
+
 def test_outlier_channels_fp32_accumulation():
     """A few channels of magnitude 1e2..1e3: 16-bit accumulation would
     overflow; fp32 accumulation must keep the result finite and correct."""
