@@ -185,6 +185,10 @@ def main():
                     help="query heads per sequence the CPU oracle baseline covers")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
+    ap.add_argument("--cold-steps", type=int, default=0,
+                    help="after the timed region, time this many launches each preceded by a "
+                         "write of --flush-mib MiB (evicts L2 and the MALL); reported under 'cold'")
+    ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--window", type=int, default=None,
                     help="override the window width of a sliding-window workload (cost vs W)")
     args = ap.parse_args()
@@ -273,6 +277,28 @@ def main():
     # stored counter readings belong to the workload as defined (not to an overridden window)
     traffic = stored_traffic(args.workload) if args.window is None else None
 
+    cold = None
+    if args.cold_steps > 0:
+        # Cold-cache launches: a large write between launches evicts L2 and the
+        # MALL (256 MB), so inputs come from HBM again.  Each launch is timed
+        # on its own; the flush is outside its events.
+        flush = torch.empty(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.cold_steps)]
+        for s_, e_ in cev:
+            flush.fill_(1.0)
+            s_.record(stream)
+            step()
+            e_.record(stream)
+        torch.cuda.synchronize()
+        cms = sorted(s_.elapsed_time(e_) for s_, e_ in cev)
+        cmean = sum(cms) / len(cms)
+        cold = {"launches": args.cold_steps, "flush_mib": args.flush_mib,
+                "kernel_ms": round(cmean, 4), "median_ms": round(cms[len(cms) // 2], 4),
+                "tflops": round(flops / (cmean * 1e-3) / 1e12, 2),
+                "algorithmic_gbps": round(algorithmic_bytes(w, out.element_size()) / (cmean * 1e-3) / 1e9, 1)}
+        del flush
+
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -322,6 +348,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if cold is not None:
+        result["cold"] = cold
     print(f"# GPU: {ms_per_step:.4f} ms/step, {value:.1f} useful TFLOP/s "
           f"({100 * value / peak:.1f}% of {peak} TFLOP/s)", file=sys.stderr, flush=True)
 
