@@ -3,8 +3,10 @@
 // One workgroup = 4 wave64s = BM = 128 query rows of one (sequence, query
 // head); each wave owns 32 rows.  The workgroup walks the key tiles of its
 // sequence that hold at least one visible key for its rows (diagonal skip
-// and window-band jump), staging K and V through LDS (double-buffered, the
-// next tile's HBM loads in flight while the current tile is computed).
+// and window-band jump), staging K and V through LDS (double-buffered, or
+// four buffers where they fit, the next tiles' HBM loads in flight while
+// the current tile is computed).  Key tiles are 64 keys (32 for the 192-wide
+// head and the biased 128-wide head, 128 for the bias-free 64-wide head).
 // Per tile and wave:
 //   S^T = K Q^T           on MFMA 32x32x16 (bf16/fp16) or 32x32x2 (fp32),
 //                         fp32 accumulate; keys on the M axis, queries on N,
@@ -12,7 +14,9 @@
 //   mask / bias / scale   fp32, masks only on boundary tiles;
 //   online softmax        fp32 running max and sum per row (the row max is
 //                         an in-lane reduction plus one exchange with the
-//                         lane 32 away, so all 64 lanes work);
+//                         lane 32 away, so all 64 lanes work); in the 16-bit
+//                         kernel the running max follows every increase, so
+//                         a row's largest p is exactly 1;
 //   O^T += V^T P^T        on MFMA, P rounded to the input type (RNE), with
 //                         a hi/lo split of P on tiles of rows that see few
 //                         keys.
