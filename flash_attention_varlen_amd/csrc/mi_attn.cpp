@@ -233,12 +233,15 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
                   hm_wgs <= (int64_t)INT32_MAX / 256) ? 1 : 0;
   // Many heads without kv sharing (16-bit kernels): more items per row and
   // XCD (hq * num_seqs / 8) than the 64 an XCD holds at once means that the
-  // items running together would each stream different K/V; run kKvRows rows
-  // of one head together instead so that they share it through L2.
+  // items running together would each stream different K/V; run up to
+  // kKvRows rows of one head together instead so that they share it through
+  // L2 (never more rows than there are, which would only add empty items).
   constexpr int64_t kKvRows = 8;
-  const int64_t kv_rows_wgs = grid_x * ((n_qtiles + kKvRows - 1) / kKvRows * kKvRows);
+  const int64_t kv_r = n_qtiles < kKvRows ? n_qtiles : kKvRows;
+  const int64_t kv_rows_wgs = kv_r > 0 ? grid_x * ((n_qtiles + kv_r - 1) / kv_r * kv_r) : 0;
   a.kv_rows = (!a.head_major && dt != MI_ATTN_F32 && p->hq == p->hkv && grid_x % 8 == 0 &&
-               grid_x / 8 >= 64 && kv_rows_wgs <= (int64_t)INT32_MAX / 256) ? (int32_t)kKvRows : 0;
+               grid_x / 8 >= 64 && kv_r >= 2 && kv_rows_wgs <= (int64_t)INT32_MAX / 256)
+                  ? (int32_t)kv_r : 0;
   const dim3 grid = a.head_major ? dim3((unsigned)hm_wgs, 1u)
                     : a.kv_rows   ? dim3((unsigned)kv_rows_wgs, 1u)
                                   : dim3((unsigned)grid_x, (unsigned)n_qtiles);

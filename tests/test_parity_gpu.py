@@ -114,12 +114,14 @@ def test_broadcast_bias_mixed_lengths(dims):
     check(w.name, out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, w.dtype)
 
 
-def test_many_heads_without_kv_sharing():
+@pytest.mark.parametrize("lens", [(300, 1, 129, 700, 64, 5, 257, 513),  # 6 q-tiles: groups of 6
+                                  (200, 1, 129, 256, 64, 5, 17, 3),     # 2 q-tiles: groups of 2
+                                  (100, 1, 128, 64, 64, 5, 17, 3)])     # 1 q-tile: plain order
+def test_many_heads_without_kv_sharing(lens):
     """hq = hkv with hq * num_seqs >= 512 takes the schedule that runs several
-    query tiles of one head together; varlen lengths leave empty items and a
-    partial last group of rows."""
-    w = W(name="mha_many_heads", seqlens_q=(300, 1, 129, 700, 64, 5, 257, 513),
-          seqlens_kv=(300, 1, 129, 700, 64, 5, 257, 513), hq=64, hkv=64, d_qk=64, d_v=64,
+    query tiles of one head together (as many as the longest sequence has,
+    up to 8); varlen lengths leave empty items."""
+    w = W(name="mha_many_heads", seqlens_q=lens, seqlens_kv=lens, hq=64, hkv=64, d_qk=64, d_v=64,
           dtype="bf16", causal=True, seed=36)
     say(f"[small] {w.name}")
     inp = workloads.make_inputs(w)
