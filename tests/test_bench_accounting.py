@@ -38,3 +38,21 @@ def test_multi_gpu_request_exits_with_message():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
                        text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_window_override_is_refused_for_windowless_workloads():
+    """--window only applies to a sliding-window workload; elsewhere bench.py
+    exits with status 2 before it does any work."""
+    import subprocess, sys, os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--workload", "gqa_causal_bf16",
+                        "--window", "64"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "--window" in r.stderr
+
+
+def test_window_override_changes_the_accounting():
+    w = workloads.SWA_BF16.with_(window=1024)
+    assert bench.useful_pairs(w) < bench.useful_pairs(workloads.SWA_BF16)
+    # each 16384-token causal sequence with W keys per row: W*(W+1)/2 + (L-W)*W per head
+    L, W = 16384, 1024
+    assert bench.useful_pairs(w) == 4 * 32 * (W * (W + 1) // 2 + (L - W) * W)
