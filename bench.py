@@ -37,7 +37,7 @@ METRIC = "attn fwd useful TFLOP/s + % of MI355X bf16 MFMA peak (causal GQA D=128
 # bf16/fp16; fp32 matrix 157.3.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 HBM_GBPS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "flash_attention_varlen_amd", "csrc", "attn_fwd.hip")
+KERNEL_SOURCE = os.path.join(ROOT, "flash_attention_varlen_amd", "csrc", "attn_fwd_kernels.h")
 PROFILES = os.path.join(ROOT, "profiles")
 
 

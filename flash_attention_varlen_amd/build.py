@@ -2,23 +2,31 @@
 
     python -m flash_attention_varlen_amd.build
 
-hipcc compiles every source for gfx950 only.  Packed fp32 VALU instructions
-are switched off (``-packed-fp32-ops``); hipcc's host pass warns that it does
-not know the feature, which is harmless.
+hipcc compiles every source for gfx950 only, one object per kernel instance
+unit (in parallel), then links them into one shared library.  Packed fp32
+VALU instructions are switched off (``-packed-fp32-ops``); hipcc's host pass
+warns that it does not know the feature, which is harmless.
 """
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmi_attn.so")
-SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "mi_attn.cpp")]
 ARCH = "gfx950"
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
+         "-packed-fp32-ops", "-Wall", "-Wno-pass-failed", "-Wno-unused-function",
+         "-Wno-cuda-compat", "-I", INCLUDE, "-I", CSRC]
+# Sources compiled once each.
+PLAIN = ["attn_fwd.hip", "mi_attn.cpp"]
 
 
 def hipcc() -> str:
@@ -27,22 +35,55 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the shared library; returns its path.  Always recompiles."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-Wno-pass-failed", "-Wno-unused-function",
-           "-I", INCLUDE, "-I", CSRC, "-x", "hip", SOURCES[0], "-x", "hip", SOURCES[1],
-           "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def instances():
+    """(tag, type, dqk, dv) of every forward kernel instance, read from the
+    MI_ATTN_FWD_INSTANCES list in attn_fwd.h."""
+    text = open(os.path.join(CSRC, "attn_fwd.h")).read()
+    body = text[text.index("#define MI_ATTN_FWD_INSTANCES(X)"):]
+    body = body[:body.index("\n#define", 1)]
+    return re.findall(r"X\((\w+), (\w+), (\d+), (\d+)\)", body)
+
+
+def compile_jobs(objdir: str):
+    jobs = []
+    for src in PLAIN:
+        obj = os.path.join(objdir, src + ".o")
+        jobs.append(([hipcc(), f"--offload-arch={ARCH}", *FLAGS, "-c", "-x", "hip",
+                      os.path.join(CSRC, src), "-o", obj], obj))
+    for tag, t, dqk, dv in instances():
+        obj = os.path.join(objdir, f"attn_fwd_inst_{tag}_{dqk}_{dv}.o")
+        jobs.append(([hipcc(), f"--offload-arch={ARCH}", *FLAGS, f"-DMI_ATTN_INST_TAG={tag}",
+                      f"-DMI_ATTN_INST_T={t}", f"-DMI_ATTN_INST_DQK={dqk}",
+                      f"-DMI_ATTN_INST_DV={dv}", "-c", "-x", "hip",
+                      os.path.join(CSRC, "attn_fwd_inst.hip"), "-o", obj], obj))
+    return jobs
+
+
+def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    lines = [l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l]
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
-    if verbose and lines:
-        print("\n".join(lines))
+    return r.returncode, [l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l]
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile the shared library; returns its path.  Always recompiles."""
+    jobs = jobs or min(16, os.cpu_count() or 1)
+    with tempfile.TemporaryDirectory(prefix="mi_attn_build_") as objdir:
+        todo = compile_jobs(objdir)
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(lambda j: _run(j[0]), todo))
+        for (cmd, _), (rc, lines) in zip(todo, results):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            if rc != 0:
+                raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(lines))
+            if verbose and lines:
+                print("\n".join(lines))
+        tmp = LIB + ".tmp"
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC",
+                *[obj for _, obj in todo], "-o", tmp]
+        rc, lines = _run(link)
+        if rc != 0:
+            raise RuntimeError("link failed:\n" + "\n".join(lines))
     os.replace(tmp, LIB)
     return LIB
 

@@ -50,6 +50,19 @@ int tile_bn(int in_dtype, int dqk, int dv);
 // Query rows per workgroup for an input type and head dims.
 int tile_bm(int in_dtype, int dqk, int dv);
 
+// The kernel instances, one per (element type, head dims) pair.  Each is
+// compiled in its own translation unit (attn_fwd_inst.hip, built once per
+// pair) and launches the template for (bias, out type) on `stream`.
+#define MI_ATTN_FWD_INSTANCES(X)                                                        \
+  X(bf16, __bf16, 64, 64) X(bf16, __bf16, 128, 128) X(bf16, __bf16, 192, 128)           \
+  X(f16, _Float16, 64, 64) X(f16, _Float16, 128, 128) X(f16, _Float16, 192, 128)        \
+  X(f32, float, 64, 64) X(f32, float, 128, 128)
+#define MI_ATTN_FWD_INSTANCE_NAME(tag, dqk, dv) launch_fwd_##tag##_##dqk##_##dv
+#define MI_ATTN_FWD_DECLARE(tag, T, dqk, dv)                                            \
+  hipError_t MI_ATTN_FWD_INSTANCE_NAME(tag, dqk, dv)(const KernelArgs& a, bool bias,   \
+                                                     bool out_f32, dim3 grid, hipStream_t s);
+MI_ATTN_FWD_INSTANCES(MI_ATTN_FWD_DECLARE)
+
 // Launch on `stream`; grid = (hq * num_seqs, n_qtiles), or with head_major
 // (hq * (num_seqs * n_qtiles rounded up to a multiple of 8), 1), or with
 // kv_rows = R (hq * num_seqs * (n_qtiles rounded up to a multiple of R), 1).

@@ -1,0 +1,1511 @@
+// Fused variable-length attention forward for gfx950 (MI355X, CDNA4).
+//
+// One workgroup = 4 wave64s = BM = 128 query rows of one (sequence, query
+// head); each wave owns 32 rows.  The workgroup walks the key tiles of its
+// sequence that hold at least one visible key for its rows (diagonal skip
+// and window-band jump), staging K and V through LDS (double-buffered, or
+// four buffers where they fit, the next tiles' HBM loads in flight while
+// the current tile is computed).  Key tiles are 64 keys (32 for the 192-wide
+// head and the biased 128-wide head, 128 for the bias-free 64-wide head).
+// Per tile and wave:
+//   S^T = K Q^T           on MFMA 32x32x16 (bf16/fp16) or 32x32x2 (fp32),
+//                         fp32 accumulate; keys on the M axis, queries on N,
+//                         so each lane holds one query column;
+//   mask / bias / scale   fp32, masks only on boundary tiles;
+//   online softmax        fp32 running max and sum per row (the row max is
+//                         an in-lane reduction plus one exchange with the
+//                         lane 32 away, so all 64 lanes work); in the 16-bit
+//                         kernel the running max follows every increase, so
+//                         a row's largest p is exactly 1;
+//   O^T += V^T P^T        on MFMA, P rounded to the input type (RNE), with
+//                         a hi/lo split of P on tiles of rows that see few
+//                         keys.
+// The method is the streaming-softmax forward described on the triton-msl
+// part-1 post (section "What works, and where the edges are": Q staged once,
+// one loop over K/V tiles doing QK^T, online softmax with running max and
+// sum and a rescale, then P.V, output accumulator resident throughout) with
+// the masking conventions of the mtlattn 0.3.0 project page (section "Use").
+// The exact diagonal skip follows the triton-msl part-2 post (section
+// "FlashAttention: faster than PyTorch, competitive with MLX").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "attn_fwd.h"
+
+namespace mi_attn {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt in 6:4, lgkmcnt in 11:8): wait for vmcnt == 0 / lgkmcnt == 0 only.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+// A running max is only raised when a tile's max exceeds it by more than
+// this many powers of two; until then p = exp2(t - m) stays below 2^8, which
+// fp32 sums and 16-bit P (8 exponent bits or more) hold without loss.
+constexpr float kRescaleThreshold = 8.0f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max(x, x of the lane 32 away).  v_permlane32_swap exchanges lanes 32-63 of
+// its first operand with lanes 0-31 of its second; given two copies of x it
+// leaves (low half of x in both halves, high half of x in both halves), whose
+// elementwise max is the pairwise max on every lane.  It is written as
+// inline assembly (with the two wait states a VALU write needs before the
+// swap reads it): the compiler builtin's second result was dropped from the
+// max by the optimiser.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  float lo = x, hi = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+  return __builtin_fmaxf(lo, hi);
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+}
+
+// Max of the 16 entries of one accumulator block as a tree (depth 3).
+__device__ __forceinline__ float max16(const f32x16_t& v) {
+  const float a0 = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
+  const float a1 = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
+  const float a2 = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
+  const float a3 = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), v[11]);
+  const float a4 = __builtin_fmaxf(__builtin_fmaxf(v[12], v[13]), v[14]);
+  const float b0 = __builtin_fmaxf(__builtin_fmaxf(a0, a1), a2);
+  const float b1 = __builtin_fmaxf(__builtin_fmaxf(a3, a4), v[15]);
+  return __builtin_fmaxf(b0, b1);
+}
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<__bf16> {
+  static constexpr bool kWide = false;  // 16-bit operands
+  __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  // Two fp32 -> two bf16 (round to nearest even), low half = lo.
+  __device__ static uint32_t pack(float lo, float hi) {
+    bf16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static float round_trip(float x) {
+    return (float)(__bf16)x;
+  }
+};
+
+template <>
+struct Elem<_Float16> {
+  static constexpr bool kWide = false;
+  __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  __device__ static uint32_t pack(float lo, float hi) {
+    f16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static float round_trip(float x) { return (float)(_Float16)x; }
+};
+
+template <>
+struct Elem<float> {
+  static constexpr bool kWide = true;  // 32-bit operands, 32x32x2 MFMA
+  __device__ static f32x16_t mma(float a, float b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Output stores: four consecutive head-dim values of one row.
+template <typename OutT>
+__device__ __forceinline__ void store4(OutT* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4_t*>(p) = (f32x4_t){a, b, c, d};
+}
+template <>
+__device__ __forceinline__ void store4<__bf16>(__bf16* p, float a, float b, float c, float d) {
+  u32x2_t w = {Elem<__bf16>::pack(a, b), Elem<__bf16>::pack(c, d)};
+  *reinterpret_cast<u32x2_t*>(p) = w;
+}
+template <>
+__device__ __forceinline__ void store4<_Float16>(_Float16* p, float a, float b, float c, float d) {
+  u32x2_t w = {Elem<_Float16>::pack(a, b), Elem<_Float16>::pack(c, d)};
+  *reinterpret_cast<u32x2_t*>(p) = w;
+}
+
+// Compile-time tile geometry.
+template <typename T, int DQK, int DV>
+struct Geo {
+  static constexpr bool kWide = Elem<T>::kWide;
+  static constexpr int BN = kWide ? 32 : 64;   // keys per tile
+  static constexpr int NMB = BN / 32;          // 32-key blocks of S^T
+  static constexpr int PAD = kWide ? 4 : 8;    // LDS row padding (elements)
+  static constexpr int KSTR = DQK + PAD;       // K tile row stride in LDS
+  // 16-bit: V is stored transposed (d rows, key positions); fp32: row-major.
+  static constexpr int VSTR = kWide ? DV + PAD : BN + PAD;
+  static constexpr int K_ELEMS = BN * KSTR;
+  static constexpr int V_ELEMS = kWide ? BN * VSTR : DV * VSTR;
+  static constexpr int STAGE = K_ELEMS + V_ELEMS;
+  static constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte chunk
+  static constexpr int KCPR = DQK / EPC;       // 16-byte chunks per K row
+  static constexpr int KPT = BN * KCPR / kThreads;  // K chunks per thread
+  static constexpr int VCPR = DV / EPC;
+  static constexpr int VPT_WIDE = BN * VCPR / kThreads;  // fp32 V chunks per thread
+  static constexpr int VOCT = DV / 8;          // 16-bit: d-octets per V row
+  static constexpr int VUNITS = 16 * VOCT;     // 16-bit: (key quad, d octet) units
+  static constexpr int KSTEPS = kWide ? DQK / 2 : DQK / 16;  // MFMA k-steps of QK^T
+  static constexpr int NDB = DV / 32;          // 32-row blocks of O^T
+  static_assert(BN * KCPR % kThreads == 0, "K staging must divide evenly");
+  static_assert(kWide ? (BN * VCPR % kThreads == 0) : (VUNITS <= kThreads), "V staging");
+};
+
+// ----------------------------------------------------------------------------
+// The kernel.
+// ----------------------------------------------------------------------------
+template <typename T, int DQK, int DV, bool BIAS, typename OutT>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs a) {
+  using G = Geo<T, DQK, DV>;
+  using E = Elem<T>;
+  constexpr int BN = G::BN;
+  constexpr int NMB = G::NMB;
+  constexpr bool kWide = G::kWide;
+  typedef typename std::conditional<kWide, float, uint16_t>::type Raw;
+
+  __shared__ __attribute__((aligned(16))) Raw smem[2 * G::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // The wave index is made a scalar so that every per-wave condition below
+  // (rows, tile range, masking, P split) is a uniform scalar branch.  MFMA
+  // writes all 64 lanes whatever EXEC holds, so an MFMA must never sit in a
+  // branch the compiler could execute with a partial or empty EXEC mask.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5;   // which half of the wave
+  const int l32 = lane & 31;  // column (query) index inside a 32-wide block
+
+  // ---- work decode: (q-tile counted from the end, sequence, head)
+  const int head = blockIdx.x % a.hq;
+  const int seq = blockIdx.x / a.hq;
+  const int cq0 = a.cu_q[seq];
+  const int lq = a.cu_q[seq + 1] - cq0;
+  const int ck0 = a.cu_kv[seq];
+  const int lk = a.cu_kv[seq + 1] - ck0;
+  const int n_qtiles = (lq + kBM - 1) / kBM;
+  const int qtile = n_qtiles - 1 - (int)blockIdx.y;  // heaviest causal tiles first
+  if (qtile < 0) return;
+
+  const int r0 = qtile * kBM;
+  const int r1 = min(lq, r0 + kBM);
+  const int off = lk - lq;  // end-aligned diagonal offset
+  const int g = head / a.group;
+  const bool causal = a.causal != 0;
+  const int W = a.window;
+
+  // Key range holding at least one visible key for rows [r0, r1).
+  int kv_hi = lk;
+  if (causal) kv_hi = min(lk, r1 - 1 + off + 1);
+  int kv_lo = 0;
+  if (W > 0) kv_lo = max(0, r0 + off - W + 1);
+  const int t_begin = kv_lo / BN;
+  int t_end = kv_hi > 0 ? (kv_hi + BN - 1) / BN : 0;
+  if (t_end < t_begin) t_end = t_begin;
+
+  if (a.tile_counts != nullptr && tid == 0 && qtile < (int)gridDim.y)
+    a.tile_counts[((int64_t)qtile * a.num_seqs + seq) * a.hq + head] = t_end - t_begin;
+
+  // ---- per-wave rows
+  const int w0 = r0 + wave * 32;
+  const int w1 = min(lq, w0 + 32);
+  const bool wave_active = w0 < lq;
+  const int my_row = w0 + l32;
+  const bool row_ok = my_row < lq;
+  int wkv_hi = lk;
+  if (causal) wkv_hi = min(lk, w1 - 1 + off + 1);
+  int wkv_lo = 0;
+  if (W > 0) wkv_lo = max(0, w0 + off - W + 1);
+
+  // Few visible keys for the wave's first row -> hi/lo split of P.
+  bool split = false;
+  if constexpr (!kWide) {
+    int nvis = (causal ? min(lk, w0 + off + 1) : lk) - wkv_lo;
+    split = (nvis < a.split_keys) || (BIAS && a.split_bias != 0);
+  }
+
+  const T* __restrict__ kbase = reinterpret_cast<const T*>(a.k) + (int64_t)ck0 * a.k_st +
+                                (int64_t)g * a.k_sh;
+  const T* __restrict__ vbase = reinterpret_cast<const T*>(a.v) + (int64_t)ck0 * a.v_st +
+                                (int64_t)g * a.v_sh;
+
+  // ---- Q fragments (MFMA B operand), loaded once.
+  typedef typename std::conditional<kWide, float, u32x4_t>::type QFrag;
+  QFrag qf[G::KSTEPS];
+  {
+    const T* qp = reinterpret_cast<const T*>(a.q) + (int64_t)(cq0 + my_row) * a.q_st +
+                  (int64_t)head * a.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < G::KSTEPS; ++ks) {
+      if constexpr (kWide) {
+        qf[ks] = row_ok ? reinterpret_cast<const float*>(qp)[2 * ks + hf] : 0.0f;
+      } else {
+        qf[ks] = row_ok ? *reinterpret_cast<const u32x4_t*>(qp + 16 * ks + 8 * hf)
+                        : (u32x4_t){0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  // ---- staging registers for one K/V tile
+  u32x4_t kreg[G::KPT];
+  constexpr int VREG = kWide ? G::VPT_WIDE : 4;
+  u32x4_t vreg[VREG];
+  const bool v_stager = kWide || tid < G::VUNITS;
+
+  auto load_tile = [&](int t) {
+    const int kb = t * BN;
+#pragma unroll
+    for (int i = 0; i < G::KPT; ++i) {
+      const int idx = tid + kThreads * i;
+      const int row = idx / G::KCPR;
+      const int c = idx % G::KCPR;
+      const int key = kb + row;
+      kreg[i] = key < lk ? *reinterpret_cast<const u32x4_t*>(kbase + (int64_t)key * a.k_st +
+                                                              G::EPC * c)
+                         : (u32x4_t){0u, 0u, 0u, 0u};
+    }
+    if constexpr (kWide) {
+#pragma unroll
+      for (int i = 0; i < VREG; ++i) {
+        const int idx = tid + kThreads * i;
+        const int row = idx / G::VCPR;
+        const int c = idx % G::VCPR;
+        const int key = kb + row;
+        vreg[i] = key < lk ? *reinterpret_cast<const u32x4_t*>(vbase + (int64_t)key * a.v_st +
+                                                                G::EPC * c)
+                           : (u32x4_t){0u, 0u, 0u, 0u};
+      }
+    } else {
+      if (v_stager) {
+        const int oc = tid % G::VOCT;
+        const int kq = tid / G::VOCT;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kb + 4 * kq + r;
+          vreg[r] = key < lk ? *reinterpret_cast<const u32x4_t*>(vbase + (int64_t)key * a.v_st +
+                                                                  8 * oc)
+                             : (u32x4_t){0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    Raw* ks = smem + buf * G::STAGE;
+    Raw* vs = ks + G::K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < G::KPT; ++i) {
+      const int idx = tid + kThreads * i;
+      const int row = idx / G::KCPR;
+      const int c = idx % G::KCPR;
+      *reinterpret_cast<u32x4_t*>(ks + row * G::KSTR + G::EPC * c) = kreg[i];
+    }
+    if constexpr (kWide) {
+#pragma unroll
+      for (int i = 0; i < VREG; ++i) {
+        const int idx = tid + kThreads * i;
+        const int row = idx / G::VCPR;
+        const int c = idx % G::VCPR;
+        *reinterpret_cast<u32x4_t*>(vs + row * G::VSTR + G::EPC * c) = vreg[i];
+      }
+    } else {
+      if (v_stager) {
+        // 4 keys x 8 head-dims in registers -> 8 rows of V^T, 4 keys each.
+        const int oc = tid % G::VOCT;
+        const int kq = tid / G::VOCT;
+        const int quad = kq & 3;
+        // Key positions inside each 16-key group follow the order in which
+        // the S^T accumulator hands keys to the P operand (see PV below):
+        // keys 0-3, 8-11, 4-7, 12-15.
+        const int pos = 16 * (kq >> 2) + 4 * (((quad & 1) << 1) | (quad >> 1));
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+          const int w = dd >> 1;
+          const int sh = (dd & 1) * 16;
+          const uint32_t e0 = (vreg[0][w] >> sh) & 0xffffu;
+          const uint32_t e1 = (vreg[1][w] >> sh) & 0xffffu;
+          const uint32_t e2 = (vreg[2][w] >> sh) & 0xffffu;
+          const uint32_t e3 = (vreg[3][w] >> sh) & 0xffffu;
+          u32x2_t pk = {e0 | (e1 << 16), e2 | (e3 << 16)};
+          *reinterpret_cast<u32x2_t*>(vs + (8 * oc + dd) * G::VSTR + pos) = pk;
+        }
+      }
+    }
+  };
+
+  // ---- accumulators
+  f32x16_t o[G::NDB];
+#pragma unroll
+  for (int i = 0; i < G::NDB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
+  float m_run = kNegInf;  // running max, log2 units (scale folded in)
+  float l_run = 0.0f;     // this lane's share of the running sum
+
+  const float c_scale = a.scale_log2;
+  const float* brow = nullptr;
+  if constexpr (BIAS) {
+    brow = a.bias + (int64_t)(cq0 + (row_ok ? my_row : 0)) * a.b_st +
+           (int64_t)(a.bias_heads == 1 ? 0 : head) * a.b_sh;
+  }
+
+  if (t_begin < t_end) {
+    load_tile(t_begin);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = (t - t_begin) & 1;
+    const bool has_next = t + 1 < t_end;
+    if (has_next) load_tile(t + 1);
+
+    const int kb = t * BN;
+    const bool wave_tile = wave_active && kb < wkv_hi && kb + BN > wkv_lo;
+    if (wave_tile) {
+      const Raw* ks = smem + buf * G::STAGE;
+      const Raw* vs = ks + G::K_ELEMS;
+
+      // ---- S^T = K Q^T (keys x queries), fp32
+      f32x16_t s[NMB];
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[mb][e] = 0.0f;
+#pragma unroll
+      for (int ks_ = 0; ks_ < G::KSTEPS; ++ks_) {
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          if constexpr (kWide) {
+            const float kf = ks[(32 * mb + l32) * G::KSTR + 2 * ks_ + hf];
+            s[mb] = E::mma(kf, qf[ks_], s[mb]);
+          } else {
+            const u32x4_t kf =
+                *reinterpret_cast<const u32x4_t*>(ks + (32 * mb + l32) * G::KSTR + 16 * ks_ + 8 * hf);
+            s[mb] = E::mma(kf, qf[ks_], s[mb]);
+          }
+        }
+      }
+
+      // ---- mask (boundary tiles only): sequence end, causal diagonal, window
+      const bool need_mask = (kb + BN > lk) || (causal && kb + BN - 1 > w0 + off) ||
+                             (W > 0 && kb <= w1 - 1 + off - W);
+      if (need_mask) {
+        const int lim_hi = causal ? my_row + off : lk - 1;
+        const int lim_lo = W > 0 ? my_row + off - W : -1;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kb + 32 * mb + 8 * (e >> 2) + 4 * hf + (e & 3);
+            const bool ok = key < lk && key <= lim_hi && key > lim_lo;
+            s[mb][e] = ok ? s[mb][e] : kNegInf;
+          }
+      }
+
+      // ---- logits in log2 units; bias added here
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int key0 = kb + 32 * mb + 8 * qd + 4 * hf;
+            f32x4_t bv;
+            if (row_ok && key0 + 3 < lk) {
+              bv = *reinterpret_cast<const f32x4_t*>(brow + key0);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) bv[e] = (row_ok && key0 + e < lk) ? brow[key0 + e] : 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              s[mb][4 * qd + e] = __builtin_fmaf(s[mb][4 * qd + e], c_scale, bv[e] * kLog2e);
+          }
+      }
+
+      // ---- row max: in-lane over this lane's keys, then with the lane 32 away
+      float mx = kNegInf;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_tile = BIAS ? mx : mx * c_scale;
+
+      // ---- online rescale.  Each row decides for itself (alpha = 1, an
+      // exact no-op, for rows whose max did not grow past the threshold), so
+      // a row's result never depends on the other rows of its wave; the
+      // wave only skips the work when no row needs it.
+      const bool grow = m_tile > m_run + kRescaleThreshold;
+      if (__ballot(grow) != 0ull) {
+        const float m_new = grow ? m_tile : m_run;
+        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < G::NDB; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+
+      // ---- p = exp2(t - m); fp32 partial row sum from the unrounded p
+      float lsum = 0.0f;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float x = BIAS ? s[mb][e] - m_use : __builtin_fmaf(s[mb][e], c_scale, -m_use);
+          const float p = fast_exp2(x);
+          s[mb][e] = p;
+          lsum += p;
+        }
+      l_run += lsum;
+
+      // ---- O^T += V^T P^T
+      if constexpr (kWide) {
+        // fp32: one key per MFMA k-step.  S^T entry e of block mb is key
+        // 32 mb + 8 (e/4) + 4 hf + e%4 for this lane; V is row-major in LDS.
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = 32 * mb + 8 * (e >> 2) + 4 * hf + (e & 3);
+#pragma unroll
+            for (int db = 0; db < G::NDB; ++db) {
+              const float vf = vs[key * G::VSTR + 32 * db + l32];
+              o[db] = E::mma(vf, s[mb][e], o[db]);
+            }
+          }
+      } else {
+        // 16-bit: k-step kk covers keys 16kk..16kk+15.  The B operand of a
+        // lane is 8 consecutive S^T entries of its own column, i.e. keys
+        // 16kk + {0,1,2,3,8,9,10,11} + 4 hf; V^T rows in LDS store the keys
+        // of every 16-key group in exactly that order, so the A operand is
+        // one 16-byte read.
+        constexpr int PK = BN / 16;
+        u32x4_t ph[PK];
+        u32x4_t pl[PK];
+#pragma unroll
+        for (int kk = 0; kk < PK; ++kk) {
+          const int mb = kk >> 1;
+          const int b8 = 8 * (kk & 1);
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            ph[kk][w] = E::pack(s[mb][b8 + 2 * w], s[mb][b8 + 2 * w + 1]);
+        }
+        if (split) {
+#pragma unroll
+          for (int kk = 0; kk < PK; ++kk) {
+            const int mb = kk >> 1;
+            const int b8 = 8 * (kk & 1);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const float x0 = s[mb][b8 + 2 * w], x1 = s[mb][b8 + 2 * w + 1];
+              pl[kk][w] = E::pack(x0 - E::round_trip(x0), x1 - E::round_trip(x1));
+            }
+          }
+        }
+        if (split) {
+#pragma unroll
+          for (int kk = 0; kk < PK; ++kk) {
+#pragma unroll
+            for (int db = 0; db < G::NDB; ++db) {
+              const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(
+                  vs + (32 * db + l32) * G::VSTR + 16 * kk + 8 * hf);
+              o[db] = E::mma(vf, ph[kk], o[db]);
+              o[db] = E::mma(vf, pl[kk], o[db]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < PK; ++kk) {
+#pragma unroll
+            for (int db = 0; db < G::NDB; ++db) {
+              const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(
+                  vs + (32 * db + l32) * G::VSTR + 16 * kk + 8 * hf);
+              o[db] = E::mma(vf, ph[kk], o[db]);
+            }
+          }
+        }
+      }
+    }
+
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: out = O / l, lse = (m + log2 l) ln 2
+  if (!wave_active) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  OutT* op = reinterpret_cast<OutT*>(a.out) + (int64_t)(cq0 + my_row) * a.o_st +
+             (int64_t)head * a.o_sh;
+#pragma unroll
+  for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int d0 = 32 * db + 8 * qd + 4 * hf;
+      store4<OutT>(op + d0, o[db][4 * qd] * inv, o[db][4 * qd + 1] * inv, o[db][4 * qd + 2] * inv,
+                   o[db][4 * qd + 3] * inv);
+    }
+  if (a.lse != nullptr && hf == 0) {
+    const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
+    a.lse[(int64_t)head * a.total_q + cq0 + my_row] =
+        l_tot > 0.0f ? (m_use + fast_log2(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 16-bit kernel with direct HBM -> LDS staging.
+//
+// K and V tiles are copied by buffer_load ... lds: lane i of each wave-wide
+// load writes 16 bytes at LDS base + 16 i, so the tile layout in LDS is
+// chosen by which (key, 16-byte chunk) each lane fetches.  Loads past the
+// end of the sequence fall outside the buffer's byte range and come back as
+// zeros.  Chunks are XOR-swizzled per key so that the MFMA operand reads
+// (K as 16-byte rows, V through the transposing 8-byte read) hit 16
+// different 16-byte bank groups.
+// ----------------------------------------------------------------------------
+template <int D>
+struct KSwz {
+  // 16-byte-chunk swizzle of K rows: D=128 rows are 256 B (all 64 banks), so
+  // 16 consecutive keys take 16 distinct chunk slots; 128 B / 384 B rows
+  // alternate bank halves with key parity, so pairs of keys share a pattern.
+  __device__ static int f(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
+};
+template <int D>
+struct VSwz {
+  // V rows are read four keys at a time by the transposing read; the four
+  // keys must land in four different 4-chunk groups.
+  __device__ static int f(int key) { return D == 128 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2); }
+};
+
+// A pointer the compiler cannot prove wave-uniform, made uniform (every lane
+// must hold the same value): keeps buffer descriptors in scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // word 3 = 0x00020000: raw (untyped) dword access, no swizzle, no stride.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy rows [kb, kb + rows) of one tensor's 64-key tile into LDS at dst
+// (this wave's 1 KB slice); rows past `rows` read as zeros.
+template <int D, int LOADS>
+__device__ __forceinline__ void load_tile_part(const char* base, int64_t st_b, int kb, int rows,
+                                               lds_char* dst, const uint32_t* off) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base + kb * st_b, (uint32_t)((rows - 1) * st_b + D * 2));
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * kThreads * 16), 16, off[i], 0, 0, 0);
+}
+
+// ----------------------------------------------------------------------------
+// Software-pipelined 16-bit kernel.
+//
+// A wave owns NB blocks of 32 query rows (BM = 4 waves x 32 NB).  Every K
+// and V^T fragment read from LDS feeds NB MFMAs, one per query block.  Each
+// wave runs its key loop one tile ahead: the MFMAs of tile t+1's scores, the
+// PV MFMAs of tile t and tile t's softmax form one interleaved instruction
+// stream, with operand reads issued ahead of their MFMAs.  K and V have
+// separate double buffers so K(t+2) and V(t+1) stream in while tile t is
+// consumed.  Whether P is split into hi/lo halves is decided once per
+// workgroup (rows that see few keys), giving two straight-line variants.
+// ----------------------------------------------------------------------------
+
+// Compile-time order of one tile's stream: QK^T MFMAs of the next tile
+// (after the first kHead), PV MFMAs of this tile, the softmax chunks (one
+// chunk = one pair of scores of one query block) and, when MAXOPS, the next
+// tile's masking and row max in small pieces: kMaxPieces per (query block,
+// key block) once that block's last QK^T MFMA is two MFMAs old, then two
+// that combine the blocks and exchange with the other half of the wave.
+// Chunk q covers k-step q / (4 NB), query block (q / 4) % NB, P word q % 4,
+// so the P operand of (k-step kk, block n) is complete after chunk
+// (kk NB + n) 4 + 3.  PV MFMA p uses V fragment p / NB (k-step (p / NB) /
+// NDB, d-block (p / NB) % NDB) for block p % NB; QK MFMA i uses K fragment
+// i / NB (d-step (i / NB) / NMB, key block (i / NB) % NMB) for block i % NB.
+// MFMAs alternate between QK and PV where possible; one chunk (else one max
+// op) follows each MFMA.
+enum : int { kOpQK = 0, kOpPV = 1, kOpChunk = 2, kOpMax = 3, kOpMaxEnd = 4 };
+constexpr int kMaxPieces = 3;  // max-tree pieces per 16-entry accumulator block
+constexpr int kMaxEndPieces = 2;
+
+template <int NQK, int NPV, int NB, int NDB, int NKS, int NMB, bool MAXOPS>
+struct StreamPlan {
+  static constexpr int kHead = NQK < 4 ? NQK : 4;
+  static constexpr int kChunks = 4 * NKS * NB;
+  static constexpr int kBlockMaxOps = NB * NMB * kMaxPieces;
+  static constexpr int kMaxOps = MAXOPS ? kBlockMaxOps + kMaxEndPieces : 0;
+  static constexpr int kOps = (NQK - kHead) + NPV + kChunks + kMaxOps;
+  struct Table {
+    int8_t op[kOps];
+    int8_t ix[kOps];
+  };
+  static constexpr int pv_needs(int p) {
+    return (((p / NB) / NDB) * NB + (p % NB)) * 4 + 4;
+  }
+  // QK MFMA index after which block (n, mb) of the next tile's scores is final
+  static constexpr int qk_last(int n, int mb) {
+    return ((NQK / NB / NMB - 1) * NMB + mb) * NB + n;
+  }
+  static constexpr Table build() {
+    Table t{};
+    int n = 0, qk = kHead, pv = 0, ch = 0, mx = 0, mfmas = 0;
+    int qk_pos[NQK > 0 ? NQK : 1] = {};  // MFMA ordinal of each QK MFMA
+    for (int i = 0; i < kHead; ++i) qk_pos[i] = i - kHead;
+    bool last_pv = false;
+    auto max_ready = [&](int m) {
+      if (m >= kBlockMaxOps) return true;  // combine ops: after all block ops
+      const int b = m / kMaxPieces;
+      const int i = qk_last(b / NMB, b % NMB);
+      return i < qk && mfmas - qk_pos[i] >= 3;
+    };
+    while (qk < NQK || pv < NPV || ch < kChunks || mx < kMaxOps) {
+      const bool pv_ready = pv < NPV && ch >= pv_needs(pv);
+      bool mfma = false;
+      if (pv_ready && (qk >= NQK || !last_pv)) {
+        t.op[n] = kOpPV; t.ix[n] = (int8_t)pv++; ++n; last_pv = true; mfma = true; ++mfmas;
+      } else if (qk < NQK) {
+        qk_pos[qk] = mfmas;
+        t.op[n] = kOpQK; t.ix[n] = (int8_t)qk++; ++n; last_pv = false; mfma = true; ++mfmas;
+      }
+      if (ch < kChunks) {
+        t.op[n] = kOpChunk; t.ix[n] = (int8_t)ch++; ++n;
+      } else if (mx < kMaxOps && (max_ready(mx) || (!mfma && qk >= NQK))) {
+        t.op[n] = mx >= kBlockMaxOps ? kOpMaxEnd : kOpMax;
+        t.ix[n] = (int8_t)(mx >= kBlockMaxOps ? mx - kBlockMaxOps : mx);
+        ++mx; ++n;
+      } else if (!mfma && qk >= NQK && pv >= NPV && mx >= kMaxOps) {
+        break;
+      }
+    }
+    return t;
+  }
+  static constexpr Table kTable = build();
+  static constexpr int op(int n) { return kTable.op[n]; }
+  static constexpr int index(int n) { return kTable.ix[n]; }
+};
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Per head-dim pair: NB query blocks of 32 rows per wave, NMB key blocks
+// of 32 keys per tile, OCC workgroups per CU (the register budget).  The
+// 192-wide contraction keeps 32-key tiles: its Q fragments need 48
+// registers, and 64-key tiles would push two workgroups per CU into spills.
+template <int DQK, int DV, bool BIAS = false>
+struct WaveBlocks {
+  static constexpr int NB = 1;
+  // 32-key tiles where 64 would not fit the registers: the 192-wide head,
+  // and the 128-wide head with a bias (whose next tile's bias values are
+  // held in registers through a step).  The 64-wide head without a bias
+  // has room for 128-key tiles, which halves its per-tile overheads (barrier,
+  // max exchange, copy issue) per key.
+  static constexpr int NMB = (DQK > 128 || (BIAS && DQK == 128)) ? 1 : (DQK == 64 && !BIAS) ? 4 : 2;
+  static constexpr int OCC = 2;
+  // K/V buffer slots.  Where four of each fit the LDS of two workgroups per
+  // CU (80 KB each) copies run one more step ahead and the workgroup
+  // synchronises every second step instead of every step.
+  static constexpr int NSLOT = 4 * 32 * NMB * (DQK + DV) * 2 <= 80 * 1024 ? 4 : 2;
+  // keys per tile as reported by mi_attn_tile_shape (tile counts are given
+  // in these units): the bias-free tile
+  static constexpr int kReportBN = 32 * (DQK > 128 ? 1 : DQK == 64 ? 4 : 2);
+};
+
+template <typename T, int DQK, int DV, bool BIAS, typename OutT>
+__global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void attn_fwd16p_kernel(
+    const KernelArgs a) {
+  using E = Elem<T>;
+  // A row's running max m follows every increase of the row max (O and l
+  // are rescaled between tiles when one happens), so the row's largest p is
+  // exactly 1.  A stale m would leave it at some 2^f, f fractional, whose
+  // 16-bit rounding error (up to 2^-9 relative for bf16) lands on the
+  // dominant term of P V: up to 0.2% of |v| on a peaked row.
+  constexpr int NB = WaveBlocks<DQK, DV, BIAS>::NB;
+  constexpr int NMB = WaveBlocks<DQK, DV, BIAS>::NMB;
+  constexpr int RW = 32 * NB;  // query rows per wave
+  constexpr int BM = 4 * RW;   // query rows per workgroup
+  constexpr int BN = 32 * NMB; // keys per tile
+  constexpr int NKS = BN / 16; // PV k-steps per tile
+  constexpr int KRB = DQK * 2;
+  constexpr int VRB = DV * 2;
+  constexpr int KCPR = DQK / 8;
+  constexpr int VCPR = DV / 8;
+  constexpr int K_BYTES = BN * KRB;
+  constexpr int V_BYTES = BN * VRB;
+  constexpr int KLOADS = K_BYTES / (kThreads * 16);
+  constexpr int VLOADS = V_BYTES / (kThreads * 16);
+  constexpr int KSTEPS = DQK / 16;
+  constexpr int NDB = DV / 32;
+  constexpr int OUT_RB = DV * (int)sizeof(OutT);
+  constexpr int OUT_CPR = OUT_RB / 16;
+  static_assert(K_BYTES % (kThreads * 16) == 0 && V_BYTES % (kThreads * 16) == 0, "tile loads");
+  // output rows staged per pass (a wave stages in one K or V buffer)
+  constexpr int STAGE_BYTES = K_BYTES < V_BYTES ? K_BYTES : V_BYTES;
+  constexpr int STAGE_ROWS = 32 * OUT_RB <= STAGE_BYTES ? 32 : STAGE_BYTES / OUT_RB;
+  static_assert(STAGE_ROWS >= 1 && 32 % STAGE_ROWS == 0, "output staging");
+
+  // K and V buffers (NSLOT of each) as separate LDS objects.  Each access
+  // names its buffer at compile time, so the compiler can tell that reads of
+  // the current tiles do not overlap the copies in flight into the other
+  // buffers and does not wait for those copies before reading.
+  constexpr int NSLOT = WaveBlocks<DQK, DV, BIAS>::NSLOT;
+  constexpr int K_BYTES_HI = NSLOT == 4 ? K_BYTES : 16;  // slots 2 and 3
+  constexpr int V_BYTES_HI = NSLOT == 4 ? V_BYTES : 16;
+  __shared__ __attribute__((aligned(1024))) char kbuf_0[K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf_1[K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf_0[V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf_1[V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf_2[K_BYTES_HI];
+  __shared__ __attribute__((aligned(1024))) char kbuf_3[K_BYTES_HI];
+  __shared__ __attribute__((aligned(1024))) char vbuf_2[V_BYTES_HI];
+  __shared__ __attribute__((aligned(1024))) char vbuf_3[V_BYTES_HI];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // Scalar wave index: every per-wave condition below is a uniform scalar
+  // branch.  MFMA writes all 64 lanes whatever EXEC holds, so an MFMA must
+  // never sit in a branch the compiler could run with a partial EXEC mask.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5;
+  const int l32 = lane & 31;
+
+  // ---- work decode.  blockIdx.y counts query tiles down from the last tile
+  // of the longest sequence: tile index gridDim.y - 1 - blockIdx.y from the
+  // start of every sequence, so workgroups are dispatched roughly by
+  // decreasing row position, i.e. (for causal rows) decreasing work, and
+  // the last ones to start are the lightest.  Within one (sequence, tile) slab
+  // the query heads are ordered so that the heads dispatched to one XCD
+  // (consecutive workgroups go round-robin over 8 XCDs) are neighbours and
+  // mostly share their kv head, i.e. hit the same L2.
+  //
+  // With a bias shared by all query heads (head_major, one-dimensional
+  // grid) the order is different: XCD c (workgroups c, c + 8, ...) takes the
+  // (sequence, tile) groups c, c + 8, c + 16, ... in turn, all query heads of
+  // a group back to back, so that the group's bias rows are fetched from HBM
+  // into that XCD's L2 once and read there by every head.  Groups are
+  // numbered tile-major (sequence fastest), counting tiles down from the
+  // last as above; with a few sequences the groups an XCD holds at one time
+  // are tiles of the same sequence and share its K/V.
+  //
+  // With many heads and no kv sharing between them (kv_rows = R > 0, one-
+  // dimensional grid), one row holds more items per XCD than the XCD runs at
+  // once, so concurrent items would all read different K/V.  Instead XCD c
+  // takes its (sequence, head) slots R rows at a time: slot 0 for rows
+  // 0..R-1, slot 1 for rows 0..R-1, ..., then rows R..2R-1, so the R query
+  // tiles of one head that run together share their K/V through L2.  Rows
+  // still count down from the last tile, R at a time.
+  int seq, head, by;
+  if (a.kv_rows > 0) {
+    const int R = a.kv_rows;
+    const int per_xcd = (a.hq * a.num_seqs) >> 3;  // (sequence, head) slots per XCD
+    const int k = (int)(blockIdx.x >> 3);
+    const int sr = k / (per_xcd * R);
+    const int rem = k - sr * (per_xcd * R);
+    const int slot = rem / R;
+    by = sr * R + (rem - slot * R);
+    if (by >= a.n_qtiles) return;  // padding rows of the last group of R
+    const int bx = slot * 8 + (int)(blockIdx.x & 7);
+    const int hx = bx % a.hq;
+    seq = bx / a.hq;
+    head = hx;
+    if ((a.hq & 7) == 0) head = (hx & 7) * (a.hq >> 3) + (hx >> 3);
+  } else if (a.head_major) {
+    const int k = (int)(blockIdx.x >> 3);
+    const int kg = k / a.hq;
+    head = k - kg * a.hq;
+    const int gb = kg * 8 + (int)(blockIdx.x & 7);
+    by = gb / a.num_seqs;
+    seq = gb - by * a.num_seqs;
+    if (by >= a.n_qtiles) return;  // padding of the last round of 8 groups
+  } else {
+    const int hx = blockIdx.x % a.hq;
+    seq = blockIdx.x / a.hq;
+    by = blockIdx.y;
+    head = hx;
+    if ((a.hq & 7) == 0) {
+      const int per_xcd = a.hq >> 3;
+      head = (hx & 7) * per_xcd + (hx >> 3);
+    }
+  }
+  // The sequence bounds and the arguments the set-up needs are fetched in
+  // one round trip: the empty asm keeps the compiler from deferring loads
+  // past the early exit, one dependent wait at a time.
+  int cq0 = a.cu_q[seq], cq1 = a.cu_q[seq + 1];
+  int ck0 = a.cu_kv[seq], ck1 = a.cu_kv[seq + 1];
+  asm volatile("" : "+s"(cq0), "+s"(cq1), "+s"(ck0), "+s"(ck1)
+               : "s"(a.q_st), "s"(a.q_sh), "s"(a.k_st), "s"(a.k_sh), "s"(a.v_st), "s"(a.v_sh),
+                 "s"(a.group), "s"(a.causal), "s"(a.window), "s"(a.split_keys), "s"(a.n_qtiles));
+  const int lq = cq1 - cq0;
+  const int lk = ck1 - ck0;
+  const int n_qtiles = (lq + BM - 1) / BM;
+  const int qtile = a.n_qtiles - 1 - by;
+  if (qtile >= n_qtiles) return;
+
+  const int r0 = qtile * BM;
+  const int r1 = min(lq, r0 + BM);
+  const int off = lk - lq;
+  const int g = head / a.group;
+  const bool causal = a.causal != 0;
+  const int W = a.window;
+
+  // Key range holding at least one visible key for rows [r0, r1).
+  int kv_hi = lk;
+  if (causal) kv_hi = min(lk, r1 - 1 + off + 1);
+  int kv_lo = 0;
+  if (W > 0) kv_lo = max(0, r0 + off - W + 1);
+  const int t_begin = kv_lo / BN;
+  int t_end = kv_hi > 0 ? (kv_hi + BN - 1) / BN : 0;
+  if (t_end < t_begin) t_end = t_begin;
+
+  if (a.tile_counts != nullptr && tid == 0) {
+    // in units of the reported tile width (a multiple of BN)
+    constexpr int RBN = WaveBlocks<DQK, DV, BIAS>::kReportBN;
+    a.tile_counts[((int64_t)qtile * a.num_seqs + seq) * a.hq + head] =
+        t_end > t_begin ? (t_end * BN + RBN - 1) / RBN - (t_begin * BN) / RBN : 0;
+  }
+
+  const int w0 = r0 + wave * RW;
+  const int w1 = min(lq, w0 + RW);
+  const bool wave_active = w0 < lq;
+  int my_row[NB];
+  bool row_ok[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    my_row[n] = w0 + 32 * n + l32;
+    row_ok[n] = my_row[n] < lq;
+  }
+  // Tiles from wt_end on hold no key visible to any row of this wave (causal
+  // rows that end before the workgroup's last diagonal; no rows at all past
+  // the sequence end): the wave skips their work but still does its share of
+  // the copies and the barriers.
+  const int wt_end = !wave_active ? t_begin
+                     : causal    ? (min(lk, w1 - 1 + off + 1) + BN - 1) / BN
+                                 : t_end;
+  // hi/lo split of P for the whole workgroup when its first row sees few keys
+  const int nvis0 = (causal ? min(lk, r0 + off + 1) : lk) - kv_lo;
+  const bool split = (nvis0 < a.split_keys) || (BIAS && a.split_bias != 0);
+
+  const int64_t k_st_b = a.k_st * 2;
+  const int64_t v_st_b = a.v_st * 2;
+  const char* kbase = reinterpret_cast<const char*>(a.k) + ((int64_t)ck0 * a.k_st + (int64_t)g * a.k_sh) * 2;
+  const char* vbase = reinterpret_cast<const char*>(a.v) + ((int64_t)ck0 * a.v_st + (int64_t)g * a.v_sh) * 2;
+
+  // Per-lane byte offsets (within a tile, from its first key) of the chunks
+  // this lane copies; the same for every tile.
+  uint32_t koff[KLOADS];
+  uint32_t voff[VLOADS];
+#pragma unroll
+  for (int i = 0; i < KLOADS; ++i) {
+    const int pos = i * kThreads + tid;  // 16-byte slot in the LDS tile
+    const int key = pos / KCPR;
+    const int c = (pos % KCPR) ^ KSwz<DQK>::f(key);
+    koff[i] = (uint32_t)(key * k_st_b + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < VLOADS; ++i) {
+    const int pos = i * kThreads + tid;
+    const int key = pos / VCPR;
+    const int c = (pos % VCPR) ^ VSwz<DV>::f(key);
+    voff[i] = (uint32_t)(key * v_st_b + c * 16);
+  }
+  // buffer of compile-time slot S
+  auto kbuf = [&](auto S) __attribute__((device)) -> lds_char* {
+    constexpr int i = decltype(S)::value;
+    static_assert(i < NSLOT, "K slot");
+    if constexpr (i == 0) return (lds_char*)kbuf_0;
+    else if constexpr (i == 1) return (lds_char*)kbuf_1;
+    else if constexpr (i == 2) return (lds_char*)kbuf_2;
+    else return (lds_char*)kbuf_3;
+  };
+  auto vbuf = [&](auto S) __attribute__((device)) -> lds_char* {
+    constexpr int i = decltype(S)::value;
+    static_assert(i < NSLOT, "V slot");
+    if constexpr (i == 0) return (lds_char*)vbuf_0;
+    else if constexpr (i == 1) return (lds_char*)vbuf_1;
+    else if constexpr (i == 2) return (lds_char*)vbuf_2;
+    else return (lds_char*)vbuf_3;
+  };
+  auto load_k = [&](int t, auto S) __attribute__((device)) {
+    load_tile_part<DQK, KLOADS>(kbase, k_st_b, t * BN, min(lk - t * BN, BN), kbuf(S) + wave * 1024, koff);
+  };
+  auto load_v = [&](int t, auto S) __attribute__((device)) {
+    load_tile_part<DV, VLOADS>(vbase, v_st_b, t * BN, min(lk - t * BN, BN), vbuf(S) + wave * 1024, voff);
+  };
+
+  // ---- Q fragments (B operand of S^T = K Q^T), loaded once.
+  // Rows past the sequence end fall outside the buffer window and read as 0.
+  u32x4_t qf[NB][KSTEPS];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const int64_t q_st_b = a.q_st * 2;
+    const int rows = min(32, lq - (w0 + 32 * n));  // valid rows of this block (may be <= 0)
+    const char* qb = uniform_ptr(reinterpret_cast<const char*>(a.q) +
+                                 ((int64_t)(cq0 + w0 + 32 * n) * a.q_st + (int64_t)head * a.q_sh) * 2);
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(qb, rows > 0 ? (uint32_t)((rows - 1) * q_st_b + DQK * 2) : 0u);
+    const int qoff = (int)(l32 * q_st_b) + 16 * hf;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qf[n][ks] = __builtin_amdgcn_raw_buffer_load_b128(r, qoff + 32 * ks, 0, 0);
+  }
+
+  // V^T fragment (A operand of O^T += V^T P^T): two transposing reads of the
+  // row-major V tile.  Read h of k-step kk, d-block db gives this lane keys
+  // 16 kk + 8 h + 4 hf + k (k = 0..3) at head dim 32 db + lane % 32.
+  const int vkey_lane = 4 * hf + ((lane & 15) >> 2);
+  const int vchunk_lane = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vbyte_lane = (lane & 1) * 8;
+  auto vfrag = [&](const lds_char* vt, int kk, int db) __attribute__((device)) -> u32x4_t {
+    u32x4_t r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int key = 16 * kk + 8 * h + vkey_lane;
+      const int c = (4 * db + vchunk_lane) ^ VSwz<DV>::f(key);
+      const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16_t*)(vt + key * VRB + c * 16 + vbyte_lane));
+      const u32x2_t xw = __builtin_bit_cast(u32x2_t, x);
+      r[2 * h] = xw[0];
+      r[2 * h + 1] = xw[1];
+    }
+    return r;
+  };
+
+  f32x16_t o[NB][NDB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[n][i][e] = 0.0f;
+  float m_run[NB];
+  float l_run[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    m_run[n] = kNegInf;  // running max, log2 units (scale folded in)
+    l_run[n] = 0.0f;     // this lane's share of the running sum
+  }
+  const float c_scale = a.scale_log2;
+  // With a bias, logits stay in natural units (scale s + b, one fma) until
+  // the exponent's argument multiplies them by log2(e).
+  const float c_nat = a.scale_log2 * (1.0f / kLog2e);
+  const float* brow[NB];
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      brow[n] = a.bias + (int64_t)(cq0 + (row_ok[n] ? my_row[n] : 0)) * a.b_st +
+                (int64_t)(a.bias_heads == 1 ? 0 : head) * a.b_sh;
+  }
+
+  // S^T = K Q^T for the whole K tile at kt (prologue only).
+  auto qk_all = [&](const lds_char* kt, f32x16_t (&s)[NB][NMB]) __attribute__((device)) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[n][mb][e] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int key = 32 * mb + l32;
+        const int c = (2 * kk + hf) ^ KSwz<DQK>::f(key);
+        const u32x4_t kf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+            kt + key * KRB + c * 16);
+#pragma unroll
+        for (int n = 0; n < NB; ++n) s[n][mb] = E::mma(kf, qf[n][kk], s[n][mb]);
+      }
+  };
+
+  // Mask (boundary tiles only) and bias the raw scores of tile t, then take
+  // each row's max; returns true when some row's max exceeds its running max
+  // by more than the growth bound (m_pend holds the new maxima).  A row whose
+  // running max is still -inf (nothing visible yet: O and l are zero) simply
+  // adopts the new max.
+  // Tile t holds keys that some row of this wave must not see (sequence
+  // end, causal diagonal, window start).
+  auto tile_needs_mask = [&](int t) __attribute__((device)) -> bool {
+    const int kb = t * BN;
+    return (kb + BN > lk) || (causal && kb + BN - 1 > w0 + off) || (W > 0 && kb <= w1 - 1 + off - W);
+  };
+  // Masks key block mb of query block n of tile t: entry e of the lane holds
+  // key kb + 32 mb + 8 (e / 4) + 4 hf + e % 4, visible iff lo < key <= hi
+  // (one unsigned compare per entry).
+  auto mask_block = [&](int t, f32x16_t& sc, int n, int mb) __attribute__((device)) {
+    const int key0 = t * BN + 32 * mb + 4 * hf;
+    const int hi = min(lk - 1, causal ? my_row[n] + off : lk - 1);
+    const int lo = W > 0 ? my_row[n] + off - W : -1;
+    const int base = lo + 1 - key0;         // first visible entry offset
+    const uint32_t span = (uint32_t)max(hi - lo, 0);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 8 * (e >> 2) + (e & 3);
+      sc[e] = (uint32_t)(c - base) < span ? sc[e] : kNegInf;
+    }
+  };
+  // Given the row max of tile t's (masked) scores for each query block, set
+  // the pending max; returns true when some row's max exceeds its running
+  // max by more than the growth bound.  A row whose running max is still
+  // -inf (nothing visible yet: O and l are zero) adopts the new max.
+  // mx holds the maxima over both halves of the wave (max_with_other_half).
+  auto finish_max = [&](float (&mx)[NB], float (&m_pend)[NB]) __attribute__((device)) -> bool {
+    bool grow = false;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const float m_all = mx[n];
+      const float m_tile = BIAS ? m_all * kLog2e : m_all * c_scale;
+      if (m_run[n] == kNegInf) m_run[n] = m_tile;
+      m_pend[n] = m_tile;
+      grow = grow || (m_tile > m_run[n]);
+    }
+    return __ballot(grow) != 0ull;
+  };
+  // This lane's bias values of tile t (the entries of its S^T registers);
+  // keys past the sequence end read as 0 (they are masked).  They are loaded
+  // at the start of the step whose end consumes them (prep_tile of the next
+  // tile), so the loads' latency is hidden behind that step's stream.
+  auto load_bias = [&](int t, f32x4_t (&bv)[NB][NMB][4]) __attribute__((device)) {
+    const int kb = t * BN;
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int key0 = kb + 32 * mb + 8 * qd + 4 * hf;
+          if (row_ok[n] && key0 + 3 < lk) {
+            bv[n][mb][qd] = *reinterpret_cast<const f32x4_t*>(brow[n] + key0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              bv[n][mb][qd][e] = (row_ok[n] && key0 + e < lk) ? brow[n][key0 + e] : 0.0f;
+          }
+        }
+  };
+  auto prep_tile = [&](int t, f32x16_t (&sc)[NB][NMB], float (&m_pend)[NB],
+                       const f32x4_t (&bv)[NB][NMB][4]) __attribute__((device)) -> bool {
+    if (tile_needs_mask(t)) {
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) mask_block(t, sc[n][mb], n, mb);
+    }
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sc[n][mb][4 * qd + e] =
+                  __builtin_fmaf(sc[n][mb][4 * qd + e], c_nat, bv[n][mb][qd][e]);
+    }
+    float mx[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      mx[n] = max16(sc[n][0]);
+#pragma unroll
+      for (int mb = 1; mb < NMB; ++mb) mx[n] = __builtin_fmaxf(mx[n], max16(sc[n][mb]));
+      mx[n] = max_with_other_half(mx[n]);
+    }
+    return finish_max(mx, m_pend);
+  };
+
+  // Rows whose max grew: move their running max and rescale O and l (kept
+  // outside the interleaved stream so that O needs no VALU work there).
+  auto rescale = [&](const float (&m_pend)[NB]) __attribute__((device)) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const bool g = m_pend[n] > m_run[n];
+      const float alpha = g ? fast_exp2(m_run[n] - m_pend[n]) : 1.0f;
+      if (g) m_run[n] = m_pend[n];
+      l_run[n] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[n][i][e] *= alpha;
+    }
+  };
+
+  // One loop step for tile t.  Entry: s_cur holds tile t's masked, biased
+  // scores and m_run is final for them.  One interleaved stream (StreamPlan):
+  // QK^T MFMAs of tile t+1, PV MFMAs of tile t as soon as their slice of P
+  // is packed, and tile t's softmax in pairs of scores, with operand reads
+  // issued ahead.  Then tile t+1's scores are prepared; the return value says
+  // whether a rescale is due before tile t+1.
+  auto step = [&](auto split_tag, auto slot_tag, int j, f32x16_t (&s_cur)[NB][NMB],
+                  f32x16_t (&s_nxt)[NB][NMB], float (&m_pend)[NB],
+                  f32x4_t (&bpre)[NB][NMB][4]) __attribute__((device)) -> bool {
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    constexpr int NKF = NMB * KSTEPS;     // K fragments per tile
+    constexpr int NQK = NKF * NB;         // QK^T MFMAs per tile
+    constexpr int NVF = NKS * NDB;        // V^T fragments per tile
+    constexpr int NPV = NVF * NB;         // PV MFMA slots per tile (x2 with the split)
+    // The next tile's masking, bias and row max run inside the stream, in
+    // pieces after each key block's last QK^T MFMA.
+    constexpr bool MAXOPS = true;
+    using Plan = StreamPlan<NQK, NPV, NB, NDB, NKS, NMB, MAXOPS>;
+    const int nt = t_end - t_begin;
+    const int t = t_begin + j;
+    // slot = j % NSLOT (the caller's loop is unrolled NSLOT times).  K(t+u)
+    // lives in K slot (slot + u) % NSLOT and V(t+u) in V slot
+    // (slot + u) % NSLOT.  This step reads K(t+1) and V(t) and starts the
+    // copies of K(t+LK) and V(t+LV), into the slots of the tiles read
+    // NSLOT - LK + 1 steps earlier.  With two slots every step ends with a
+    // barrier; with four, copies start one step further ahead and only odd
+    // steps end with one.  Either way a barrier separates the last read of a
+    // slot from the copy that refills it, and the end of a copy (each wave's
+    // vmcnt wait at its step's end) from the first read of its tile.
+    constexpr int slot = decltype(slot_tag)::value;
+    constexpr int LK = NSLOT == 4 ? 3 : 2;  // K copies run LK tiles ahead
+    constexpr int LV = LK - 1;              // V copies LV tiles ahead
+    using KR = std::integral_constant<int, (slot + 1) % NSLOT>;
+    using VR = std::integral_constant<int, slot>;
+    using KW = std::integral_constant<int, (slot + LK) % NSLOT>;
+    using VW = std::integral_constant<int, (slot + LV) % NSLOT>;
+    constexpr bool BAR = NSLOT == 2 || (slot & 1) != 0;
+    if (j + LV < nt) load_v(t + LV, VW{});
+    if (j + LK < nt) load_k(t + LK, KW{});
+    if (t >= wt_end) {  // nothing visible to this wave from here on
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      if constexpr (BAR) __syncthreads();
+      return false;
+    }
+    if constexpr (BIAS) {
+      if (j + 1 < nt) load_bias(t + 1, bpre);
+    }
+
+    const lds_char* kt = kbuf(KR{});
+    const lds_char* vt = vbuf(VR{});
+    // K fragment fi: d-step fi / NMB, key block fi % NMB
+    auto kread = [&](int fi) __attribute__((device)) -> u32x4_t {
+      const int kk = fi / NMB, mb = fi % NMB;
+      const int key = 32 * mb + l32;
+      const int c = (2 * kk + hf) ^ KSwz<DQK>::f(key);
+      return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(kt + key * KRB + c * 16);
+    };
+    u32x4_t kf[3];
+    u32x4_t vf[3];
+    // QK MFMA i: K fragment i / NB, query block i % NB
+    auto do_qk = [&](int i) __attribute__((device)) {
+      const int fi = i / NB, n = i % NB;
+      if (n == 0 && fi + 2 < NKF) kf[(fi + 2) % 3] = kread(fi + 2);
+      s_nxt[n][fi % NMB] = E::mma(kf[fi % 3], qf[n][fi / NMB], s_nxt[n][fi % NMB]);
+    };
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s_nxt[n][mb][e] = 0.0f;
+    kf[0] = kread(0);
+    if (NKF > 1) kf[1] = kread(1);
+    float neg_m[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) neg_m[n] = (m_run[n] == kNegInf) ? 0.0f : -m_run[n];
+
+    u32x4_t ph[NB][NKS];
+    u32x4_t pl[NB][NKS];
+    float lsum[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) lsum[n] = 0.0f;
+    const bool has_next = j + 1 < nt;
+    const bool mask_next = has_next && tile_needs_mask(t + 1);
+    float mxp[NB];
+    float mpart[NB][NMB][5];  // leaf maxima of the max tree of each block
+    bool grow = false;
+    auto vread = [&](int vi) __attribute__((device)) -> u32x4_t { return vfrag(vt, vi / NDB, vi % NDB); };
+#pragma unroll
+    for (int i = 0; i < Plan::kHead; ++i) do_qk(i);
+    vf[0] = vread(0);
+    if (NVF > 1) vf[1] = vread(1);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, Plan::kOps>([&](auto qc) __attribute__((device)) {
+      constexpr int op = Plan::op(decltype(qc)::value);
+      constexpr int ix = Plan::index(decltype(qc)::value);
+      if constexpr (op == kOpQK) {
+        do_qk(ix);
+      } else if constexpr (op == kOpPV) {
+        const int vi = ix / NB, n = ix % NB;
+        if (n == 0 && vi + 2 < NVF) vf[(vi + 2) % 3] = vread(vi + 2);
+        const int kk = vi / NDB, db = vi % NDB;
+        o[n][db] = E::mma(vf[vi % 3], ph[n][kk], o[n][db]);
+        if constexpr (SPLIT) o[n][db] = E::mma(vf[vi % 3], pl[n][kk], o[n][db]);
+      } else if constexpr (op == kOpMax) {
+        // next tile, query block n, key block mb: masking, then the max tree
+        // (leaves of three entries, then two levels), in kMaxPieces pieces.
+        // On the last tile the scores are stale and the result is unused.
+        constexpr int b = ix / kMaxPieces, piece = ix % kMaxPieces;
+        constexpr int n = b / NMB, mb = b % NMB;
+        f32x16_t& v = s_nxt[n][mb];
+        float* mp = mpart[n][mb];
+        // (empty asm fences keep each piece at its slot, as in the chunks)
+        // With a bias the entries become logits (natural units) first.
+        auto add_bias = [&](int e0, int e1) __attribute__((device)) {
+          if constexpr (BIAS) {
+#pragma unroll
+            for (int e = e0; e < e1; ++e)
+              v[e] = __builtin_fmaf(v[e], c_nat, bpre[n][mb][e / 4][e % 4]);
+          }
+        };
+        if constexpr (piece == 0) {
+          if (mask_next) mask_block(t + 1, v, n, mb);
+          add_bias(0, 6);
+          mp[0] = max3f(v[0], v[1], v[2]);
+          mp[1] = max3f(v[3], v[4], v[5]);
+          asm volatile("" : "+v"(mp[0]), "+v"(mp[1]));
+        } else if constexpr (piece == 1) {
+          add_bias(6, 15);
+          mp[2] = max3f(v[6], v[7], v[8]);
+          mp[3] = max3f(v[9], v[10], v[11]);
+          mp[4] = max3f(v[12], v[13], v[14]);
+          asm volatile("" : "+v"(mp[2]), "+v"(mp[3]), "+v"(mp[4]));
+        } else {
+          add_bias(15, 16);
+          const float m = __builtin_fmaxf(max3f(mp[0], mp[1], mp[2]), max3f(mp[3], mp[4], v[15]));
+          mxp[n] = mb == 0 ? m : __builtin_fmaxf(mxp[n], m);
+          asm volatile("" : "+v"(mxp[n]));
+        }
+      } else if constexpr (op == kOpMaxEnd) {
+        if constexpr (ix == 0) {
+#pragma unroll
+          for (int n = 0; n < NB; ++n) {
+            mxp[n] = max_with_other_half(mxp[n]);
+            asm volatile("" : "+v"(mxp[n]));
+          }
+        } else {
+          if (has_next) grow = finish_max(mxp, m_pend);
+        }
+      } else {
+        static_assert(op == kOpChunk, "stream op");
+        // chunk ix: k-step kk, query block n, P word w -> S^T block kk / 2,
+        // entries 8 (kk % 2) + 2 w, +1 (keys 16 kk + {2w, 2w+1 | +8} + 4 hf)
+        const int kk = ix / (4 * NB), n = (ix / 4) % NB, w = ix % 4;
+        const int mb = kk >> 1, e0 = 8 * (kk & 1) + 2 * w;
+        const float cx = BIAS ? kLog2e : c_scale;
+        const float x0 = __builtin_fmaf(s_cur[n][mb][e0], cx, neg_m[n]);
+        const float x1 = __builtin_fmaf(s_cur[n][mb][e0 + 1], cx, neg_m[n]);
+        const float p0 = fast_exp2(x0);
+        const float p1 = fast_exp2(x1);
+        lsum[n] += p0;
+        lsum[n] += p1;
+        uint32_t hw = E::pack(p0, p1);
+        // Empty asm with in/out register operands: an optimisation fence
+        // that keeps this pair's VALU work at its slot in the stream (pure
+        // arithmetic would otherwise be sunk below the MFMAs).
+        if constexpr (SPLIT) {
+          uint32_t lw = E::pack(p0 - E::round_trip(p0), p1 - E::round_trip(p1));
+          asm volatile("" : "+v"(hw), "+v"(lw), "+v"(lsum[n]));
+          pl[n][kk][w] = lw;
+        } else {
+          asm volatile("" : "+v"(hw), "+v"(lsum[n]));
+        }
+        ph[n][kk][w] = hw;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int n = 0; n < NB; ++n) l_run[n] += lsum[n];
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of V(t+LV), K(t+LK) have landed
+    if constexpr (BAR) __syncthreads();
+    return grow;
+  };
+
+  auto run = [&](auto split_tag) __attribute__((device)) {
+    const int nt = t_end - t_begin;
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    load_k(t_begin, S0{});
+    load_v(t_begin, S0{});
+    if (nt > 1) load_k(t_begin + 1, S1{});
+    if constexpr (NSLOT == 4) {  // copies run a step further ahead
+      using S2 = std::integral_constant<int, 2>;
+      if (nt > 1) load_v(t_begin + 1, S1{});
+      if (nt > 2) load_k(t_begin + 2, S2{});
+    }
+    // bias of the first tile: in flight together with the first copies
+    f32x4_t bpre[NB][NMB][4];
+    if constexpr (BIAS) load_bias(t_begin, bpre);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    f32x16_t sa[NB][NMB], sb[NB][NMB];
+    float m_pend[NB];
+    qk_all(kbuf(S0{}), sa);
+    bool need = prep_tile(t_begin, sa, m_pend, bpre);
+    __syncthreads();  // every wave is done with K buffer 0 before it is refilled
+    if constexpr (NSLOT == 2) {
+      for (int j = 0; j < nt; j += 2) {
+        need = step(split_tag, S0{}, j, sa, sb, m_pend, bpre);
+        if (need) rescale(m_pend);
+        if (j + 1 < nt) {
+          need = step(split_tag, S1{}, j + 1, sb, sa, m_pend, bpre);
+          if (need) rescale(m_pend);
+        }
+      }
+    } else {
+      using S2 = std::integral_constant<int, 2>;
+      using S3 = std::integral_constant<int, 3>;
+      for (int j = 0; j < nt; j += 4) {
+        need = step(split_tag, S0{}, j, sa, sb, m_pend, bpre);
+        if (need) rescale(m_pend);
+        if (j + 1 < nt) {
+          need = step(split_tag, S1{}, j + 1, sb, sa, m_pend, bpre);
+          if (need) rescale(m_pend);
+        }
+        if (j + 2 < nt) {
+          need = step(split_tag, S2{}, j + 2, sa, sb, m_pend, bpre);
+          if (need) rescale(m_pend);
+        }
+        if (j + 3 < nt) {
+          need = step(split_tag, S3{}, j + 3, sb, sa, m_pend, bpre);
+          if (need) rescale(m_pend);
+        }
+      }
+      // the last step ended without a barrier when it was an even one: the
+      // epilogue reuses the buffers as staging
+      if (nt & 1) __syncthreads();
+    }
+  };
+  if (t_begin < t_end) {
+    if (split) run(std::true_type{});
+    else run(std::false_type{});
+  }
+
+  // ---- epilogue: O / l staged through LDS (the K/V buffers are free after
+  // the loop's last barrier), STAGE_ROWS rows of a 32-row query block at a
+  // time, so that every output row is written as contiguous 16-byte stores.
+  if (!wave_active) return;
+  // each wave stages its rows in one of the four (now free) buffers
+  lds_char* ostage = wave == 0 ? (lds_char*)kbuf_0 : wave == 1 ? (lds_char*)kbuf_1
+                   : wave == 2 ? (lds_char*)vbuf_0 : (lds_char*)vbuf_1;
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const float l_tot = l_run[n] + __shfl_xor(l_run[n], 32);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+#pragma unroll
+    for (int pass = 0; pass < 32 / STAGE_ROWS; ++pass) {
+      if (n > 0 || pass > 0) __builtin_amdgcn_wave_barrier();
+      const int sr = l32 - pass * STAGE_ROWS;  // this lane's row within the pass
+      if (sr >= 0 && sr < STAGE_ROWS) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int d0 = 32 * db + 8 * qd + 4 * hf;
+            const float v0 = o[n][db][4 * qd] * inv, v1 = o[n][db][4 * qd + 1] * inv;
+            const float v2 = o[n][db][4 * qd + 2] * inv, v3 = o[n][db][4 * qd + 3] * inv;
+            const int byte = d0 * (int)sizeof(OutT);
+            const int c = (byte >> 4) ^ (sr & (OUT_CPR - 1));
+            lds_char* dst = ostage + sr * OUT_RB + c * 16 + (byte & 15);
+            if constexpr (sizeof(OutT) == 4) {
+              *(__attribute__((address_space(3))) f32x4_t*)dst = (f32x4_t){v0, v1, v2, v3};
+            } else {
+              *(__attribute__((address_space(3))) u32x2_t*)dst =
+                  (u32x2_t){Elem<OutT>::pack(v0, v1), Elem<OutT>::pack(v2, v3)};
+            }
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();
+      constexpr int RPI = 64 / OUT_CPR;  // rows per wave-wide pass
+      const int cc = lane % OUT_CPR;
+      const int qb = w0 + 32 * n + pass * STAGE_ROWS;  // first row of this pass
+      // The pass's rows through one buffer window: rows past the sequence
+      // end fall outside it and their stores are dropped.
+      const int o_rows = min(max(lq - qb, 0), STAGE_ROWS);
+      const int64_t o_st_b = a.o_st * (int64_t)sizeof(OutT);
+      const char* obase = uniform_ptr(reinterpret_cast<const char*>(a.out) +
+                                      ((int64_t)(cq0 + qb) * a.o_st + (int64_t)head * a.o_sh) *
+                                          (int64_t)sizeof(OutT));
+      const __amdgpu_buffer_rsrc_t orsrc =
+          make_rsrc(obase, o_rows > 0 ? (uint32_t)((o_rows - 1) * o_st_b + OUT_RB) : 0u);
+#pragma unroll
+      for (int it = 0; it < (STAGE_ROWS + RPI - 1) / RPI; ++it) {
+        const int q = it * RPI + lane / OUT_CPR;
+        const int c = cc ^ (q & (OUT_CPR - 1));
+        if (q < STAGE_ROWS) {
+          const u32x4_t val =
+              *(const __attribute__((address_space(3))) u32x4_t*)(ostage + q * OUT_RB + c * 16);
+          __builtin_amdgcn_raw_buffer_store_b128(val, orsrc, (int)(q * o_st_b) + cc * 16, 0, 0);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    }
+    if (a.lse != nullptr && hf == 0 && row_ok[n]) {
+      const float m_use = (m_run[n] == kNegInf) ? 0.0f : m_run[n];
+      a.lse[(int64_t)head * a.total_q + cq0 + my_row[n]] =
+          l_tot > 0.0f ? (m_use + fast_log2(l_tot)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+template <typename T, int DQK, int DV, bool BIAS, typename OutT>
+hipError_t launch_one(const KernelArgs& a, dim3 grid, hipStream_t stream) {
+  if constexpr (Elem<T>::kWide) {
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, BIAS, OutT>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_fwd16p_kernel<T, DQK, DV, BIAS, OutT>), grid, dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int DQK, int DV>
+hipError_t launch_dims(const KernelArgs& a, bool bias, bool out_f32, dim3 grid, hipStream_t s) {
+  if (bias) {
+    return out_f32 ? launch_one<T, DQK, DV, true, float>(a, grid, s)
+                   : launch_one<T, DQK, DV, true, T>(a, grid, s);
+  }
+  return out_f32 ? launch_one<T, DQK, DV, false, float>(a, grid, s)
+                 : launch_one<T, DQK, DV, false, T>(a, grid, s);
+}
+
+}  // namespace
+}  // namespace mi_attn
