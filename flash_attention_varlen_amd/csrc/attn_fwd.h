@@ -37,8 +37,7 @@ struct KernelArgs {
   int32_t causal;
   int32_t window;
   float scale_log2;    // softmax scale * log2(e)
-  int32_t split_keys;  // rows seeing fewer keys get a hi/lo split of P
-  int32_t split_bias;  // with a bias, split P on every tile (16-bit types)
+  float split_l;       // 16-bit kernels: low half of P multiplied in while a row's sum is below this
   int32_t n_qtiles;    // query tiles of the longest sequence (grid.y unless head_major)
   int32_t head_major;  // 16-bit kernels: 1-D grid, all heads of a (sequence, tile) on one XCD
   int32_t kv_rows;     // 16-bit kernels: > 0 = 1-D grid, this many rows of one head run together

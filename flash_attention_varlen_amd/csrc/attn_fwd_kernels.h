@@ -14,12 +14,13 @@
 //   mask / bias / scale   fp32, masks only on boundary tiles;
 //   online softmax        fp32 running max and sum per row (the row max is
 //                         an in-lane reduction plus one exchange with the
-//                         lane 32 away, so all 64 lanes work); in the 16-bit
-//                         kernel the running max follows every increase, so
-//                         a row's largest p is exactly 1;
-//   O^T += V^T P^T        on MFMA, P rounded to the input type (RNE), with
-//                         a hi/lo split of P on tiles of rows that see few
-//                         keys.
+//                         lane 32 away, so all 64 lanes work); the running
+//                         max is raised (and O, l rescaled) only when a row's
+//                         max grows by more than 2^8;
+//   O^T += V^T P^T        on MFMA, P rounded to the input type (RNE); on
+//                         tiles after which some row's sum l is still small
+//                         (a few keys carry the row) the rounding residue
+//                         P - round(P) is rounded and multiplied in too.
 // The method is the streaming-softmax forward described on the triton-msl
 // part-1 post (section "What works, and where the edges are": Q staged once,
 // one loop over K/V tiles doing QK^T, online softmax with running max and
@@ -60,7 +61,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 // A running max is only raised when a tile's max exceeds it by more than
 // this many powers of two; until then p = exp2(t - m) stays below 2^8, which
-// fp32 sums and 16-bit P (8 exponent bits or more) hold without loss.
+// fp32 sums and 16-bit P (5 exponent bits or more) hold without overflow.
 constexpr float kRescaleThreshold = 8.0f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -76,6 +77,13 @@ __device__ __forceinline__ float max_with_other_half(float x) {
   float lo = x, hi = x;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
   return __builtin_fmaxf(lo, hi);
+}
+
+// x + (x of the lane 32 away), by the same exchange.
+__device__ __forceinline__ float sum_with_other_half(float x) {
+  float lo = x, hi = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+  return lo + hi;
 }
 
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -113,6 +121,11 @@ struct Elem<__bf16> {
   __device__ static float round_trip(float x) {
     return (float)(__bf16)x;
   }
+  // The two values of a packed pair, exactly, as fp32 (low half first).
+  __device__ static void unpack(uint32_t w, float& lo, float& hi) {
+    lo = __builtin_bit_cast(float, w << 16);
+    hi = __builtin_bit_cast(float, w & 0xffff0000u);
+  }
 };
 
 template <>
@@ -127,6 +140,11 @@ struct Elem<_Float16> {
     return __builtin_bit_cast(uint32_t, v);
   }
   __device__ static float round_trip(float x) { return (float)(_Float16)x; }
+  __device__ static void unpack(uint32_t w, float& lo, float& hi) {
+    const f16x2_t v = __builtin_bit_cast(f16x2_t, w);
+    lo = (float)v[0];
+    hi = (float)v[1];
+  }
 };
 
 template <>
@@ -246,12 +264,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
   int wkv_lo = 0;
   if (W > 0) wkv_lo = max(0, w0 + off - W + 1);
 
-  // Few visible keys for the wave's first row -> hi/lo split of P.
-  bool split = false;
-  if constexpr (!kWide) {
-    int nvis = (causal ? min(lk, w0 + off + 1) : lk) - wkv_lo;
-    split = (nvis < a.split_keys) || (BIAS && a.split_bias != 0);
-  }
 
   const T* __restrict__ kbase = reinterpret_cast<const T*>(a.k) + (int64_t)ck0 * a.k_st +
                                 (int64_t)g * a.k_sh;
@@ -507,56 +519,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
             }
           }
       } else {
-        // 16-bit: k-step kk covers keys 16kk..16kk+15.  The B operand of a
-        // lane is 8 consecutive S^T entries of its own column, i.e. keys
-        // 16kk + {0,1,2,3,8,9,10,11} + 4 hf; V^T rows in LDS store the keys
-        // of every 16-key group in exactly that order, so the A operand is
-        // one 16-byte read.
-        constexpr int PK = BN / 16;
-        u32x4_t ph[PK];
-        u32x4_t pl[PK];
-#pragma unroll
-        for (int kk = 0; kk < PK; ++kk) {
-          const int mb = kk >> 1;
-          const int b8 = 8 * (kk & 1);
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            ph[kk][w] = E::pack(s[mb][b8 + 2 * w], s[mb][b8 + 2 * w + 1]);
-        }
-        if (split) {
-#pragma unroll
-          for (int kk = 0; kk < PK; ++kk) {
-            const int mb = kk >> 1;
-            const int b8 = 8 * (kk & 1);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const float x0 = s[mb][b8 + 2 * w], x1 = s[mb][b8 + 2 * w + 1];
-              pl[kk][w] = E::pack(x0 - E::round_trip(x0), x1 - E::round_trip(x1));
-            }
-          }
-        }
-        if (split) {
-#pragma unroll
-          for (int kk = 0; kk < PK; ++kk) {
-#pragma unroll
-            for (int db = 0; db < G::NDB; ++db) {
-              const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(
-                  vs + (32 * db + l32) * G::VSTR + 16 * kk + 8 * hf);
-              o[db] = E::mma(vf, ph[kk], o[db]);
-              o[db] = E::mma(vf, pl[kk], o[db]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < PK; ++kk) {
-#pragma unroll
-            for (int db = 0; db < G::NDB; ++db) {
-              const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(
-                  vs + (32 * db + l32) * G::VSTR + 16 * kk + 8 * hf);
-              o[db] = E::mma(vf, ph[kk], o[db]);
-            }
-          }
-        }
+        static_assert(kWide, "the register-staged kernel runs fp32 inputs only");
       }
     }
 
@@ -648,8 +611,8 @@ __device__ __forceinline__ void load_tile_part(const char* base, int64_t st_b, i
 // PV MFMAs of tile t and tile t's softmax form one interleaved instruction
 // stream, with operand reads issued ahead of their MFMAs.  K and V have
 // separate double buffers so K(t+2) and V(t+1) stream in while tile t is
-// consumed.  Whether P is split into hi/lo halves is decided once per
-// workgroup (rows that see few keys), giving two straight-line variants.
+// consumed.  Whether a tile's P also needs its low half multiplied in is
+// decided per wave after the tile's row sums are known.
 // ----------------------------------------------------------------------------
 
 // Compile-time order of one tile's stream: QK^T MFMAs of the next tile
@@ -761,11 +724,13 @@ template <typename T, int DQK, int DV, bool BIAS, typename OutT>
 __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void attn_fwd16p_kernel(
     const KernelArgs a) {
   using E = Elem<T>;
-  // A row's running max m follows every increase of the row max (O and l
-  // are rescaled between tiles when one happens), so the row's largest p is
-  // exactly 1.  A stale m would leave it at some 2^f, f fractional, whose
-  // 16-bit rounding error (up to 2^-9 relative for bf16) lands on the
-  // dominant term of P V: up to 0.2% of |v| on a peaked row.
+  // A row's running max m lags the true row max by less than
+  // 2^kRescaleThreshold: O and l are rescaled between tiles only when a row's
+  // max grows by more than that, so most steps skip the O rescale.  The
+  // largest p of a row is then some 2^f rather than exactly 1, and its
+  // 16-bit rounding lands on the dominant term of P V; where that matters
+  // (rows whose sum l is small against their largest p) the tile's P is
+  // carried to 16 bits by the low-half pass of step().
   constexpr int NB = WaveBlocks<DQK, DV, BIAS>::NB;
   constexpr int NMB = WaveBlocks<DQK, DV, BIAS>::NMB;
   constexpr int RW = 32 * NB;  // query rows per wave
@@ -880,7 +845,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   int ck0 = a.cu_kv[seq], ck1 = a.cu_kv[seq + 1];
   asm volatile("" : "+s"(cq0), "+s"(cq1), "+s"(ck0), "+s"(ck1)
                : "s"(a.q_st), "s"(a.q_sh), "s"(a.k_st), "s"(a.k_sh), "s"(a.v_st), "s"(a.v_sh),
-                 "s"(a.group), "s"(a.causal), "s"(a.window), "s"(a.split_keys), "s"(a.n_qtiles));
+                 "s"(a.group), "s"(a.causal), "s"(a.window), "s"(a.n_qtiles));
   const int lq = cq1 - cq0;
   const int lk = ck1 - ck0;
   const int n_qtiles = (lq + BM - 1) / BM;
@@ -927,9 +892,6 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   const int wt_end = !wave_active ? t_begin
                      : causal    ? (min(lk, w1 - 1 + off + 1) + BN - 1) / BN
                                  : t_end;
-  // hi/lo split of P for the whole workgroup when its first row sees few keys
-  const int nvis0 = (causal ? min(lk, r0 + off + 1) : lk) - kv_lo;
-  const bool split = (nvis0 < a.split_keys) || (BIAS && a.split_bias != 0);
 
   const int64_t k_st_b = a.k_st * 2;
   const int64_t v_st_b = a.v_st * 2;
@@ -1091,7 +1053,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   };
   // Given the row max of tile t's (masked) scores for each query block, set
   // the pending max; returns true when some row's max exceeds its running
-  // max by more than the growth bound.  A row whose running max is still
+  // max by more than the growth bound (2^kRescaleThreshold).  A row whose running max is still
   // -inf (nothing visible yet: O and l are zero) adopts the new max.
   // mx holds the maxima over both halves of the wave (max_with_other_half).
   auto finish_max = [&](float (&mx)[NB], float (&m_pend)[NB]) __attribute__((device)) -> bool {
@@ -1102,7 +1064,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
       const float m_tile = BIAS ? m_all * kLog2e : m_all * c_scale;
       if (m_run[n] == kNegInf) m_run[n] = m_tile;
       m_pend[n] = m_tile;
-      grow = grow || (m_tile > m_run[n]);
+      grow = grow || (m_tile > m_run[n] + kRescaleThreshold);
     }
     return __ballot(grow) != 0ull;
   };
@@ -1159,12 +1121,14 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     return finish_max(mx, m_pend);
   };
 
-  // Rows whose max grew: move their running max and rescale O and l (kept
-  // outside the interleaved stream so that O needs no VALU work there).
+  // Rows whose max grew past the bound: move their running max and rescale
+  // O and l (kept outside the interleaved stream so that O needs no VALU
+  // work there).  Every other row multiplies by exactly 1, so a row's
+  // result never depends on the other rows of its wave.
   auto rescale = [&](const float (&m_pend)[NB]) __attribute__((device)) {
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const bool g = m_pend[n] > m_run[n];
+      const bool g = m_pend[n] > m_run[n] + kRescaleThreshold;
       const float alpha = g ? fast_exp2(m_run[n] - m_pend[n]) : 1.0f;
       if (g) m_run[n] = m_pend[n];
       l_run[n] *= alpha;
@@ -1181,14 +1145,13 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   // is packed, and tile t's softmax in pairs of scores, with operand reads
   // issued ahead.  Then tile t+1's scores are prepared; the return value says
   // whether a rescale is due before tile t+1.
-  auto step = [&](auto split_tag, auto slot_tag, int j, f32x16_t (&s_cur)[NB][NMB],
+  auto step = [&](auto slot_tag, int j, f32x16_t (&s_cur)[NB][NMB],
                   f32x16_t (&s_nxt)[NB][NMB], float (&m_pend)[NB],
                   f32x4_t (&bpre)[NB][NMB][4]) __attribute__((device)) -> bool {
-    constexpr bool SPLIT = decltype(split_tag)::value;
     constexpr int NKF = NMB * KSTEPS;     // K fragments per tile
     constexpr int NQK = NKF * NB;         // QK^T MFMAs per tile
     constexpr int NVF = NKS * NDB;        // V^T fragments per tile
-    constexpr int NPV = NVF * NB;         // PV MFMA slots per tile (x2 with the split)
+    constexpr int NPV = NVF * NB;         // PV MFMAs per tile
     // The next tile's masking, bias and row max run inside the stream, in
     // pieces after each key block's last QK^T MFMA.
     constexpr bool MAXOPS = true;
@@ -1249,11 +1212,14 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     kf[0] = kread(0);
     if (NKF > 1) kf[1] = kread(1);
     float neg_m[NB];
+    float m_cur[NB];  // this tile's row max (-inf: nothing visible to the row here)
 #pragma unroll
-    for (int n = 0; n < NB; ++n) neg_m[n] = (m_run[n] == kNegInf) ? 0.0f : -m_run[n];
+    for (int n = 0; n < NB; ++n) {
+      neg_m[n] = (m_run[n] == kNegInf) ? 0.0f : -m_run[n];
+      m_cur[n] = m_pend[n];
+    }
 
     u32x4_t ph[NB][NKS];
-    u32x4_t pl[NB][NKS];
     float lsum[NB];
 #pragma unroll
     for (int n = 0; n < NB; ++n) lsum[n] = 0.0f;
@@ -1278,7 +1244,6 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
         if (n == 0 && vi + 2 < NVF) vf[(vi + 2) % 3] = vread(vi + 2);
         const int kk = vi / NDB, db = vi % NDB;
         o[n][db] = E::mma(vf[vi % 3], ph[n][kk], o[n][db]);
-        if constexpr (SPLIT) o[n][db] = E::mma(vf[vi % 3], pl[n][kk], o[n][db]);
       } else if constexpr (op == kOpMax) {
         // next tile, query block n, key block mb: masking, then the max tree
         // (leaves of three entries, then two levels), in kMaxPieces pieces.
@@ -1341,25 +1306,62 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
         // Empty asm with in/out register operands: an optimisation fence
         // that keeps this pair's VALU work at its slot in the stream (pure
         // arithmetic would otherwise be sunk below the MFMAs).
-        if constexpr (SPLIT) {
-          uint32_t lw = E::pack(p0 - E::round_trip(p0), p1 - E::round_trip(p1));
-          asm volatile("" : "+v"(hw), "+v"(lw), "+v"(lsum[n]));
-          pl[n][kk][w] = lw;
-        } else {
-          asm volatile("" : "+v"(hw), "+v"(lsum[n]));
-        }
+        asm volatile("" : "+v"(hw), "+v"(lsum[n]));
         ph[n][kk][w] = hw;
+        // p stays in the score registers for a possible low-half pass
+        s_cur[n][mb][e0] = p0;
+        s_cur[n][mb][e0 + 1] = p1;
       }
       __builtin_amdgcn_sched_barrier(0);
     });
+    // Low halves of P.  The stream multiplied V by P rounded to 16 bits,
+    // which errs by up to 2^-9 (bf16) or 2^-12 (fp16) of each p.  Relative
+    // to the row's sum l those errors are at most about sqrt(p_max / l) of
+    // the rounding unit, p_max being this tile's largest p: they count only
+    // while l is small against p_max (a few keys of this tile carry the
+    // row).  So when a row has l < split_l * p_max after this tile, this
+    // tile's P - round(P) is rounded too and multiplied in: P is then carried
+    // to about 16 bits.  Each row decides for itself (the other rows of the
+    // wave multiply in zeros, an exact no-op), so that a row's result never
+    // depends on the other rows; rows that saw nothing in this tile skip it.
+    bool lo_row[NB];
+    bool lo_pass = false;
 #pragma unroll
-    for (int n = 0; n < NB; ++n) l_run[n] += lsum[n];
+    for (int n = 0; n < NB; ++n) {
+      l_run[n] += lsum[n];
+      const float l_row = sum_with_other_half(l_run[n]);
+      // this tile's largest p is exp2(m_cur - m_run) (below 2^kRescaleThreshold)
+      lo_row[n] = m_cur[n] != kNegInf && l_row < a.split_l * fast_exp2(m_cur[n] - m_run[n]);
+      lo_pass = lo_pass || lo_row[n];
+    }
+    if (__ballot(lo_pass) != 0ull) {
+#pragma unroll
+      for (int kk = 0; kk < NKS; ++kk) {
+        u32x4_t pl[NB];
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int mb = kk >> 1, e0 = 8 * (kk & 1) + 2 * w;
+            const float p0 = s_cur[n][mb][e0], p1 = s_cur[n][mb][e0 + 1];
+            float h0, h1;  // the rounded values the stream multiplied
+            E::unpack(E::pack(p0, p1), h0, h1);
+            pl[n][w] = lo_row[n] ? E::pack(p0 - h0, p1 - h1) : 0u;
+          }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const u32x4_t v = vfrag(vt, kk, db);
+#pragma unroll
+          for (int n = 0; n < NB; ++n) o[n][db] = E::mma(v, pl[n], o[n][db]);
+        }
+      }
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of V(t+LV), K(t+LK) have landed
     if constexpr (BAR) __syncthreads();
     return grow;
   };
 
-  auto run = [&](auto split_tag) __attribute__((device)) {
+  auto run = [&]() __attribute__((device)) {
     const int nt = t_end - t_begin;
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
@@ -1383,10 +1385,10 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     __syncthreads();  // every wave is done with K buffer 0 before it is refilled
     if constexpr (NSLOT == 2) {
       for (int j = 0; j < nt; j += 2) {
-        need = step(split_tag, S0{}, j, sa, sb, m_pend, bpre);
+        need = step(S0{}, j, sa, sb, m_pend, bpre);
         if (need) rescale(m_pend);
         if (j + 1 < nt) {
-          need = step(split_tag, S1{}, j + 1, sb, sa, m_pend, bpre);
+          need = step(S1{}, j + 1, sb, sa, m_pend, bpre);
           if (need) rescale(m_pend);
         }
       }
@@ -1394,18 +1396,18 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
       using S2 = std::integral_constant<int, 2>;
       using S3 = std::integral_constant<int, 3>;
       for (int j = 0; j < nt; j += 4) {
-        need = step(split_tag, S0{}, j, sa, sb, m_pend, bpre);
+        need = step(S0{}, j, sa, sb, m_pend, bpre);
         if (need) rescale(m_pend);
         if (j + 1 < nt) {
-          need = step(split_tag, S1{}, j + 1, sb, sa, m_pend, bpre);
+          need = step(S1{}, j + 1, sb, sa, m_pend, bpre);
           if (need) rescale(m_pend);
         }
         if (j + 2 < nt) {
-          need = step(split_tag, S2{}, j + 2, sa, sb, m_pend, bpre);
+          need = step(S2{}, j + 2, sa, sb, m_pend, bpre);
           if (need) rescale(m_pend);
         }
         if (j + 3 < nt) {
-          need = step(split_tag, S3{}, j + 3, sb, sa, m_pend, bpre);
+          need = step(S3{}, j + 3, sb, sa, m_pend, bpre);
           if (need) rescale(m_pend);
         }
       }
@@ -1414,10 +1416,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
       if (nt & 1) __syncthreads();
     }
   };
-  if (t_begin < t_end) {
-    if (split) run(std::true_type{});
-    else run(std::false_type{});
-  }
+  if (t_begin < t_end) run();
 
   // ---- epilogue: O / l staged through LDS (the K/V buffers are free after
   // the loop's last barrier), STAGE_ROWS rows of a 32-row query block at a

@@ -47,11 +47,13 @@ bool env_flag(const char* name) {
   return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
 }
 
-// Rows that see fewer keys than this get a hi/lo split of P in the PV
-// product (bf16 keeps 8 mantissa bits, so a plain bf16 P costs up to ~2e-3
-// of absolute output error when only a handful of keys are averaged).
-constexpr int kSplitKeysBf16 = 256;
-constexpr int kSplitKeysF16 = 64;
+// While a row's softmax sum l (in units of its largest p) is below this
+// after a tile, the tile's P is carried to 16 bits (hi + lo halves) in the
+// PV product.  bf16 keeps 8 significant bits: P rounded once errs by up to
+// 2^-9 of each p, and with only a few keys carrying the row that reaches
+// ~2e-3 of |v| in the output.  fp16 keeps 11 bits, 8x less.
+constexpr float kSplitLBf16 = 12.0f;
+constexpr float kSplitLF16 = 3.0f;
 
 int validate_cu(const int32_t* cu_dev, int64_t n, int64_t total, int64_t max_len,
                 const char* what) {
@@ -219,8 +221,7 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
   a.causal = p->causal;
   a.window = p->window;
   a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
-  a.split_keys = dt == MI_ATTN_BF16 ? kSplitKeysBf16 : (dt == MI_ATTN_F16 ? kSplitKeysF16 : 0);
-  a.split_bias = (has_bias && dt == MI_ATTN_BF16) ? 1 : 0;
+  a.split_l = dt == MI_ATTN_BF16 ? kSplitLBf16 : (dt == MI_ATTN_F16 ? kSplitLF16 : 0.0f);
 
   a.n_qtiles = (int32_t)n_qtiles;
   // A bias shared by all query heads (16-bit kernels): every head of one

@@ -175,6 +175,72 @@ def test_many_heads_bias_window(bias_heads):
     check(w.name, out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, w.dtype)
 
 
+@pytest.mark.parametrize("n_dom", [2, 3])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_near_tied_dominant_keys(d, dtype, n_dom):
+    """Rows that see 300-700 keys, where two or three keys in later tiles
+    carry almost all of the weight with logits a fraction of a unit apart
+    (p of the second and third near 0.5-1, not exactly representable) and
+    their values are large.  16-bit rounding of those p lands directly on
+    the output; the kernel must still meet the tolerance."""
+    lens = (700, 410)
+    w = W(name=f"near_tied_{n_dom}_{dtype}_d{d}", seqlens_q=lens, seqlens_kv=lens, hq=4, hkv=2,
+          d_qk=d, d_v=d, dtype=dtype, causal=True, seed=41 + d + n_dom)
+    say(f"[small] {w.name}")
+    inp = workloads.make_inputs(w)
+    rng = np.random.default_rng(42 + d + n_dom)
+    u = np.ones(d) / math.sqrt(d)
+    q = inp.q.double().numpy() + 3.0 * u
+    k = inp.k.double().numpy()
+    v = inp.v.double().numpy()
+    # dominant keys: one at the start of a tile, one mid-tile, one in the last tile
+    for s0, lk, keys in ((0, 700, (300, 301, 650)), (700, 410, (260, 333, 400))):
+        for i, key in enumerate(keys[:n_dom]):
+            k[s0 + key] = (2.2 - 0.04 * i) * math.sqrt(d) * u + 0.3 * rng.standard_normal((w.hkv, d))
+            v[s0 + key] = 2.5 * np.sign(rng.standard_normal((w.hkv, d)))
+    dt = inp.q.dtype
+    inp.q, inp.k, inp.v = (torch.from_numpy(x).to(dt) for x in (q, k, v))
+    out, lse = run_gpu(inp, out_dtype=torch.float32)
+    ref_out, ref_lse = run_oracle(inp)
+    check(w.name, out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, w.dtype)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_outlier_channels_bf16(d):
+    """bf16 with outlier channels (values 1e2..1e3 in four channels of q, k
+    and v, as transformer activations spike).  fp32 accumulation keeps the
+    result finite; channels without outliers meet the absolute bf16
+    tolerance, the outlier channels (magnitude ~1e3, where one fp32 ulp is
+    already 6e-5) the same tolerance relative to their magnitude."""
+    w = W(name=f"outlier_bf16_d{d}", seqlens_q=(333, 200), seqlens_kv=(333, 200), hq=2, hkv=2,
+          d_qk=d, d_v=d, dtype="bf16", causal=True, seed=43 + d)
+    inp = workloads.make_inputs(w)
+    g = torch.Generator().manual_seed(44 + d)
+    chans = {}
+    for name in ("q", "k", "v"):
+        t = getattr(inp, name)
+        ch = torch.randperm(d, generator=g)[:4]
+        t[:, :, ch] = (torch.rand(t.shape[0], t.shape[1], 4, generator=g) * 900 + 100).to(t.dtype)
+        chans[name] = ch
+    say(f"[outlier] {w.name}")
+    out, lse = run_gpu(inp, out_dtype=torch.float32)
+    ref_out, ref_lse = run_oracle(inp)
+    out = out.cpu().numpy()
+    assert np.isfinite(out).all()
+    vch = chans["v"].numpy()
+    plain = np.setdiff1d(np.arange(d), vch)
+    e_plain = float(np.abs(out[:, :, plain] - ref_out[:, :, plain]).max())
+    scale = float(np.abs(ref_out[:, :, vch]).max())
+    e_out = float(np.abs(out[:, :, vch] - ref_out[:, :, vch]).max()) / scale
+    e_lse = float(np.abs(lse.cpu().numpy() - ref_lse).max())
+    say(f"  plain channels {e_plain:.3e}, outlier channels {e_out:.3e} of {scale:.0f}, "
+        f"lse {e_lse:.3e} (|lse| up to {np.abs(ref_lse).max():.3g})")
+    assert e_plain <= 2e-3
+    assert e_out <= 2e-3
+    assert e_lse <= 1e-4 * max(1.0, float(np.abs(ref_lse).max()))
+
+
 def test_outlier_channels_fp32_accumulation():
     """A few channels of magnitude 1e2..1e3: 16-bit accumulation would
     overflow; fp32 accumulation must keep the result finite and correct."""
