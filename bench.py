@@ -37,6 +37,7 @@ METRIC = "attn fwd useful TFLOP/s + % of MI355X bf16 MFMA peak (causal GQA D=128
 # bf16/fp16; fp32 matrix 157.3.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 HBM_GBPS = 8000.0
+CPU_SHARE = 16  # host cores a one-GPU machine is given
 KERNEL_SOURCE = os.path.join(ROOT, "flash_attention_varlen_amd", "csrc", "attn_fwd_kernels.h")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -178,6 +179,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=15)
+    ap.add_argument("--prewarm-ms", type=float, default=500.0,
+                    help="before the warmup steps, run the step back to back for this long so the "
+                         "GPU reaches its steady clock (0 = off)")
     ap.add_argument("--workload", default="gqa_causal_bf16", choices=sorted(workloads.ALL))
     ap.add_argument("--out-dtype", default="input", choices=["input", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -215,11 +219,20 @@ def main():
     # in this process touches the GPU.
     cpu = None
     if not args.no_cpu_baseline:
-        cores = min(len(os.sched_getaffinity(0)), 16)
+        # One process per host core this process may use, at most 16: a
+        # one-GPU machine is given a 16-core share of its host, whatever the
+        # affinity mask shows.
+        visible = len(os.sched_getaffinity(0))
+        cores = min(visible, CPU_SHARE)
         heads = list(range(0, w.hq, max(1, w.hq // args.cpu_heads)))[:args.cpu_heads]
         print(f"# CPU oracle baseline on {cores} processes, heads {heads} ...", file=sys.stderr,
               flush=True)
         cpu = cpu_baseline(inp, heads, cores)
+        cpu["host_cores_visible"] = visible
+        cpu["cores_note"] = (f"{cores} worker processes: all {visible} cores this process may use"
+                             if cores == visible else
+                             f"{cores} worker processes: the {CPU_SHARE}-core share of the host a "
+                             f"one-GPU box is given ({visible} cores visible)")
         print(f"# CPU oracle: {cpu['value']:.4g} TFLOP/s in {cpu['seconds']} s", file=sys.stderr,
               flush=True)
 
@@ -244,6 +257,18 @@ def main():
                              causal=w.causal, window=w.window, attn_bias=bias, out=out, lse=lse,
                              out_dtype=out_dtype, stream=stream.cuda_stream)
 
+    # GPU clocks depend on the load state: a cold GPU reads well below its
+    # warmed rate (the mtlattn 0.3.0 page, section "Performance", gives the
+    # same caveat for Apple GPUs).  Run the step back to back until the clock
+    # settles, then the W warmup steps, then exactly K timed steps.
+    prewarm_launches = 0
+    if args.prewarm_ms > 0:
+        t_pw = time.perf_counter()
+        while (time.perf_counter() - t_pw) * 1e3 < args.prewarm_ms:
+            for _ in range(20):
+                step()
+            prewarm_launches += 20
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -333,6 +358,7 @@ def main():
             "pct_of_peak": round(100.0 * value / peak, 2),
             "median_launch_ms": round(per[len(per) // 2], 4),
             "host_wall_s": round(wall, 3),
+            "prewarm": {"ms": args.prewarm_ms, "launches": prewarm_launches},
             "parallelism": "single GPU",
         },
         "roofline": {

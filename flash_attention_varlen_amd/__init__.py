@@ -127,10 +127,18 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     """Fused varlen attention forward.  Returns ``out`` or ``(out, lse)``.
 
     q ``[Tq, Hq, Dqk]``, k ``[Tk, Hkv, Dqk]``, v ``[Tk, Hkv, Dv]`` (device,
-    last dim contiguous); ``out`` is ``[Tq, Hq, Dv]`` in ``out_dtype``
-    (default: q's dtype; ``torch.float32`` is also accepted); ``lse`` is
-    ``[Hq, Tq]`` fp32 (natural log).  Forward only: inputs that require grad
-    are refused.
+    last dim contiguous, any token / head strides the C ABI accepts);
+    ``out`` is ``[Tq, Hq, Dv]`` in ``out_dtype`` (default: q's dtype;
+    ``torch.float32`` is also accepted); ``lse`` is ``[Hq, Tq]`` fp32
+    (natural log).  Forward only: inputs that require grad are refused.
+
+    ``stream`` (a ``torch.cuda.Stream``, a raw ``hipStream_t`` handle, or
+    None for the current stream) is where the kernel runs; outputs and the
+    converted bias are allocated on it too.  The caller orders the inputs'
+    producers before it.  A bool ``attn_bias`` (True = visible) becomes an
+    fp32 0 / -inf tensor whose last dim is padded to a multiple of 4; an
+    fp32 bias whose strides are not multiples of 4 elements is copied into
+    such a layout.
     """
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -153,6 +161,54 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     if k.shape[2] != dqk or v.shape[0] != tk or v.shape[1] != hkv:
         raise MiAttnError(ERR_INVALID_ARG, "k/v shapes do not match q")
     out_dtype = q.dtype if out_dtype is None else out_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if stream is None:
+        s_obj = torch.cuda.current_stream(q.device)
+    elif isinstance(stream, torch.cuda.Stream):
+        s_obj = stream
+    else:
+        s_obj = torch.cuda.ExternalStream(int(stream), device=q.device)
+    with torch.cuda.stream(s_obj):
+        return _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
+                                           scale, causal, window, attn_bias, out_dtype,
+                                           return_lse, out, lse, tile_counts, s_obj, tq, hq, dqk,
+                                           tk, hkv, dv)
+
+
+def _aligned_bias(bias):
+    """fp32 [Tq, H, C] with strides that are multiples of 4 elements, from a
+    bool mask (True = visible -> 0, False -> -inf) or an fp32 bias."""
+    import torch
+    cols = bias.shape[2]
+    if bias.dtype == torch.bool:
+        buf = torch.empty(bias.shape[0], bias.shape[1], (cols + 3) // 4 * 4, dtype=torch.float32,
+                          device=bias.device)
+        view = buf[:, :, :cols]
+        view.zero_().masked_fill_(~bias, float("-inf"))
+        return view
+    if bias.stride(0) % 4 == 0 and bias.stride(1) % 4 == 0 and bias.data_ptr() % 16 == 0:
+        return bias
+    buf = torch.empty(bias.shape[0], bias.shape[1], (cols + 3) // 4 * 4, dtype=torch.float32,
+                      device=bias.device)
+    view = buf[:, :, :cols]
+    view.copy_(bias)
+    return view
+
+
+def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, scale, causal,
+                                window, attn_bias, out_dtype, return_lse, out, lse, tile_counts,
+                                s_obj, tq, hq, dqk, tk, hkv, dv):
+    import torch
+    bias = attn_bias
+    if bias is not None:
+        if (bias.dtype not in (torch.float32, torch.bool) or bias.dim() != 3
+                or bias.stride(-1) != 1 or not bias.is_cuda):
+            raise MiAttnError(ERR_INVALID_ARG,
+                              "attn_bias must be fp32 or bool [Tq, H or 1, max_kv] on device")
+        if bias.shape[0] != tq or bias.shape[1] not in (1, hq):
+            raise MiAttnError(ERR_INVALID_ARG, "attn_bias must be [Tq, H or 1, max_kv]")
+        bias = _aligned_bias(bias)
     if out is None:
         out = torch.empty(tq, hq, dv, dtype=out_dtype, device=q.device)
     elif out.shape != (tq, hq, dv) or out.dtype != out_dtype or out.stride(-1) != 1:
@@ -162,17 +218,6 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     if lse is not None and (lse.shape != (hq, tq) or lse.dtype != torch.float32
                             or not lse.is_contiguous()):
         raise MiAttnError(ERR_INVALID_ARG, "lse must be a contiguous fp32 [Hq, Tq] tensor")
-    bias = attn_bias
-    if bias is not None:
-        if bias.dtype == torch.bool:
-            bias = torch.zeros(bias.shape, dtype=torch.float32, device=bias.device).masked_fill_(
-                ~bias, float("-inf"))
-        if bias.dtype != torch.float32 or bias.dim() != 3 or bias.stride(-1) != 1 or not bias.is_cuda:
-            raise MiAttnError(ERR_INVALID_ARG, "attn_bias must be fp32 [Tq, H or 1, max_kv] on device")
-        if bias.shape[0] != tq or bias.shape[1] not in (1, hq):
-            raise MiAttnError(ERR_INVALID_ARG, "attn_bias must be [Tq, H or 1, max_kv]")
-    if scale is None:
-        scale = 1.0 / math.sqrt(dqk)
 
     p = MiAttnFwdParams()
     p.q, p.k, p.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
@@ -198,7 +243,5 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     p.scale = float(scale)
     p.causal = 1 if causal else 0
     p.window = int(window)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    mi_attn_varlen_fwd(p, int(stream))
+    mi_attn_varlen_fwd(p, int(s_obj.cuda_stream))
     return (out, lse) if return_lse else out

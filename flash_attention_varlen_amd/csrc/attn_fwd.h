@@ -34,6 +34,7 @@ struct KernelArgs {
   int32_t hq;
   int32_t group;  // hq / hkv
   int32_t bias_heads;
+  int32_t bias_cols;   // bias columns; keys at or past it read a bias of 0 (never out of bounds)
   int32_t causal;
   int32_t window;
   float scale_log2;    // softmax scale * log2(e)

@@ -452,11 +452,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
           for (int qd = 0; qd < 4; ++qd) {
             const int key0 = kb + 32 * mb + 8 * qd + 4 * hf;
             f32x4_t bv;
-            if (row_ok && key0 + 3 < lk) {
+            const int blim = min(lk, a.bias_cols);  // bias columns read: below both
+            if (row_ok && key0 + 3 < blim) {
               bv = *reinterpret_cast<const f32x4_t*>(brow + key0);
             } else {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) bv[e] = (row_ok && key0 + e < lk) ? brow[key0 + e] : 0.0f;
+              for (int e = 0; e < 4; ++e) bv[e] = (row_ok && key0 + e < blim) ? brow[key0 + e] : 0.0f;
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -1072,6 +1073,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   // keys past the sequence end read as 0 (they are masked).  They are loaded
   // at the start of the step whose end consumes them (prep_tile of the next
   // tile), so the loads' latency is hidden behind that step's stream.
+  const int blim = BIAS ? min(lk, a.bias_cols) : 0;  // bias columns read: below both
   auto load_bias = [&](int t, f32x4_t (&bv)[NB][NMB][4]) __attribute__((device)) {
     const int kb = t * BN;
 #pragma unroll
@@ -1081,12 +1083,12 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           const int key0 = kb + 32 * mb + 8 * qd + 4 * hf;
-          if (row_ok[n] && key0 + 3 < lk) {
+          if (row_ok[n] && key0 + 3 < blim) {
             bv[n][mb][qd] = *reinterpret_cast<const f32x4_t*>(brow[n] + key0);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              bv[n][mb][qd][e] = (row_ok[n] && key0 + e < lk) ? brow[n][key0 + e] : 0.0f;
+              bv[n][mb][qd][e] = (row_ok[n] && key0 + e < blim) ? brow[n][key0 + e] : 0.0f;
           }
         }
   };

@@ -55,6 +55,21 @@ bool env_flag(const char* name) {
 constexpr float kSplitLBf16 = 12.0f;
 constexpr float kSplitLF16 = 3.0f;
 
+// The n_tok x n_head x width elements at t * st + h * sh + d (d < width)
+// are pairwise distinct: the smaller stride spans a full row and the larger
+// one spans the whole extent of the smaller dimension (a dimension of size 1
+// places no constraint).  Exotic interleavings that are disjoint but fail
+// this test are refused, not miscomputed.
+bool layout_disjoint(int64_t st, int64_t n_tok, int64_t sh, int64_t n_head, int64_t width) {
+  if (n_tok <= 1 && n_head <= 1) return true;
+  if (n_tok <= 1) return sh >= width;
+  if (n_head <= 1) return st >= width;
+  const bool tok_inner = st <= sh;
+  const int64_t s_in = tok_inner ? st : sh, n_in = tok_inner ? n_tok : n_head;
+  const int64_t s_out = tok_inner ? sh : st;
+  return s_in >= width && s_out >= s_in * (n_in - 1) + width;
+}
+
 int validate_cu(const int32_t* cu_dev, int64_t n, int64_t total, int64_t max_len,
                 const char* what) {
   std::vector<int32_t> cu(static_cast<size_t>(n + 1));
@@ -160,10 +175,16 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
       p->out_stride_head % out_mult != 0)
     return fail(MI_ATTN_ERR_INVALID_ARG, "out strides must be non-negative multiples of %lld",
                 (long long)out_mult);
-  // Output rows must not overlap; the 16-bit kernels store 32-row blocks
-  // through 32-bit buffer offsets.
+  // Output rows must not overlap (different workgroups would write the same
+  // addresses); the 16-bit kernels store 32-row blocks through 32-bit buffer
+  // offsets.
   if (p->out_stride_tok < p->d_v)
     return fail(MI_ATTN_ERR_UNSUPPORTED, "out token stride must be >= d_v");
+  if (!layout_disjoint(p->out_stride_tok, p->total_q, p->out_stride_head, p->hq, p->d_v))
+    return fail(MI_ATTN_ERR_UNSUPPORTED,
+                "out strides (token %lld, head %lld) make the [%lld, %d, %d] rows overlap",
+                (long long)p->out_stride_tok, (long long)p->out_stride_head, (long long)p->total_q,
+                p->hq, p->d_v);
   if (dt != MI_ATTN_F32 && p->out_stride_tok * elem_size(p->out_dtype) * 32 > INT32_MAX)
     return fail(MI_ATTN_ERR_UNSUPPORTED, "out token stride too large (more than 64 MiB per token)");
   const bool has_bias = p->bias != nullptr;
@@ -212,6 +233,7 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
   a.o_st = p->out_stride_tok;
   a.o_sh = p->out_stride_head;
   a.b_st = has_bias ? p->bias_stride_tok : 0;
+  a.bias_cols = has_bias ? (int32_t)(p->bias_cols < INT32_MAX ? p->bias_cols : INT32_MAX) : 0;
   a.b_sh = has_bias ? p->bias_stride_head : 0;
   a.total_q = p->total_q;
   a.num_seqs = (int32_t)p->num_seqs;

@@ -83,13 +83,15 @@ enum { MI_ATTN_F32 = 0, MI_ATTN_F16 = 1, MI_ATTN_BF16 = 2 };
  *
  * Sizes: num_seqs >= 0, max_seqlen_q >= every sequence's query length,
  * total_q / total_kv = cu_seqlens_q[num_seqs] / cu_seqlens_kv[num_seqs],
- * bias_cols >= every sequence's key length.
+ * bias_cols >= every sequence's key length (the kernels never read a bias
+ * column at or past bias_cols: a key there would get a bias of 0).
  * Strides are in elements (not bytes); *_stride_tok between consecutive
  * tokens, *_stride_head between consecutive heads; each must be a multiple
  * of 8 elements for 16-bit types and of 4 for fp32.  q/k token strides must
  * be >= d_qk and v's and out's >= d_v; for 16-bit types 64 q/k/v token
- * strides and 32 out token strides must fit in 2^31 bytes.  Anything else is
- * refused with MI_ATTN_ERR_UNSUPPORTED.
+ * strides and 32 out token strides must fit in 2^31 bytes; the out strides
+ * must keep the [total_q, hq, d_v] rows disjoint.  Anything else is refused
+ * with MI_ATTN_ERR_UNSUPPORTED.
  *
  * The device-side contracts (cu_seqlens non-decreasing from 0 to total,
  * lengths within max_seqlen_q / bias_cols) are the caller's; with the

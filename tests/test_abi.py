@@ -106,6 +106,11 @@ REFUSALS = {
     "too_many_q_tiles": (dict(max_seqlen_q=128 * 65536), fav.ERR_UNSUPPORTED),
     "overlapping_out_rows": (dict(out_stride_tok=64, out_stride_head=8), fav.ERR_UNSUPPORTED),
     "huge_out_stride": (dict(out_stride_tok=1 << 26), fav.ERR_UNSUPPORTED),
+    # head slices of one token overlap (head stride below d_v)
+    "overlapping_out_heads": (dict(out_stride_tok=8 * 128 * 8, out_stride_head=64),
+                              fav.ERR_UNSUPPORTED),
+    # token rows overlap the next token's heads (token stride below hq * d_v)
+    "overlapping_out_tokens": (dict(out_stride_tok=512, out_stride_head=128), fav.ERR_UNSUPPORTED),
 }
 
 
