@@ -179,7 +179,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=15)
-    ap.add_argument("--prewarm-ms", type=float, default=500.0,
+    ap.add_argument("--prewarm-ms", type=float, default=1000.0,
                     help="before the warmup steps, run the step back to back for this long so the "
                          "GPU reaches its steady clock (0 = off)")
     ap.add_argument("--workload", default="gqa_causal_bf16", choices=sorted(workloads.ALL))
