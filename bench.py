@@ -193,6 +193,8 @@ def main():
                     help="after the timed region, time this many launches each preceded by a "
                          "write of --flush-mib MiB (evicts L2 and the MALL); reported under 'cold'")
     ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--no-bias-ranges", action="store_true",
+                    help="with a bias, do not compute the bias key ranges (visit every tile)")
     ap.add_argument("--window", type=int, default=None,
                     help="override the window width of a sliding-window workload (cost vs W)")
     args = ap.parse_args()
@@ -252,10 +254,19 @@ def main():
     lse = torch.empty(w.hq, w.total_q, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    # With a bias, each step first computes the bias rows' key ranges (one
+    # read of the bias), then the forward skips the -inf tiles outside them.
+    use_ranges = bias is not None and not args.no_bias_ranges
+
+    def step(mid_event=None):
+        rg = None
+        if use_ranges:
+            rg = fav.bias_key_ranges(bias, cq, ck, w.max_seqlen_q, stream=stream)
+        if mid_event is not None:
+            mid_event.record(stream)
         fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, scale=w.softmax_scale,
                              causal=w.causal, window=w.window, attn_bias=bias, out=out, lse=lse,
-                             out_dtype=out_dtype, stream=stream.cuda_stream)
+                             out_dtype=out_dtype, stream=stream, bias_ranges=rg)
 
     # GPU clocks depend on the load state: a cold GPU reads well below its
     # warmed rate (the mtlattn 0.3.0 page, section "Performance", gives the
@@ -277,20 +288,24 @@ def main():
     # around the whole timed region
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     start_all = torch.cuda.Event(enable_timing=True)
     end_all = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start_all.record(stream)
-    for s, e in evs:
+    for (s, e), m in zip(evs, mids):
         s.record(stream)
-        step()
+        step(m)
         e.record(stream)
     end_all.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start_all.elapsed_time(end_all)
-    per = sorted(s.elapsed_time(e) for s, e in evs)
+    # the attention kernel alone: from the event after the range pass (if
+    # any) to the end of the step
+    per = sorted(m.elapsed_time(e) for (s, e), m in zip(evs, mids))
+    pre_ms = [s.elapsed_time(m) for (s, e), m in zip(evs, mids)]
     ms_per_step = total_ms / args.steps
     kernel_ms = sum(per) / len(per)
 
@@ -359,6 +374,7 @@ def main():
             "median_launch_ms": round(per[len(per) // 2], 4),
             "host_wall_s": round(wall, 3),
             "prewarm": {"ms": args.prewarm_ms, "launches": prewarm_launches},
+            "bias_ranges_pass_ms": round(sum(pre_ms) / len(pre_ms), 4) if use_ranges else None,
             "parallelism": "single GPU",
         },
         "roofline": {

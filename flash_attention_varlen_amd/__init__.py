@@ -21,7 +21,7 @@ import os
 from typing import Optional
 
 __all__ = ["mi_attn_varlen_fwd", "mi_attn_last_error", "mi_attn_version", "mi_attn_tile_shape",
-           "varlen_attention", "MiAttnFwdParams", "MiAttnError", "load_library", "LIB_PATH",
+           "mi_attn_bias_key_ranges", "bias_key_ranges", "varlen_attention", "MiAttnFwdParams", "MiAttnError", "load_library", "LIB_PATH",
            "F32", "F16", "BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi_attn.so")
@@ -57,6 +57,7 @@ class MiAttnFwdParams(ctypes.Structure):
         ("bias_stride_tok", ctypes.c_int64), ("bias_stride_head", ctypes.c_int64),
         ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
         ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("bias_ranges", ctypes.c_void_p),
     ]
 
 
@@ -81,6 +82,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mi_attn_tile_shape.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     lib.mi_attn_tile_shape.restype = ctypes.c_int
+    lib.mi_attn_bias_key_ranges.argtypes = [ctypes.POINTER(MiAttnFwdParams), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+    lib.mi_attn_bias_key_ranges.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -111,6 +115,15 @@ def mi_attn_varlen_fwd(params: MiAttnFwdParams, stream: int = 0) -> None:
         raise MiAttnError(rc, mi_attn_last_error())
 
 
+def mi_attn_bias_key_ranges(params: MiAttnFwdParams, ranges_ptr: int, stream: int = 0) -> None:
+    """Call the C entry point; raise MiAttnError on a non-OK return."""
+    params.struct_size = ctypes.sizeof(MiAttnFwdParams)
+    rc = load_library().mi_attn_bias_key_ranges(ctypes.byref(params), ctypes.c_void_p(ranges_ptr),
+                                                ctypes.c_void_p(stream))
+    if rc != OK:
+        raise MiAttnError(rc, mi_attn_last_error())
+
+
 # ---------------------------------------------------------------- torch front end
 def _dtype_code(t) -> int:
     import torch
@@ -123,7 +136,7 @@ def _dtype_code(t) -> int:
 def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
                      scale: Optional[float] = None, causal: bool = False, window: int = 0,
                      attn_bias=None, out_dtype=None, return_lse: bool = False, out=None,
-                     lse=None, tile_counts=None, stream=None):
+                     lse=None, tile_counts=None, stream=None, bias_ranges=None):
     """Fused varlen attention forward.  Returns ``out`` or ``(out, lse)``.
 
     q ``[Tq, Hq, Dqk]``, k ``[Tk, Hkv, Dqk]``, v ``[Tk, Hkv, Dv]`` (device,
@@ -138,7 +151,8 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     producers before it.  A bool ``attn_bias`` (True = visible) becomes an
     fp32 0 / -inf tensor whose last dim is padded to a multiple of 4; an
     fp32 bias whose strides are not multiples of 4 elements is copied into
-    such a layout.
+    such a layout.  ``bias_ranges`` (from ``bias_key_ranges`` on the same
+    bias) lets the kernels skip key tiles that are -inf for all their rows.
     """
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -163,17 +177,57 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
-    if stream is None:
-        s_obj = torch.cuda.current_stream(q.device)
-    elif isinstance(stream, torch.cuda.Stream):
-        s_obj = stream
-    else:
-        s_obj = torch.cuda.ExternalStream(int(stream), device=q.device)
+    s_obj = _stream_of(stream, q.device)
+    if bias_ranges is not None:
+        if attn_bias is None:
+            raise MiAttnError(ERR_INVALID_ARG, "bias_ranges needs the attn_bias it was computed from")
+        if (bias_ranges.dtype != torch.int32 or not bias_ranges.is_contiguous()
+                or bias_ranges.shape != (attn_bias.shape[1], tq, 2)):
+            raise MiAttnError(ERR_INVALID_ARG, "bias_ranges must be contiguous int32 [H_b, Tq, 2]")
     with torch.cuda.stream(s_obj):
         return _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
                                            scale, causal, window, attn_bias, out_dtype,
                                            return_lse, out, lse, tile_counts, s_obj, tq, hq, dqk,
-                                           tk, hkv, dv)
+                                           tk, hkv, dv, bias_ranges)
+
+
+def _stream_of(stream, device):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def bias_key_ranges(attn_bias, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int, stream=None):
+    """int32 ``[H_b, Tq, 2]``: for each bias row, the first and one-past-last
+    key of its sequence whose bias is not -inf (``[0, 0)`` if none).  Pass the
+    result as ``bias_ranges`` to ``varlen_attention`` with the same bias: the
+    kernels then skip, exactly, key tiles whose bias is -inf for all their
+    rows.  Valid for as long as the bias and cu_seqlens are."""
+    import torch
+    if attn_bias.dim() != 3 or not attn_bias.is_cuda or attn_bias.stride(-1) != 1:
+        raise MiAttnError(ERR_INVALID_ARG, "attn_bias must be [Tq, H or 1, max_kv] on device")
+    s_obj = _stream_of(stream, attn_bias.device)
+    with torch.cuda.stream(s_obj):
+        bias = _aligned_bias(attn_bias) if attn_bias.dtype in (torch.float32, torch.bool) else None
+        if bias is None:
+            raise MiAttnError(ERR_INVALID_ARG, "attn_bias must be fp32 or bool")
+        tq, hb, cols = bias.shape
+        ranges = torch.empty(hb, tq, 2, dtype=torch.int32, device=bias.device)
+        p = MiAttnFwdParams()
+        p.bias = bias.data_ptr()
+        p.cu_seqlens_q, p.cu_seqlens_kv = cu_seqlens_q.data_ptr(), cu_seqlens_kv.data_ptr()
+        p.num_seqs = cu_seqlens_q.numel() - 1
+        p.max_seqlen_q = int(max_seqlen_q)
+        p.total_q = tq
+        p.hq = hb
+        p.bias_heads = hb
+        p.bias_cols = cols
+        p.bias_stride_tok, p.bias_stride_head = bias.stride(0), bias.stride(1)
+        mi_attn_bias_key_ranges(p, ranges.data_ptr(), int(s_obj.cuda_stream))
+    return ranges
 
 
 def _aligned_bias(bias):
@@ -198,7 +252,7 @@ def _aligned_bias(bias):
 
 def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, scale, causal,
                                 window, attn_bias, out_dtype, return_lse, out, lse, tile_counts,
-                                s_obj, tq, hq, dqk, tk, hkv, dv):
+                                s_obj, tq, hq, dqk, tk, hkv, dv, bias_ranges=None):
     import torch
     bias = attn_bias
     if bias is not None:
@@ -225,6 +279,7 @@ def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen
     p.lse = lse.data_ptr() if lse is not None else None
     p.cu_seqlens_q, p.cu_seqlens_kv = cu_seqlens_q.data_ptr(), cu_seqlens_kv.data_ptr()
     p.bias = bias.data_ptr() if bias is not None else None
+    p.bias_ranges = bias_ranges.data_ptr() if bias_ranges is not None else None
     p.tile_counts = tile_counts.data_ptr() if tile_counts is not None else None
     p.num_seqs = cu_seqlens_q.numel() - 1
     p.max_seqlen_q = int(max_seqlen_q)

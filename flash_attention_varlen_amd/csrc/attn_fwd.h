@@ -26,6 +26,7 @@ struct KernelArgs {
   const int32_t* cu_q;
   const int32_t* cu_kv;
   const float* bias;
+  const int32_t* bias_ranges;  // optional [bias_heads, total_q, 2] key ranges of the bias rows
   int32_t* tile_counts;
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
   int64_t b_st, b_sh;

@@ -86,6 +86,41 @@ __device__ __forceinline__ float sum_with_other_half(float x) {
   return lo + hi;
 }
 
+// Minimum / maximum of an int over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_min_i32(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_max_i32(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Key hull of the bias rows [r0, r0 + rows) of one sequence and head: the
+// smallest lo and largest hi over the rows' ranges [lo, hi) of keys whose
+// bias is not -inf (empty ranges count for nothing), and the largest hi over
+// the rows [w0, w0 + wrows).  Every lane of the wave returns the same values.
+struct KeyHull {
+  int lo, hi, wave_hi;
+};
+__device__ __forceinline__ KeyHull bias_key_hull(const int32_t* rg, int r0, int rows, int lq, int w0,
+                                                 int wrows, int lane) {
+  int lo = 0x7fffffff, hi = 0, whi = 0;
+  for (int r = r0 + lane; r < min(lq, r0 + rows); r += 64) {
+    const int2 v = *reinterpret_cast<const int2*>(rg + 2 * (int64_t)r);
+    if (v.y > v.x) {
+      lo = min(lo, v.x);
+      hi = max(hi, v.y);
+      if (r >= w0 && r < w0 + wrows) whi = max(whi, v.y);
+    }
+  }
+  return KeyHull{__builtin_amdgcn_readfirstlane(wave_min_i32(lo)),
+                 __builtin_amdgcn_readfirstlane(wave_max_i32(hi)),
+                 __builtin_amdgcn_readfirstlane(wave_max_i32(whi))};
+}
+
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
@@ -246,6 +281,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
   if (causal) kv_hi = min(lk, r1 - 1 + off + 1);
   int kv_lo = 0;
   if (W > 0) kv_lo = max(0, r0 + off - W + 1);
+  if constexpr (BIAS) {
+    // keys outside the hull of the rows' bias ranges have a -inf bias
+    if (a.bias_ranges != nullptr) {
+      const int32_t* rg = a.bias_ranges +
+          ((int64_t)(a.bias_heads == 1 ? 0 : head) * a.total_q + cq0) * 2;
+      const KeyHull h = bias_key_hull(rg, r0, kBM, lq, r0, kBM, tid & 63);
+      kv_lo = max(kv_lo, h.lo);
+      kv_hi = min(kv_hi, h.hi);
+    }
+  }
   const int t_begin = kv_lo / BN;
   int t_end = kv_hi > 0 ? (kv_hi + BN - 1) / BN : 0;
   if (t_end < t_begin) t_end = t_begin;
@@ -865,6 +910,21 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   if (causal) kv_hi = min(lk, r1 - 1 + off + 1);
   int kv_lo = 0;
   if (W > 0) kv_lo = max(0, r0 + off - W + 1);
+  // With the bias rows' key ranges given: keys outside the hull of the
+  // workgroup's rows have a -inf bias for every row, so their tiles are
+  // skipped exactly as masked tiles are; a wave also stops after the last
+  // tile its own rows can see.
+  int wave_bias_hi = lk;
+  if constexpr (BIAS) {
+    if (a.bias_ranges != nullptr) {
+      const int32_t* rg = a.bias_ranges +
+          ((int64_t)(a.bias_heads == 1 ? 0 : head) * a.total_q + cq0) * 2;
+      const KeyHull h = bias_key_hull(rg, r0, BM, lq, r0 + wave * RW, RW, lane);
+      kv_lo = max(kv_lo, h.lo);
+      kv_hi = min(kv_hi, h.hi);
+      wave_bias_hi = h.wave_hi;
+    }
+  }
   const int t_begin = kv_lo / BN;
   int t_end = kv_hi > 0 ? (kv_hi + BN - 1) / BN : 0;
   if (t_end < t_begin) t_end = t_begin;
@@ -890,9 +950,10 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   // rows that end before the workgroup's last diagonal; no rows at all past
   // the sequence end): the wave skips their work but still does its share of
   // the copies and the barriers.
-  const int wt_end = !wave_active ? t_begin
-                     : causal    ? (min(lk, w1 - 1 + off + 1) + BN - 1) / BN
-                                 : t_end;
+  const int wt_end = max(t_begin, min(!wave_active ? t_begin
+                                      : causal    ? (min(lk, w1 - 1 + off + 1) + BN - 1) / BN
+                                                  : t_end,
+                                      (wave_bias_hi + BN - 1) / BN));
 
   const int64_t k_st_b = a.k_st * 2;
   const int64_t v_st_b = a.v_st * 2;

@@ -1,0 +1,80 @@
+// Key ranges of additive-bias rows: for every query row and bias head, the
+// first and one-past-last key of its sequence whose bias is not -inf.  Keys
+// whose bias is -inf contribute exactly nothing to the softmax (mtlattn 0.3.0
+// project page, section "Use": the bias composes with the masks; the
+// triton-msl part-2 post, section "FlashAttention: faster than PyTorch,
+// competitive with MLX": skipping fully masked tiles is exact), so the
+// forward kernels skip the key tiles outside a workgroup's hull of these
+// ranges.  One wave per row; the row is read once with 16-byte loads, so the
+// pass is bound by HBM bandwidth (4 bytes per bias element).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bias_ranges.h"
+
+namespace mi_attn {
+namespace {
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+__global__ __launch_bounds__(256) void bias_key_ranges_kernel(const BiasRangeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int seq = blockIdx.y;
+  const int hb = blockIdx.z;
+  const int r = blockIdx.x * 4 + wave;  // local row of the sequence
+  const int cq0 = a.cu_q[seq];
+  const int lq = a.cu_q[seq + 1] - cq0;
+  if (r >= lq) return;
+  const int lk = min(a.cu_kv[seq + 1] - a.cu_kv[seq], a.bias_cols);
+  const float* row = a.bias + (int64_t)(cq0 + r) * a.b_st + (int64_t)hb * a.b_sh;
+  int lo = 0x7fffffff, hi = 0;
+  // full 16-byte chunks: 64 lanes x 4 keys per pass, four passes in flight
+  const int full = lk & ~3;
+  for (int j0 = 4 * lane; j0 < full; j0 += 4 * 64 * 4) {
+    f32x4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * 256;
+      v[u] = j < full ? *reinterpret_cast<const f32x4_t*>(row + j)
+                      : (f32x4_t){-__builtin_inff(), -__builtin_inff(), -__builtin_inff(),
+                                  -__builtin_inff()};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (v[u][e] != -__builtin_inff()) {
+          const int j = j0 + u * 256 + e;
+          lo = min(lo, j);
+          hi = max(hi, j + 1);
+        }
+  }
+  // the last lk % 4 keys
+  if (lane < lk - full && row[full + lane] != -__builtin_inff()) {
+    lo = min(lo, full + lane);
+    hi = max(hi, full + lane + 1);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, __shfl_xor(lo, o));
+    hi = max(hi, __shfl_xor(hi, o));
+  }
+  if (lane == 0) {
+    int32_t* out = a.ranges + ((int64_t)hb * a.total_q + cq0 + r) * 2;
+    out[0] = hi > 0 ? lo : 0;
+    out[1] = hi;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bias_key_ranges(const BiasRangeArgs& a, int max_seqlen_q, int num_seqs,
+                                  int bias_heads, hipStream_t stream) {
+  (void)hipGetLastError();
+  const dim3 grid((unsigned)((max_seqlen_q + 3) / 4), (unsigned)num_seqs, (unsigned)bias_heads);
+  hipLaunchKernelGGL(bias_key_ranges_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mi_attn

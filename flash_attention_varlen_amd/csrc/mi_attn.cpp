@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -16,6 +17,7 @@
 #include <vector>
 
 #include "attn_fwd.h"
+#include "bias_ranges.h"
 
 namespace {
 
@@ -40,6 +42,19 @@ bool dims_supported(int32_t dt, int32_t dqk, int32_t dv) {
   if (dqk == 128 && dv == 128) return true;
   if (dqk == 192 && dv == 128) return dt != MI_ATTN_F32;
   return false;
+}
+
+// The params of a 1.0 caller end before bias_ranges; later fields read as 0.
+constexpr size_t kParamsSizeV1 = offsetof(mi_attn_fwd_params, bias_ranges);
+
+int copy_params(const mi_attn_fwd_params* p, mi_attn_fwd_params* out) {
+  if (p == nullptr) return fail(MI_ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (p->struct_size < kParamsSizeV1)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "struct_size %zu < %zu (not an mi_attn_fwd_params)",
+                p->struct_size, kParamsSizeV1);
+  std::memset(out, 0, sizeof(*out));
+  std::memcpy(out, p, p->struct_size < sizeof(*out) ? p->struct_size : sizeof(*out));
+  return MI_ATTN_OK;
 }
 
 bool env_flag(const char* name) {
@@ -111,12 +126,12 @@ int mi_attn_tile_shape(int32_t in_dtype, int32_t d_qk, int32_t d_v, int32_t* bm,
   return MI_ATTN_OK;
 }
 
-int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
+int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
   g_last_error.clear();
-  if (p == nullptr) return fail(MI_ATTN_ERR_INVALID_ARG, "params is NULL");
-  if (p->struct_size < sizeof(mi_attn_fwd_params))
-    return fail(MI_ATTN_ERR_INVALID_ARG, "struct_size %zu < %zu (library built for a newer ABI)",
-                p->struct_size, sizeof(mi_attn_fwd_params));
+  mi_attn_fwd_params local;
+  const int rc_copy = copy_params(p_in, &local);
+  if (rc_copy != MI_ATTN_OK) return rc_copy;
+  const mi_attn_fwd_params* p = &local;
   const int32_t dt = p->in_dtype;
   if (dt != MI_ATTN_F32 && dt != MI_ATTN_F16 && dt != MI_ATTN_BF16)
     return fail(MI_ATTN_ERR_UNSUPPORTED, "unknown in_dtype %d", dt);
@@ -196,6 +211,8 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
       return fail(MI_ATTN_ERR_INVALID_ARG,
                   "bias must be 16-byte aligned with strides that are multiples of 4");
     if (p->bias_cols <= 0) return fail(MI_ATTN_ERR_INVALID_ARG, "bias_cols must be > 0");
+    if (p->bias_ranges != nullptr && (reinterpret_cast<uintptr_t>(p->bias_ranges) & 7u) != 0)
+      return fail(MI_ATTN_ERR_INVALID_ARG, "bias_ranges must be 8-byte aligned");
   }
 
   int32_t bm = 0, bn = 0;
@@ -223,6 +240,7 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
   a.cu_q = p->cu_seqlens_q;
   a.cu_kv = p->cu_seqlens_kv;
   a.bias = p->bias;
+  a.bias_ranges = has_bias ? p->bias_ranges : nullptr;
   a.tile_counts = p->tile_counts;
   a.q_st = p->q_stride_tok;
   a.q_sh = p->q_stride_head;
@@ -270,6 +288,49 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream) {
                                   : dim3((unsigned)grid_x, (unsigned)n_qtiles);
   hipError_t e = mi_attn::launch_attn_fwd(a, dt, p->out_dtype, p->d_qk, p->d_v, has_bias, grid,
                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return MI_ATTN_OK;
+}
+
+int mi_attn_bias_key_ranges(const mi_attn_fwd_params* p_in, int32_t* ranges, void* stream) {
+  g_last_error.clear();
+  mi_attn_fwd_params local;
+  const int rc_copy = copy_params(p_in, &local);
+  if (rc_copy != MI_ATTN_OK) return rc_copy;
+  const mi_attn_fwd_params* p = &local;
+  if (p->bias == nullptr || ranges == nullptr || p->cu_seqlens_q == nullptr ||
+      p->cu_seqlens_kv == nullptr)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "bias, ranges and both cu_seqlens are required");
+  if (p->hq <= 0 || (p->bias_heads != 1 && p->bias_heads != p->hq))
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "bias_heads must be 1 or hq (got %d, hq %d)",
+                p->bias_heads, p->hq);
+  if (!aligned16(p->bias) || p->bias_stride_tok < 0 || p->bias_stride_head < 0 ||
+      p->bias_stride_tok % 4 != 0 || p->bias_stride_head % 4 != 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG,
+                "bias must be 16-byte aligned with strides that are multiples of 4");
+  if ((reinterpret_cast<uintptr_t>(ranges) & 7u) != 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "ranges must be 8-byte aligned");
+  if (p->bias_cols <= 0) return fail(MI_ATTN_ERR_INVALID_ARG, "bias_cols must be > 0");
+  if (p->num_seqs < 0 || p->max_seqlen_q < 0 || p->total_q < 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "negative size");
+  if (p->num_seqs == 0 || p->max_seqlen_q == 0 || p->total_q == 0) return MI_ATTN_OK;
+  if (p->num_seqs > 65535 || (p->max_seqlen_q + 3) / 4 > INT32_MAX || p->total_q > INT32_MAX)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "too many sequences (at most 65535) or rows");
+  if (env_flag("MI_ATTN_VALIDATE")) {
+    int rc = validate_cu(p->cu_seqlens_q, p->num_seqs, p->total_q, p->max_seqlen_q, "cu_seqlens_q");
+    if (rc != MI_ATTN_OK) return rc;
+  }
+  mi_attn::BiasRangeArgs a{};
+  a.bias = p->bias;
+  a.cu_q = p->cu_seqlens_q;
+  a.cu_kv = p->cu_seqlens_kv;
+  a.ranges = ranges;
+  a.b_st = p->bias_stride_tok;
+  a.b_sh = p->bias_stride_head;
+  a.total_q = p->total_q;
+  a.bias_cols = (int32_t)(p->bias_cols < INT32_MAX ? p->bias_cols : INT32_MAX);
+  hipError_t e = mi_attn::launch_bias_key_ranges(a, (int)p->max_seqlen_q, (int)p->num_seqs,
+                                                  p->bias_heads, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return MI_ATTN_OK;
 }

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_VERSION 100 /* 1.0.0 */
+#define MI_ATTN_VERSION 110 /* 1.1.0 */
 
 /* Return codes.  On any error nothing is launched and out / lse are untouched. */
 enum {
@@ -126,6 +126,13 @@ typedef struct mi_attn_fwd_params {
   float scale;       /* softmax scale, e.g. 1/sqrt(d_qk) */
   int32_t causal;    /* 0 or 1 */
   int32_t window;    /* 0 = none, else W >= 1 (requires causal) */
+  /* Added in version 1.1 (callers built against 1.0 pass a smaller
+   * struct_size and get NULL here):
+   * optional int32 [bias_heads, total_q, 2] key ranges of the bias rows, as
+   * mi_attn_bias_key_ranges writes them for this bias.  With them the kernels
+   * skip, exactly, the key tiles in which every bias value of a workgroup's
+   * (or a wave's) rows is -inf.  NULL: no skipping.  Ignored without a bias. */
+  const int32_t* bias_ranges;
 } mi_attn_fwd_params;
 
 /*
@@ -137,6 +144,25 @@ typedef struct mi_attn_fwd_params {
  * reduction order, no atomics).
  */
 int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream);
+
+/*
+ * Key ranges of the bias rows: for every bias head hb and query row t (global)
+ * of sequence s, ranges[(hb * total_q + t) * 2 + 0 .. 1] = [lo, hi), the
+ * first and one-past-last key j < min(Lk(s), bias_cols) whose bias value
+ * p->bias[t][hb][j] is not -inf ([0, 0) when there is none).  Reads the
+ * bias, cu_seqlens, sizes and strides of *p (the same struct a forward call
+ * takes; q/k/v/out are not used) and writes ranges, an int32 device buffer
+ * of 2 * bias_heads * total_q elements, 8-byte aligned, owned by the caller.
+ * Keys with a -inf bias contribute nothing to the softmax, so skipping the
+ * tiles outside these ranges is exact (mtlattn 0.3.0 project page, section
+ * "Use", for the bias; triton-msl part-2 post, section "FlashAttention:
+ * faster than PyTorch, competitive with MLX", for skipping masked tiles).
+ * The ranges stay valid for as long as the bias and cu_seqlens do: compute
+ * them once per bias, pass them in mi_attn_fwd_params.bias_ranges.
+ * Asynchronous on `stream`; one read of the bias.  Returns MI_ATTN_OK or a
+ * negative code (nothing launched).
+ */
+int mi_attn_bias_key_ranges(const mi_attn_fwd_params* p, int32_t* ranges, void* stream);
 
 /* Reason for the last non-OK return on the calling thread ("" if none). */
 const char* mi_attn_last_error(void);

@@ -1,0 +1,36 @@
+"""fp64 / integer CPU oracle for the mask front-ends.
+
+TEST INFRASTRUCTURE ONLY (like the rest of ``oracle/``): only the tests, the
+smoke check and the benchmark's ``cpu_baseline`` leg may import it.  It
+shares no code with the HIP path.
+
+* ``bias_key_ranges``: for each bias row, the first and one-past-last key of
+  its sequence whose additive bias is not -inf.  A key with a -inf bias has
+  logit -inf and contributes exactly nothing to the softmax (mtlattn 0.3.0
+  project page, section "Use": the bias composes with the masks), so the
+  kernels may skip every key outside these ranges; the triton-msl part-2
+  post (section "FlashAttention: faster than PyTorch, competitive with MLX")
+  makes the same point for tiles that are masked in full.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def bias_key_ranges(bias, cu_q, cu_kv):
+    """int64 ``[H_b, Tq, 2]``: ``[lo, hi)`` with lo the first and hi - 1 the
+    last key ``j < min(Lk, cols)`` of the row's sequence whose bias is not
+    -inf; ``[0, 0)`` when every such key is -inf."""
+    bias = np.asarray(bias)
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_kv = np.asarray(cu_kv, dtype=np.int64)
+    tq, hb, cols = bias.shape
+    out = np.zeros((hb, tq, 2), dtype=np.int64)
+    for s in range(len(cu_q) - 1):
+        lk = min(int(cu_kv[s + 1] - cu_kv[s]), cols)
+        for t in range(int(cu_q[s]), int(cu_q[s + 1])):
+            for h in range(hb):
+                keys = np.nonzero(bias[t, h, :lk] != -np.inf)[0]
+                if keys.size:
+                    out[h, t] = (keys[0], keys[-1] + 1)
+    return out

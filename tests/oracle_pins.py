@@ -317,7 +317,57 @@ def pin_row_subset_matches_full():
         _close(l, lse[1, cu_q[s] + rows], 0.0)
 
 
+def pin_bias_ranges_prefix_lm_closed_form():
+    """Prefix-LM bias (0 where j < P or j <= i, else -inf; self-attention):
+    row i's range is [0, min(L, max(P, i + 1))), by hand."""
+    lens, prefix, cols = [7, 1, 12, 3], 4, 14
+    rows = []
+    for n in lens:
+        i = np.arange(n)[:, None]
+        j = np.arange(cols)[None, :]
+        rows.append(np.where((j < prefix) | (j <= i), 0.0, -np.inf))
+    bias = np.concatenate(rows)[:, None, :]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    got = oracle.bias_key_ranges(bias, cu, cu)
+    for s, n in enumerate(lens):
+        for i in range(n):
+            assert tuple(got[0, cu[s] + i]) == (0, min(n, max(prefix, i + 1))), (s, i)
+
+
+def pin_bias_ranges_skip_is_exact():
+    """Attention with every key outside a row's range deleted from its
+    sequence equals attention over all keys (the skip is exact); keys at the
+    range ends are finite; empty ranges are exactly the all -inf rows."""
+    rng = np.random.default_rng(12)
+    q, k, v, cu_q, cu_kv, bias = _tiny_case(rng, 3, 40, 2, 1, 8, 4, cross=True, bias_heads=2,
+                                            neg_inf=0.6)
+    bias[3] = -np.inf  # a row that sees nothing
+    rg = oracle.bias_key_ranges(bias, cu_q, cu_kv)
+    out, lse = oracle.varlen_attention(q, k, v, cu_q, cu_kv, None, False, 0, bias)
+    for s in range(len(cu_q) - 1):
+        lk = int(cu_kv[s + 1] - cu_kv[s])
+        for t in range(int(cu_q[s]), int(cu_q[s + 1])):
+            for h in range(bias.shape[1]):
+                lo, hi = rg[h, t]
+                row = bias[t, h, :lk]
+                if hi == 0:
+                    assert np.all(row == -np.inf) and lo == 0
+                    continue
+                assert row[lo] != -np.inf and row[hi - 1] != -np.inf
+                assert np.all(row[:lo] == -np.inf) and np.all(row[hi:] == -np.inf)
+                # the row restricted to [lo, hi)
+                sub_k = k[cu_kv[s] + lo:cu_kv[s] + hi]
+                sub_v = v[cu_kv[s] + lo:cu_kv[s] + hi]
+                sub_b = bias[t:t + 1, :, lo:hi]
+                o, l = oracle.attention_rows(q[t:t + 1], sub_k, sub_v, np.array([0, 1]),
+                                             np.array([0, hi - lo]), 0, h, [0], None, False, 0,
+                                             sub_b)
+                _close(o[0], out[t, h], 1e-13)
+                _close(l[0], lse[h, t], 1e-13)
+
+
 ALL_PINS = [pin_brute_force_tiny, pin_sdpa_special_case, pin_rows_sum_to_one,
             pin_one_key_sequence, pin_zero_queries_mean, pin_key_permutation_invariance,
             pin_neg_inf_key_is_removed, pin_mask_counts_closed_form, pin_golden_hand_worked,
-            pin_row_subset_matches_full]
+            pin_row_subset_matches_full, pin_bias_ranges_prefix_lm_closed_form,
+            pin_bias_ranges_skip_is_exact]

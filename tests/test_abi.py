@@ -23,8 +23,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["mi_attn_last_error", "mi_attn_tile_shape", "mi_attn_varlen_fwd",
-                     "mi_attn_version"]
+    assert names == ["mi_attn_bias_key_ranges", "mi_attn_last_error", "mi_attn_tile_shape",
+                     "mi_attn_varlen_fwd", "mi_attn_version"]
     lib = fav.load_library()
     for n in names:
         assert hasattr(lib, n), n
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_tile_shape():
-    assert fav.mi_attn_version() == 100
+    assert fav.mi_attn_version() == 110
     for dt in (fav.BF16, fav.F16):
         for dqk, dv in ((64, 64), (128, 128), (192, 128)):
             bm, bn = fav.mi_attn_tile_shape(dt, dqk, dv)
@@ -131,6 +131,40 @@ def test_short_struct_is_refused():
     lib = fav.load_library()
     p.struct_size = 8
     assert lib.mi_attn_varlen_fwd(ctypes.byref(p), None) == fav.ERR_INVALID_ARG
+
+
+def test_version_1_0_struct_is_accepted():
+    """A caller built against 1.0 passes the struct without bias_ranges: the
+    library reads the fields it has and takes bias_ranges as NULL (the call
+    below is a refusal found after the copy: an unsupported head size)."""
+    p = _valid_params()
+    lib = fav.load_library()
+    p.struct_size = fav.MiAttnFwdParams.bias_ranges.offset
+    p.bias_ranges = 1 << 20  # beyond the 1.0 struct: must not be read
+    p.d_qk = p.d_v = 96
+    assert lib.mi_attn_varlen_fwd(ctypes.byref(p), None) == fav.ERR_UNSUPPORTED
+    assert "head dims" in fav.mi_attn_last_error()
+
+
+RANGE_REFUSALS = {
+    "no_bias": (dict(bias=None), fav.ERR_INVALID_ARG),
+    "bias_heads": (dict(bias_heads=3), fav.ERR_UNSUPPORTED),
+    "odd_bias_stride": (dict(bias_stride_tok=66), fav.ERR_INVALID_ARG),
+    "zero_cols": (dict(bias_cols=0), fav.ERR_INVALID_ARG),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RANGE_REFUSALS))
+def test_bias_key_ranges_refuses(name):
+    changes, code = RANGE_REFUSALS[name]
+    p = _valid_params()
+    p.bias, p.bias_heads, p.bias_cols = 1 << 20, 1, 64
+    p.bias_stride_tok, p.bias_stride_head = 64, 64
+    for k, v in changes.items():
+        setattr(p, k, v)
+    with pytest.raises(fav.MiAttnError) as ei:
+        fav.mi_attn_bias_key_ranges(p, 1 << 21, 0)
+    assert ei.value.code == code, fav.mi_attn_last_error()
 
 
 def test_empty_problem_is_a_no_op():

@@ -12,7 +12,7 @@ import types
 import pytest
 
 import oracle
-from oracle import ref_attention
+from oracle import ref_attention, ref_masks
 from oracle_pins import ALL_PINS
 
 MUTATIONS = {
@@ -35,17 +35,38 @@ MUTATIONS = {
     "key_range_upper_open": ("ok = (j >= 0) & (j < lk)", "ok = (j >= 0) & (j < lk - 1)"),
 }
 
-SOURCE = inspect.getsource(ref_attention)
+# mutations of the mask front-end oracle (oracle/ref_masks.py)
+MASK_MUTATIONS = {
+    "ranges_hi_closed": ("out[h, t] = (keys[0], keys[-1] + 1)", "out[h, t] = (keys[0], keys[-1])"),
+    "ranges_ignore_key_length": ("lk = min(int(cu_kv[s + 1] - cu_kv[s]), cols)", "lk = cols"),
+    "ranges_lo_zero": ("out[h, t] = (keys[0], keys[-1] + 1)", "out[h, t] = (0, keys[-1] + 1)"),
+    "ranges_finite_test": ("keys = np.nonzero(bias[t, h, :lk] != -np.inf)[0]",
+                           "keys = np.nonzero(bias[t, h, :lk] > 0)[0]"),
+}
+
+SOURCES = {"attention": inspect.getsource(ref_attention), "masks": inspect.getsource(ref_masks)}
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
-def test_pins_catch_mutation(name, monkeypatch):
-    old, new = MUTATIONS[name]
-    assert SOURCE.count(old) >= 1, f"mutation anchor not found: {old!r}"
+def _mutant(module_key, old, new):
+    src = SOURCES[module_key]
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
     mutated = types.ModuleType("oracle_mutant")
-    exec(compile(SOURCE.replace(old, new), "oracle_mutant", "exec"), mutated.__dict__)
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mutated.__dict__)
+    return mutated
+
+
+ALL_MUTATIONS = {**{("attention", k): v for k, v in MUTATIONS.items()},
+                 **{("masks", k): v for k, v in MASK_MUTATIONS.items()}}
+
+
+@pytest.mark.parametrize("key", sorted(ALL_MUTATIONS), ids=lambda k: f"{k[0]}-{k[1]}")
+def test_pins_catch_mutation(key, monkeypatch):
+    module_key, name = key
+    old, new = ALL_MUTATIONS[key]
+    mutated = _mutant(module_key, old, new)
     for attr in oracle.__all__:
-        monkeypatch.setattr(oracle, attr, getattr(mutated, attr))
+        if hasattr(mutated, attr):
+            monkeypatch.setattr(oracle, attr, getattr(mutated, attr))
     caught = []
     for pin in ALL_PINS:
         try:
