@@ -8,7 +8,9 @@ routine on its special cases, closed forms and invariants; none is
 """
 from .ref_attention import (attention_rows, bias_head, finish_rows, kv_head_of, logits,
                             softmax_rows, varlen_attention, visible, visible_counts)
+from .ref_backward import varlen_attention_backward
 from .ref_masks import bias_key_ranges
 
 __all__ = ["attention_rows", "bias_head", "bias_key_ranges", "finish_rows", "kv_head_of", "logits",
-           "softmax_rows", "varlen_attention", "visible", "visible_counts"]
+           "softmax_rows", "varlen_attention", "varlen_attention_backward", "visible",
+           "visible_counts"]

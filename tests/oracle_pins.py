@@ -366,8 +366,109 @@ def pin_bias_ranges_skip_is_exact():
                 _close(l[0], lse[h, t], 1e-13)
 
 
+# ---------------------------------------------------------------- backward pins
+def _loss_and_grads(q, k, v, cu_q, cu_kv, scale, causal, window, bias, G):
+    out, _ = oracle.varlen_attention(q, k, v, cu_q, cu_kv, scale, causal, window, bias)
+    return float((out * G).sum()), oracle.varlen_attention_backward(q, k, v, G, cu_q, cu_kv, scale,
+                                                                     causal, window, bias)
+
+
+def pin_backward_finite_differences():
+    """Central differences of L = sum(out * G) in fp64 against dq, dk, dv, over
+    causal / full / window, cross-attention lengths, GQA and a bias with -inf
+    entries (every element of q, k, v perturbed)."""
+    rng = np.random.default_rng(20)
+    cases = [(False, 0, 0), (True, 0, 0), (True, 3, 0), (True, 0, 4), (False, 0, 1)]
+    for causal, window, bias_heads in cases:
+        q, k, v, cu_q, cu_kv, bias = _tiny_case(rng, 2, 5, 4, 2, 3, 2, cross=True,
+                                                bias_heads=bias_heads, neg_inf=0.2)
+        G = rng.standard_normal((q.shape[0], q.shape[1], v.shape[2]))
+        _, (dq, dk, dv) = _loss_and_grads(q, k, v, cu_q, cu_kv, 0.7, causal, window, bias, G)
+        h = 1e-6
+        for x, dx in ((q, dq), (k, dk), (v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + h
+                lp, _ = _loss_and_grads(q, k, v, cu_q, cu_kv, 0.7, causal, window, bias, G)
+                x[idx] = old - h
+                lm, _ = _loss_and_grads(q, k, v, cu_q, cu_kv, 0.7, causal, window, bias, G)
+                x[idx] = old
+                num[idx] = (lp - lm) / (2 * h)
+            _close(dx, num, 1e-6)
+
+
+def pin_backward_sdpa_special_case():
+    """Self-attention (Lq = Lk), causal or full, GQA, additive mask: float64
+    torch.autograd through scaled_dot_product_attention gives the same dq,
+    dk, dv."""
+    rng = np.random.default_rng(21)
+    for causal in (False, True):
+        for hq, hkv in ((2, 2), (4, 2)):
+            L, d, dv_ = 9, 5, 3
+            q = rng.standard_normal((L, hq, d))
+            k = rng.standard_normal((L, hkv, d))
+            v = rng.standard_normal((L, hkv, dv_))
+            bias = rng.standard_normal((L, hq, L))
+            bias[rng.random(bias.shape) < 0.2] = -np.inf
+            bias[:, :, 0] = 0.0  # every row keeps a visible key
+            G = rng.standard_normal((L, hq, dv_))
+            cu = np.array([0, L])
+            dq, dk, dv = oracle.varlen_attention_backward(q, k, v, G, cu, cu, 0.6, causal, 0, bias)
+            tq, tk, tv = (torch.tensor(x.transpose(1, 0, 2)[None], requires_grad=True)
+                          for x in (q, k, v))
+            rep = hq // hkv
+            kk = tk.repeat_interleave(rep, dim=1)
+            vv = tv.repeat_interleave(rep, dim=1)
+            mask = torch.tensor(bias.transpose(1, 0, 2)[None])
+            if causal:
+                mask = mask.masked_fill(torch.ones(L, L, dtype=torch.bool).triu(1), float("-inf"))
+            o = torch.nn.functional.scaled_dot_product_attention(tq, kk, vv, attn_mask=mask,
+                                                                 scale=0.6)
+            (o * torch.tensor(G.transpose(1, 0, 2)[None])).sum().backward()
+            _close(dq, tq.grad[0].numpy().transpose(1, 0, 2), 1e-12)
+            _close(dk, tk.grad[0].numpy().transpose(1, 0, 2), 1e-12)
+            _close(dv, tv.grad[0].numpy().transpose(1, 0, 2), 1e-12)
+
+
+def pin_backward_closed_forms():
+    """V equal for all keys: out does not depend on q or k, so dq = dk = 0 and
+    dv_j = sum_i p_ij dout_i; a one-key sequence gives dv = sum of its rows'
+    dout and dq = dk = 0; dout = 0 gives zero gradients; shifting every key
+    by one vector leaves out unchanged, so dk sums to zero over a sequence."""
+    rng = np.random.default_rng(22)
+    q, k, v, cu_q, cu_kv, _ = _tiny_case(rng, 2, 6, 2, 1, 4, 3, cross=True)
+    v[:] = rng.standard_normal(3)
+    G = rng.standard_normal((q.shape[0], 2, 3))
+    dq, dk, dv = oracle.varlen_attention_backward(q, k, v, G, cu_q, cu_kv, None, True, 0, None)
+    _close(dq, np.zeros_like(dq), 1e-12)
+    _close(dk, np.zeros_like(dk), 1e-12)
+    # one key per sequence
+    cu_k1 = np.arange(len(cu_q))
+    k1 = rng.standard_normal((len(cu_q) - 1, 1, 4))
+    v1 = rng.standard_normal((len(cu_q) - 1, 1, 3))
+    dq, dk, dv = oracle.varlen_attention_backward(q, k1, v1, G, cu_q, cu_k1, None, False, 0, None)
+    _close(dq, np.zeros_like(dq), 1e-12)
+    _close(dk, np.zeros_like(dk), 1e-12)
+    for s in range(len(cu_q) - 1):
+        _close(dv[s, 0], G[cu_q[s]:cu_q[s + 1]].sum(axis=(0, 1)), 1e-12)
+    # dout = 0
+    q, k, v, cu_q, cu_kv, bias = _tiny_case(rng, 3, 7, 4, 2, 4, 3, cross=True, bias_heads=1,
+                                            neg_inf=0.2)
+    z = oracle.varlen_attention_backward(q, k, v, np.zeros((q.shape[0], 4, 3)), cu_q, cu_kv,
+                                         None, True, 3, bias)
+    for g in z:
+        assert not np.any(g)
+    # translation of the keys
+    G = rng.standard_normal((q.shape[0], 4, 3))
+    _, dk, _ = oracle.varlen_attention_backward(q, k, v, G, cu_q, cu_kv, None, True, 0, bias)
+    for s in range(len(cu_kv) - 1):
+        _close(dk[cu_kv[s]:cu_kv[s + 1]].sum(axis=0), np.zeros(dk.shape[1:]), 1e-12)
+
+
 ALL_PINS = [pin_brute_force_tiny, pin_sdpa_special_case, pin_rows_sum_to_one,
             pin_one_key_sequence, pin_zero_queries_mean, pin_key_permutation_invariance,
             pin_neg_inf_key_is_removed, pin_mask_counts_closed_form, pin_golden_hand_worked,
             pin_row_subset_matches_full, pin_bias_ranges_prefix_lm_closed_form,
-            pin_bias_ranges_skip_is_exact]
+            pin_bias_ranges_skip_is_exact, pin_backward_finite_differences,
+            pin_backward_sdpa_special_case, pin_backward_closed_forms]

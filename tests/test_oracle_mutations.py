@@ -12,7 +12,7 @@ import types
 import pytest
 
 import oracle
-from oracle import ref_attention, ref_masks
+from oracle import ref_attention, ref_backward, ref_masks
 from oracle_pins import ALL_PINS
 
 MUTATIONS = {
@@ -44,19 +44,37 @@ MASK_MUTATIONS = {
                            "keys = np.nonzero(bias[t, h, :lk] > 0)[0]"),
 }
 
-SOURCES = {"attention": inspect.getsource(ref_attention), "masks": inspect.getsource(ref_masks)}
+# mutations of the backward oracle (oracle/ref_backward.py)
+BACKWARD_MUTATIONS = {
+    "bwd_no_delta": ("dz = p * (dp - delta[:, None])", "dz = p * dp"),
+    "bwd_delta_unweighted": ("delta = (p * dp).sum(axis=1)", "delta = dp.sum(axis=1)"),
+    "bwd_dq_no_scale": ("dq[cq0:cq1, h] += scale * (dz @ ks)", "dq[cq0:cq1, h] += dz @ ks"),
+    "bwd_dk_untransposed": ("dk[ck0:ck1, g] += scale * (dz.T @ qs)",
+                            "dk[ck0:ck1, g] += scale * (dz.T @ qs[::-1])"),
+    "bwd_dv_unnormalised": ("p = np.where(nonempty[:, None], p / np.where(nonempty, l, 1.0)[:, None], 0.0)",
+                            "p = np.where(nonempty[:, None], p, 0.0)"),
+    "bwd_dv_from_dz": ("dv[ck0:ck1, g] += p.T @ do", "dv[ck0:ck1, g] += dz.T @ do"),
+    "bwd_dk_overwrite_gqa": ("dk[ck0:ck1, g] += scale * (dz.T @ qs)",
+                             "dk[ck0:ck1, g] = scale * (dz.T @ qs)"),
+    "bwd_mask_dropped": ("p, m, l = softmax_rows(z, mask)", "p, m, l = softmax_rows(z, mask | True)"),
+}
+
+SOURCES = {"attention": inspect.getsource(ref_attention), "masks": inspect.getsource(ref_masks),
+           "backward": inspect.getsource(ref_backward)}
 
 
 def _mutant(module_key, old, new):
     src = SOURCES[module_key]
     assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
-    mutated = types.ModuleType("oracle_mutant")
+    mutated = types.ModuleType("oracle.oracle_mutant")
+    mutated.__package__ = "oracle"  # relative imports resolve inside the oracle package
     exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mutated.__dict__)
     return mutated
 
 
 ALL_MUTATIONS = {**{("attention", k): v for k, v in MUTATIONS.items()},
-                 **{("masks", k): v for k, v in MASK_MUTATIONS.items()}}
+                 **{("masks", k): v for k, v in MASK_MUTATIONS.items()},
+                 **{("backward", k): v for k, v in BACKWARD_MUTATIONS.items()}}
 
 
 @pytest.mark.parametrize("key", sorted(ALL_MUTATIONS), ids=lambda k: f"{k[0]}-{k[1]}")
