@@ -193,6 +193,9 @@ def main():
                     help="after the timed region, time this many launches each preceded by a "
                          "write of --flush-mib MiB (evicts L2 and the MALL); reported under 'cold'")
     ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (delta, dk/dv, dq kernels) instead of the forward; "
+                         "useful FLOPs are 2.5x the forward's (five products of the same size)")
     ap.add_argument("--no-bias-ranges", action="store_true",
                     help="with a bias, do not compute the bias key ranges (visit every tile)")
     ap.add_argument("--window", type=int, default=None,
@@ -258,7 +261,25 @@ def main():
     # read of the bias), then the forward skips the -inf tiles outside them.
     use_ranges = bias is not None and not args.no_bias_ranges
 
+    if args.backward:
+        if bias is not None or w.dtype == "f32" or w.d_qk != w.d_v or w.d_qk not in (64, 128):
+            print("the backward takes bf16/fp16, head dims 64 or 128, no bias", file=sys.stderr)
+            sys.exit(2)
+        out_f, lse_f = fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, scale=w.softmax_scale,
+                                            causal=w.causal, window=w.window, return_lse=True)
+        g_do = torch.Generator().manual_seed(w.seed + 1000)
+        dout = torch.randn(w.total_q, w.hq, w.d_v, generator=g_do).to(q.dtype).to(dev)
+        dq_b, dk_b, dv_b = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        torch.cuda.synchronize()
+
     def step(mid_event=None):
+        if args.backward:
+            if mid_event is not None:
+                mid_event.record(stream)
+            fav.varlen_attention_backward(q, k, v, out_f, lse_f, dout, cq, ck, w.max_seqlen_q,
+                                          w.max_seqlen_kv, scale=w.softmax_scale, causal=w.causal,
+                                          window=w.window, dq=dq_b, dk=dk_b, dv=dv_b, stream=stream)
+            return
         rg = None
         if use_ranges:
             rg = fav.bias_key_ranges(bias, cq, ck, w.max_seqlen_q, stream=stream)
@@ -309,13 +330,13 @@ def main():
     ms_per_step = total_ms / args.steps
     kernel_ms = sum(per) / len(per)
 
-    flops = useful_flops(w, inp.bias)
+    flops = useful_flops(w, inp.bias) * (2.5 if args.backward else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     out_bytes = out.element_size()
     # stored counter readings belong to the workload as defined (not to an overridden window)
-    traffic = stored_traffic(args.workload) if args.window is None else None
+    traffic = stored_traffic(args.workload) if args.window is None and not args.backward else None
 
     cold = None
     if args.cold_steps > 0:
@@ -350,7 +371,8 @@ def main():
               file=sys.stderr, flush=True)
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if not args.backward else
+        "attn bwd useful TFLOP/s (2.5x the forward's useful FLOPs) + % of MI355X bf16 MFMA peak",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -385,13 +407,17 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "algorithmic_bytes": algorithmic_bytes(w, out_bytes),
-            "kernel": "attn_fwd_kernel" if w.dtype == "f32" else "attn_fwd16p_kernel",
+            "kernel": ("delta_kernel + dkdv_kernel + dq_kernel" if args.backward else
+                       "attn_fwd_kernel" if w.dtype == "f32" else "attn_fwd16p_kernel"),
             "kernel_ms": round(kernel_ms, 4),
         },
         "cpu_baseline": cpu,
     }
     if cold is not None:
         result["cold"] = cold
+    if args.backward:
+        result["config"]["pass"] = "backward"
+        result["cpu_baseline"] = None  # the oracle baseline is timed for the forward only
     print(f"# GPU: {ms_per_step:.4f} ms/step, {value:.1f} useful TFLOP/s "
           f"({100 * value / peak:.1f}% of {peak} TFLOP/s)", file=sys.stderr, flush=True)
 

@@ -20,8 +20,9 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["mi_attn_varlen_fwd", "mi_attn_last_error", "mi_attn_version", "mi_attn_tile_shape",
-           "mi_attn_bias_key_ranges", "bias_key_ranges", "varlen_attention", "MiAttnFwdParams", "MiAttnError", "load_library", "LIB_PATH",
+__all__ = ["mi_attn_varlen_fwd", "mi_attn_varlen_bwd", "mi_attn_last_error", "mi_attn_version",
+           "mi_attn_tile_shape", "mi_attn_bias_key_ranges", "bias_key_ranges", "varlen_attention",
+           "varlen_attention_backward", "MiAttnBwdParams", "MiAttnFwdParams", "MiAttnError", "load_library", "LIB_PATH",
            "F32", "F16", "BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi_attn.so")
@@ -61,6 +62,33 @@ class MiAttnFwdParams(ctypes.Structure):
     ]
 
 
+class MiAttnBwdParams(ctypes.Structure):
+    """Field-for-field mirror of ``mi_attn_bwd_params``."""
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("dout", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("delta", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_kv", ctypes.c_void_p),
+        ("num_seqs", ctypes.c_int64), ("max_seqlen_q", ctypes.c_int64),
+        ("max_seqlen_kv", ctypes.c_int64), ("total_q", ctypes.c_int64),
+        ("total_kv", ctypes.c_int64),
+        ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+        ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("q_stride_tok", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
+        ("k_stride_tok", ctypes.c_int64), ("k_stride_head", ctypes.c_int64),
+        ("v_stride_tok", ctypes.c_int64), ("v_stride_head", ctypes.c_int64),
+        ("out_stride_tok", ctypes.c_int64), ("out_stride_head", ctypes.c_int64),
+        ("dout_stride_tok", ctypes.c_int64), ("dout_stride_head", ctypes.c_int64),
+        ("dq_stride_tok", ctypes.c_int64), ("dq_stride_head", ctypes.c_int64),
+        ("dk_stride_tok", ctypes.c_int64), ("dk_stride_head", ctypes.c_int64),
+        ("dv_stride_tok", ctypes.c_int64), ("dv_stride_head", ctypes.c_int64),
+        ("in_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -85,6 +113,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mi_attn_bias_key_ranges.argtypes = [ctypes.POINTER(MiAttnFwdParams), ctypes.c_void_p,
                                             ctypes.c_void_p]
     lib.mi_attn_bias_key_ranges.restype = ctypes.c_int
+    lib.mi_attn_varlen_bwd.argtypes = [ctypes.POINTER(MiAttnBwdParams), ctypes.c_void_p]
+    lib.mi_attn_varlen_bwd.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -115,6 +145,14 @@ def mi_attn_varlen_fwd(params: MiAttnFwdParams, stream: int = 0) -> None:
         raise MiAttnError(rc, mi_attn_last_error())
 
 
+def mi_attn_varlen_bwd(params: MiAttnBwdParams, stream: int = 0) -> None:
+    """Call the C entry point; raise MiAttnError on a non-OK return."""
+    params.struct_size = ctypes.sizeof(MiAttnBwdParams)
+    rc = load_library().mi_attn_varlen_bwd(ctypes.byref(params), ctypes.c_void_p(stream))
+    if rc != OK:
+        raise MiAttnError(rc, mi_attn_last_error())
+
+
 def mi_attn_bias_key_ranges(params: MiAttnFwdParams, ranges_ptr: int, stream: int = 0) -> None:
     """Call the C entry point; raise MiAttnError on a non-OK return."""
     params.struct_size = ctypes.sizeof(MiAttnFwdParams)
@@ -136,14 +174,18 @@ def _dtype_code(t) -> int:
 def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
                      scale: Optional[float] = None, causal: bool = False, window: int = 0,
                      attn_bias=None, out_dtype=None, return_lse: bool = False, out=None,
-                     lse=None, tile_counts=None, stream=None, bias_ranges=None):
+                     lse=None, tile_counts=None, stream=None, bias_ranges=None,
+                     max_seqlen_kv=None):
     """Fused varlen attention forward.  Returns ``out`` or ``(out, lse)``.
 
     q ``[Tq, Hq, Dqk]``, k ``[Tk, Hkv, Dqk]``, v ``[Tk, Hkv, Dv]`` (device,
     last dim contiguous, any token / head strides the C ABI accepts);
     ``out`` is ``[Tq, Hq, Dv]`` in ``out_dtype`` (default: q's dtype;
     ``torch.float32`` is also accepted); ``lse`` is ``[Hq, Tq]`` fp32
-    (natural log).  Forward only: inputs that require grad are refused.
+    (natural log).  If q, k or v require grad (and grad mode is on), the call
+    is differentiable: ``out``'s gradient flows back through
+    ``mi_attn_varlen_bwd`` (bf16 / fp16, head dims 64 / 128, no bias;
+    ``max_seqlen_kv`` is read from ``cu_seqlens_kv`` when not given).
 
     ``stream`` (a ``torch.cuda.Stream``, a raw ``hipStream_t`` handle, or
     None for the current stream) is where the kernel runs; outputs and the
@@ -160,8 +202,6 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
             raise MiAttnError(ERR_INVALID_ARG, f"{name} must be a device tensor")
         if t.dim() != 3 or t.stride(-1) != 1:
             raise MiAttnError(ERR_INVALID_ARG, f"{name} must be [tokens, heads, dim], last dim contiguous")
-        if t.requires_grad:
-            raise MiAttnError(ERR_UNSUPPORTED, "forward-only library: inputs must not require grad")
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise MiAttnError(ERR_INVALID_ARG, "q, k and v must share one dtype")
     for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)):
@@ -177,6 +217,19 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
+    if torch.is_grad_enabled() and (q.requires_grad or k.requires_grad or v.requires_grad):
+        # differentiable path (mtlattn page, "Drop-in for scaled_dot_product_attention":
+        # inputs that require grad route through the backward kernel)
+        if attn_bias is not None or out_dtype != q.dtype or q.dtype == torch.float32 or \
+                out is not None or lse is not None or tile_counts is not None:
+            raise MiAttnError(ERR_UNSUPPORTED,
+                              "the differentiable path takes bf16/fp16 inputs, no bias, the default "
+                              "output dtype and no preallocated outputs")
+        s_obj = _stream_of(stream, q.device)
+        with torch.cuda.stream(s_obj):
+            o, l = _differentiable_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
+                                             max_seqlen_kv, scale, causal, window)
+        return (o, l) if return_lse else o
     s_obj = _stream_of(stream, q.device)
     if bias_ranges is not None:
         if attn_bias is None:
@@ -300,3 +353,101 @@ def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen
     p.window = int(window)
     mi_attn_varlen_fwd(p, int(s_obj.cuda_stream))
     return (out, lse) if return_lse else out
+
+
+# ---------------------------------------------------------------- backward
+def varlen_attention_backward(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_kv,
+                              max_seqlen_q: int, max_seqlen_kv: int, scale: Optional[float] = None,
+                              causal: bool = False, window: int = 0, dq=None, dk=None, dv=None,
+                              grad_dtype=None, stream=None):
+    """Gradients ``(dq, dk, dv)`` of the forward from its inputs, its output
+    ``out`` and ``lse`` and the output gradient ``dout`` (bf16 / fp16,
+    head dims 64 or 128, no bias).  Outputs (and the fp32 [Hq, Tq] delta
+    workspace) are allocated on ``stream`` unless given."""
+    import torch
+    tq, hq, dqk = q.shape
+    tk, hkv, _ = k.shape
+    dvd = v.shape[2]
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != (tq, hq, dvd) or t.dtype != q.dtype or t.stride(-1) != 1:
+            raise MiAttnError(ERR_INVALID_ARG, f"{name} must be [Tq, Hq, Dv] in q's dtype")
+    if lse.shape != (hq, tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise MiAttnError(ERR_INVALID_ARG, "lse must be a contiguous fp32 [Hq, Tq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    s_obj = _stream_of(stream, q.device)
+    with torch.cuda.stream(s_obj):
+        gdt = q.dtype if grad_dtype is None else grad_dtype
+        dq = torch.empty(q.shape, dtype=gdt, device=q.device) if dq is None else dq
+        dk = torch.empty(k.shape, dtype=gdt, device=q.device) if dk is None else dk
+        dv = torch.empty(v.shape, dtype=gdt, device=q.device) if dv is None else dv
+        for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+            if t.shape != ref.shape or t.dtype != gdt or t.stride(-1) != 1:
+                raise MiAttnError(ERR_INVALID_ARG, f"{name} has the wrong shape, dtype or layout")
+        delta = torch.empty(hq, tq, dtype=torch.float32, device=q.device)
+        p = MiAttnBwdParams()
+        p.q, p.k, p.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+        p.out, p.lse, p.dout = out.data_ptr(), lse.data_ptr(), dout.data_ptr()
+        p.dq, p.dk, p.dv, p.delta = dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr()
+        p.cu_seqlens_q, p.cu_seqlens_kv = cu_seqlens_q.data_ptr(), cu_seqlens_kv.data_ptr()
+        p.num_seqs = cu_seqlens_q.numel() - 1
+        p.max_seqlen_q, p.max_seqlen_kv = int(max_seqlen_q), int(max_seqlen_kv)
+        p.total_q, p.total_kv = tq, tk
+        p.hq, p.hkv, p.d_qk, p.d_v = hq, hkv, dqk, dvd
+        for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq),
+                        ("dk", dk), ("dv", dv)):
+            setattr(p, f"{name}_stride_tok", t.stride(0))
+            setattr(p, f"{name}_stride_head", t.stride(1))
+        p.in_dtype = _dtype_code(q.dtype)
+        p.grad_dtype = _dtype_code(gdt)
+        p.scale = float(scale)
+        p.causal = 1 if causal else 0
+        p.window = int(window)
+        mi_attn_varlen_bwd(p, int(s_obj.cuda_stream))
+    return dq, dk, dv
+
+
+def _autograd_fn():
+    import torch
+
+    class VarlenAttentionFn(torch.autograd.Function):
+        """Forward through mi_attn_varlen_fwd, backward through
+        mi_attn_varlen_bwd (the lse output is not differentiated)."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, scale,
+                    causal, window):
+            with torch.no_grad():
+                out, lse = varlen_attention(q.detach(), k.detach(), v.detach(), cu_seqlens_q,
+                                            cu_seqlens_kv, max_seqlen_q, scale=scale, causal=causal,
+                                            window=window, return_lse=True)
+            ctx.save_for_backward(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv)
+            ctx.args = (max_seqlen_q, max_seqlen_kv, scale, causal, window)
+            ctx.mark_non_differentiable(lse)
+            return out, lse
+
+        @staticmethod
+        def backward(ctx, dout, _dlse):
+            q, k, v, out, lse, cq, ck = ctx.saved_tensors
+            max_seqlen_q, max_seqlen_kv, scale, causal, window = ctx.args
+            dq, dk, dv = varlen_attention_backward(q, k, v, out, lse, dout.contiguous(), cq, ck,
+                                                   max_seqlen_q, max_seqlen_kv, scale, causal,
+                                                   window)
+            return dq, dk, dv, None, None, None, None, None, None, None
+
+    return VarlenAttentionFn
+
+
+_FN = None
+
+
+def _differentiable_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
+                              scale, causal, window):
+    global _FN
+    if _FN is None:
+        _FN = _autograd_fn()
+    if max_seqlen_kv is None:
+        max_seqlen_kv = int((cu_seqlens_kv[1:] - cu_seqlens_kv[:-1]).max().item()) \
+            if cu_seqlens_kv.numel() > 1 else 0
+    return _FN.apply(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, scale,
+                     causal, window)

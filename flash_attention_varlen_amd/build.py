@@ -26,7 +26,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wall", "-Wno-pass-failed", "-Wno-unused-function",
          "-Wno-cuda-compat", "-I", INCLUDE, "-I", CSRC]
 # Sources compiled once each.
-PLAIN = ["attn_fwd.hip", "bias_ranges.hip", "mi_attn.cpp"]
+PLAIN = ["attn_fwd.hip", "attn_bwd.hip", "bias_ranges.hip", "mi_attn.cpp"]
 
 
 def hipcc() -> str:
@@ -35,13 +35,22 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
+def _instance_list(header: str, macro: str, pattern: str):
+    text = open(os.path.join(CSRC, header)).read()
+    body = text[text.index(f"#define {macro}(X)"):]
+    body = body[:body.index("\n#define", 1)]
+    return re.findall(pattern, body)
+
+
 def instances():
     """(tag, type, dqk, dv) of every forward kernel instance, read from the
     MI_ATTN_FWD_INSTANCES list in attn_fwd.h."""
-    text = open(os.path.join(CSRC, "attn_fwd.h")).read()
-    body = text[text.index("#define MI_ATTN_FWD_INSTANCES(X)"):]
-    body = body[:body.index("\n#define", 1)]
-    return re.findall(r"X\((\w+), (\w+), (\d+), (\d+)\)", body)
+    return _instance_list("attn_fwd.h", "MI_ATTN_FWD_INSTANCES", r"X\((\w+), (\w+), (\d+), (\d+)\)")
+
+
+def bwd_instances():
+    """(tag, type, d) of every backward instance (MI_ATTN_BWD_INSTANCES in attn_bwd.h)."""
+    return _instance_list("attn_bwd.h", "MI_ATTN_BWD_INSTANCES", r"X\((\w+), (\w+), (\d+)\)")
 
 
 def compile_jobs(objdir: str):
@@ -56,6 +65,11 @@ def compile_jobs(objdir: str):
                       f"-DMI_ATTN_INST_T={t}", f"-DMI_ATTN_INST_DQK={dqk}",
                       f"-DMI_ATTN_INST_DV={dv}", "-c", "-x", "hip",
                       os.path.join(CSRC, "attn_fwd_inst.hip"), "-o", obj], obj))
+    for tag, t, d in bwd_instances():
+        obj = os.path.join(objdir, f"attn_bwd_inst_{tag}_{d}.o")
+        jobs.append(([hipcc(), f"--offload-arch={ARCH}", *FLAGS, f"-DMI_ATTN_INST_TAG={tag}",
+                      f"-DMI_ATTN_INST_T={t}", f"-DMI_ATTN_INST_D={d}", "-c", "-x", "hip",
+                      os.path.join(CSRC, "attn_bwd_inst.hip"), "-o", obj], obj))
     return jobs
 
 

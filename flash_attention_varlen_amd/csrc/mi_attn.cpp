@@ -16,6 +16,7 @@
 #include <string>
 #include <vector>
 
+#include "attn_bwd.h"
 #include "attn_fwd.h"
 #include "bias_ranges.h"
 
@@ -287,6 +288,103 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
                     : a.kv_rows   ? dim3((unsigned)kv_rows_wgs, 1u)
                                   : dim3((unsigned)grid_x, (unsigned)n_qtiles);
   hipError_t e = mi_attn::launch_attn_fwd(a, dt, p->out_dtype, p->d_qk, p->d_v, has_bias, grid,
+                                          reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return MI_ATTN_OK;
+}
+
+int mi_attn_varlen_bwd(const mi_attn_bwd_params* p, void* stream) {
+  g_last_error.clear();
+  if (p == nullptr) return fail(MI_ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (p->struct_size < sizeof(mi_attn_bwd_params))
+    return fail(MI_ATTN_ERR_INVALID_ARG, "struct_size %zu < %zu", p->struct_size,
+                sizeof(mi_attn_bwd_params));
+  const int32_t dt = p->in_dtype;
+  if (dt != MI_ATTN_F16 && dt != MI_ATTN_BF16)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "the backward takes bf16 or fp16 inputs (got dtype %d)", dt);
+  if (!((p->d_qk == 64 && p->d_v == 64) || (p->d_qk == 128 && p->d_v == 128)))
+    return fail(MI_ATTN_ERR_UNSUPPORTED,
+                "backward head dims (d_qk=%d, d_v=%d) unsupported; supported: (64,64), (128,128)",
+                p->d_qk, p->d_v);
+  if (p->hq <= 0 || p->hkv <= 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "head counts must be positive (hq=%d, hkv=%d)", p->hq, p->hkv);
+  if (p->hq % p->hkv != 0)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "hq (%d) must be a multiple of hkv (%d)", p->hq, p->hkv);
+  if (p->num_seqs < 0 || p->max_seqlen_q < 0 || p->max_seqlen_kv < 0 || p->total_q < 0 ||
+      p->total_kv < 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "negative size");
+  if (p->window < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "window must be >= 0");
+  if (p->causal != 0 && p->causal != 1) return fail(MI_ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->window > 0 && !p->causal)
+    return fail(MI_ATTN_ERR_UNSUPPORTED,
+                "a sliding window is defined relative to the causal diagonal; set causal=1");
+  if (!std::isfinite(p->scale) || !(p->scale > 0.0f))
+    return fail(MI_ATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (p->total_q > INT32_MAX || p->total_kv > INT32_MAX)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "total token counts must fit in int32 (cu_seqlens)");
+  if (p->num_seqs == 0 || (p->total_q == 0 && p->total_kv == 0)) return MI_ATTN_OK;
+  if (!p->q || !p->k || !p->v || !p->out || !p->lse || !p->dout || !p->dq || !p->dk || !p->dv ||
+      !p->delta || !p->cu_seqlens_q || !p->cu_seqlens_kv)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "every pointer of the backward params is required");
+  if (p->grad_dtype != dt && p->grad_dtype != MI_ATTN_F32)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "grad_dtype must equal in_dtype or be F32 (got %d)",
+                p->grad_dtype);
+  const void* ptrs16[] = {p->q, p->k, p->v, p->out, p->dout, p->dq, p->dk, p->dv};
+  for (const void* q : ptrs16)
+    if (!aligned16(q)) return fail(MI_ATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const int64_t strides[] = {p->q_stride_tok, p->q_stride_head, p->k_stride_tok, p->k_stride_head,
+                             p->v_stride_tok, p->v_stride_head, p->out_stride_tok, p->out_stride_head,
+                             p->dout_stride_tok, p->dout_stride_head, p->dq_stride_tok,
+                             p->dq_stride_head, p->dk_stride_tok, p->dk_stride_head,
+                             p->dv_stride_tok, p->dv_stride_head};
+  for (int i = 0; i < 16; ++i) {
+    const int64_t mult = (i >= 10 && p->grad_dtype == MI_ATTN_F32) ? 4 : 8;  // 16 bytes
+    if (strides[i] < 0 || strides[i] % mult != 0)
+      return fail(MI_ATTN_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
+  }
+  const int64_t d = p->d_qk;
+  const int64_t tok_strides[] = {p->q_stride_tok, p->k_stride_tok, p->v_stride_tok, p->out_stride_tok,
+                                 p->dout_stride_tok, p->dq_stride_tok, p->dk_stride_tok,
+                                 p->dv_stride_tok};
+  for (int64_t st : tok_strides) {
+    if (st < d) return fail(MI_ATTN_ERR_UNSUPPORTED, "token strides must cover a full head row");
+    if (st * 4 * 64 > INT32_MAX)
+      return fail(MI_ATTN_ERR_UNSUPPORTED, "token strides too large (more than 32 MiB per token)");
+  }
+  if (!layout_disjoint(p->dq_stride_tok, p->total_q, p->dq_stride_head, p->hq, d) ||
+      !layout_disjoint(p->dk_stride_tok, p->total_kv, p->dk_stride_head, p->hkv, d) ||
+      !layout_disjoint(p->dv_stride_tok, p->total_kv, p->dv_stride_head, p->hkv, d))
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "dq / dk / dv strides make their rows overlap");
+  const int64_t n_kt = (p->max_seqlen_kv + 127) / 128, n_qt = (p->max_seqlen_q + 127) / 128;
+  if ((int64_t)p->hq * p->num_seqs > INT32_MAX || n_kt > 65535 || n_qt > 65535 ||
+      (int64_t)p->total_q * p->hq * (d / 8) > INT32_MAX)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (env_flag("MI_ATTN_VALIDATE")) {
+    int rc = validate_cu(p->cu_seqlens_q, p->num_seqs, p->total_q, p->max_seqlen_q, "cu_seqlens_q");
+    if (rc != MI_ATTN_OK) return rc;
+    rc = validate_cu(p->cu_seqlens_kv, p->num_seqs, p->total_kv, p->max_seqlen_kv, "cu_seqlens_kv");
+    if (rc != MI_ATTN_OK) return rc;
+  }
+  mi_attn::BwdArgs a{};
+  a.q = p->q; a.k = p->k; a.v = p->v; a.out = p->out; a.dout = p->dout; a.lse = p->lse;
+  a.dq = p->dq; a.dk = p->dk; a.dv = p->dv; a.delta = p->delta;
+  a.cu_q = p->cu_seqlens_q; a.cu_kv = p->cu_seqlens_kv;
+  a.q_st = p->q_stride_tok; a.q_sh = p->q_stride_head;
+  a.k_st = p->k_stride_tok; a.k_sh = p->k_stride_head;
+  a.v_st = p->v_stride_tok; a.v_sh = p->v_stride_head;
+  a.o_st = p->out_stride_tok; a.o_sh = p->out_stride_head;
+  a.do_st = p->dout_stride_tok; a.do_sh = p->dout_stride_head;
+  a.dq_st = p->dq_stride_tok; a.dq_sh = p->dq_stride_head;
+  a.dk_st = p->dk_stride_tok; a.dk_sh = p->dk_stride_head;
+  a.dv_st = p->dv_stride_tok; a.dv_sh = p->dv_stride_head;
+  a.total_q = p->total_q;
+  a.num_seqs = (int32_t)p->num_seqs;
+  a.hq = p->hq; a.hkv = p->hkv; a.group = p->hq / p->hkv;
+  a.causal = p->causal; a.window = p->window;
+  a.scale = p->scale;
+  a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  hipError_t e = mi_attn::launch_attn_bwd(a, dt, p->grad_dtype == MI_ATTN_F32, (int)d,
+                                          (int)p->max_seqlen_q, (int)p->max_seqlen_kv,
                                           reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return MI_ATTN_OK;

@@ -1,5 +1,6 @@
 /*
- * mi_attn — fused variable-length attention forward for AMD MI355X (gfx950).
+ * mi_attn — fused variable-length attention for AMD MI355X (gfx950): the
+ * forward, its backward, and the bias key-range pass.
  *
  * C ABI.  No HIP or PyTorch types appear in the signatures: device buffers
  * are plain pointers, sizes and strides are integers, the stream is an
@@ -41,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_VERSION 110 /* 1.1.0 */
+#define MI_ATTN_VERSION 120 /* 1.2.0 */
 
 /* Return codes.  On any error nothing is launched and out / lse are untouched. */
 enum {
@@ -163,6 +164,71 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream);
  * negative code (nothing launched).
  */
 int mi_attn_bias_key_ranges(const mi_attn_fwd_params* p, int32_t* ranges, void* stream);
+
+/*
+ * Backward of the forward above: the gradients dq, dk, dv of a loss with
+ * respect to q, k, v, given its gradient dout with respect to out (the LSE
+ * output is not differentiated).  From the forward's definition, with p the
+ * forward's probabilities of each (query row, visible key):
+ *   dv_j = sum_i p_ij dout_i,  D_i = dout_i . out_i,
+ *   ds_ij = p_ij (dout_i . v_j - D_i),
+ *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+ * dk and dv summed over the query heads that share a kv head.  This is the
+ * tiled FlashAttention-2 backward the triton-msl part-2 post describes
+ * (section "Beyond softmax: linear attention and a trainable backward"); the
+ * mtlattn 0.3.0 page (section "Drop-in for scaled_dot_product_attention")
+ * composes it with causal, GQA/MQA and the sliding window, as here.  p is
+ * recomputed from the forward's lse, tile by tile.
+ *
+ * Supported: in_dtype BF16 or F16 (q, k, v, out, dout), dq / dk / dv in
+ * in_dtype or fp32, (d_qk, d_v) in {(64,64), (128,128)}, hq % hkv == 0, window > 0 only
+ * with causal; no bias.  Anything else is refused (MI_ATTN_ERR_UNSUPPORTED).
+ */
+typedef struct mi_attn_bwd_params {
+  size_t struct_size; /* sizeof(mi_attn_bwd_params) */
+  const void* q;      /* the forward's inputs, layouts as in mi_attn_fwd_params */
+  const void* k;
+  const void* v;
+  const void* out;    /* the forward's output [total_q, hq, d_v] (in_dtype) */
+  const float* lse;   /* the forward's LSE [hq, total_q] */
+  const void* dout;   /* gradient of the loss w.r.t. out, [total_q, hq, d_v] (in_dtype) */
+  void* dq;           /* outputs, [total_q, hq, d_qk], [total_kv, hkv, d_qk], */
+  void* dk;           /* [total_kv, hkv, d_v] in grad_dtype, every element */
+  void* dv;           /* written; their rows must not overlap */
+  float* delta;       /* workspace: fp32 [hq, total_q], caller-owned, overwritten */
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_kv;
+  int64_t num_seqs;
+  int64_t max_seqlen_q;  /* >= every sequence's query length */
+  int64_t max_seqlen_kv; /* >= every sequence's key length */
+  int64_t total_q;
+  int64_t total_kv;
+  int32_t hq, hkv, d_qk, d_v;
+  int64_t q_stride_tok, q_stride_head;
+  int64_t k_stride_tok, k_stride_head;
+  int64_t v_stride_tok, v_stride_head;
+  int64_t out_stride_tok, out_stride_head;
+  int64_t dout_stride_tok, dout_stride_head;
+  int64_t dq_stride_tok, dq_stride_head;
+  int64_t dk_stride_tok, dk_stride_head;
+  int64_t dv_stride_tok, dv_stride_head;
+  int32_t in_dtype;   /* MI_ATTN_BF16 or MI_ATTN_F16 */
+  int32_t grad_dtype; /* in_dtype or MI_ATTN_F32 (dq, dk, dv) */
+  float scale;        /* the forward's softmax scale */
+  int32_t causal;   /* the forward's flags */
+  int32_t window;
+} mi_attn_bwd_params;
+
+/*
+ * Enqueue the backward on `stream` (three kernels: delta, dk/dv, dq) and
+ * return without waiting.  Pointers are device memory owned by the caller;
+ * the library allocates nothing.  Strides follow the forward's rules
+ * (multiples of 8 elements, 16-byte aligned pointers).  No atomics: the run
+ * is bitwise deterministic.  Returns MI_ATTN_OK or a negative code (nothing
+ * launched); MI_ATTN_VALIDATE=1 checks the cu_seqlens contracts as for the
+ * forward.
+ */
+int mi_attn_varlen_bwd(const mi_attn_bwd_params* p, void* stream);
 
 /* Reason for the last non-OK return on the calling thread ("" if none). */
 const char* mi_attn_last_error(void);

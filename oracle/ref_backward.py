@@ -29,7 +29,7 @@ matrices, not tiles.
 from __future__ import annotations
 
 import math
-from typing import Optional
+from typing import Optional, Sequence
 
 import numpy as np
 
@@ -37,8 +37,13 @@ from .ref_attention import bias_head, kv_head_of, logits, softmax_rows, visible
 
 
 def varlen_attention_backward(q, k, v, dout, cu_q, cu_kv, scale: Optional[float] = None,
-                              causal: bool = False, window: int = 0, bias=None):
-    """Returns ``(dq, dk, dv)`` in fp64 with the shapes of q, k, v."""
+                              causal: bool = False, window: int = 0, bias=None,
+                              seqs: Optional[Sequence[int]] = None,
+                              kv_heads: Optional[Sequence[int]] = None):
+    """Returns ``(dq, dk, dv)`` in fp64 with the shapes of q, k, v.
+
+    With ``seqs`` / ``kv_heads`` only those sequences and kv heads (with all
+    their query heads) are computed; the other entries stay zero."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -53,7 +58,7 @@ def varlen_attention_backward(q, k, v, dout, cu_q, cu_kv, scale: Optional[float]
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for s in range(len(cu_q) - 1):
+    for s in (range(len(cu_q) - 1) if seqs is None else seqs):
         cq0, cq1 = int(cu_q[s]), int(cu_q[s + 1])
         ck0, ck1 = int(cu_kv[s]), int(cu_kv[s + 1])
         lq, lk = cq1 - cq0, ck1 - ck0
@@ -64,6 +69,8 @@ def varlen_attention_backward(q, k, v, dout, cu_q, cu_kv, scale: Optional[float]
         mask = visible(i, j, lq, lk, causal, window)
         for h in range(hq):
             g = kv_head_of(h, hq, hkv)
+            if kv_heads is not None and g not in kv_heads:
+                continue
             qs, ks, vs = q[cq0:cq1, h], k[ck0:ck1, g], v[ck0:ck1, g]
             brows = None
             if bias is not None:

@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == ["mi_attn_bias_key_ranges", "mi_attn_last_error", "mi_attn_tile_shape",
-                     "mi_attn_varlen_fwd", "mi_attn_version"]
+                     "mi_attn_varlen_bwd", "mi_attn_varlen_fwd", "mi_attn_version"]
     lib = fav.load_library()
     for n in names:
         assert hasattr(lib, n), n
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_tile_shape():
-    assert fav.mi_attn_version() == 110
+    assert fav.mi_attn_version() == 120
     for dt in (fav.BF16, fav.F16):
         for dqk, dv in ((64, 64), (128, 128), (192, 128)):
             bm, bn = fav.mi_attn_tile_shape(dt, dqk, dv)
@@ -47,12 +47,14 @@ def test_version_and_tile_shape():
         fav.mi_attn_tile_shape(fav.BF16, 96, 96)
 
 
-def test_struct_layout_matches_header():
-    fields = [f[0] for f in fav.MiAttnFwdParams._fields_]
+@pytest.mark.parametrize("cls,cname", [(fav.MiAttnFwdParams, "mi_attn_fwd_params"),
+                                       (fav.MiAttnBwdParams, "mi_attn_bwd_params")])
+def test_struct_layout_matches_header(cls, cname):
+    fields = [f[0] for f in cls._fields_]
     src = "#include <stdio.h>\n#include <stddef.h>\n#include \"mi_attn.h\"\nint main(void){\n"
-    src += 'printf("%zu\\n", sizeof(mi_attn_fwd_params));\n'
+    src += f'printf("%zu\\n", sizeof({cname}));\n'
     for f in fields:
-        src += f'printf("%zu\\n", offsetof(mi_attn_fwd_params, {f}));\n'
+        src += f'printf("%zu\\n", offsetof({cname}, {f}));\n'
     src += "return 0;}\n"
     with tempfile.TemporaryDirectory() as d:
         c = os.path.join(d, "layout.c")
@@ -61,9 +63,9 @@ def test_struct_layout_matches_header():
         subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
         vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
                                                check=True).stdout.split()]
-    assert vals[0] == ctypes.sizeof(fav.MiAttnFwdParams)
+    assert vals[0] == ctypes.sizeof(cls)
     for f, off in zip(fields, vals[1:]):
-        assert getattr(fav.MiAttnFwdParams, f).offset == off, f
+        assert getattr(cls, f).offset == off, f
 
 
 def _valid_params():
@@ -174,3 +176,45 @@ def test_empty_problem_is_a_no_op():
     p = _valid_params()
     p.total_q = 0
     fav.mi_attn_varlen_fwd(p, 0)
+
+
+def _valid_bwd_params():
+    p = fav.MiAttnBwdParams()
+    fake = 1 << 20
+    for name in ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv", "delta", "cu_seqlens_q",
+                 "cu_seqlens_kv"):
+        setattr(p, name, fake)
+    p.num_seqs, p.max_seqlen_q, p.max_seqlen_kv, p.total_q, p.total_kv = 2, 64, 64, 100, 100
+    p.hq, p.hkv, p.d_qk, p.d_v = 8, 2, 128, 128
+    for name, hd in (("q", 8), ("k", 2), ("v", 2), ("out", 8), ("dout", 8), ("dq", 8), ("dk", 2),
+                     ("dv", 2)):
+        setattr(p, f"{name}_stride_tok", hd * 128)
+        setattr(p, f"{name}_stride_head", 128)
+    p.in_dtype = p.grad_dtype = fav.BF16
+    p.scale = 0.088
+    return p
+
+
+BWD_REFUSALS = {
+    "fp32_inputs": (dict(in_dtype=fav.F32, grad_dtype=fav.F32), fav.ERR_UNSUPPORTED),
+    "latent_dims": (dict(d_qk=192, d_v=128), fav.ERR_UNSUPPORTED),
+    "grad_dtype": (dict(grad_dtype=fav.F16), fav.ERR_UNSUPPORTED),
+    "gqa_ratio": (dict(hq=6, hkv=4), fav.ERR_UNSUPPORTED),
+    "window_without_causal": (dict(window=8), fav.ERR_UNSUPPORTED),
+    "null_delta": (dict(delta=None), fav.ERR_INVALID_ARG),
+    "misaligned_dk": (dict(dk=(1 << 20) + 8), fav.ERR_INVALID_ARG),
+    "odd_stride": (dict(dout_stride_tok=8 * 128 + 4), fav.ERR_INVALID_ARG),
+    "overlapping_dq": (dict(dq_stride_tok=128, dq_stride_head=128), fav.ERR_UNSUPPORTED),
+    "too_many_key_tiles": (dict(max_seqlen_kv=128 * 65536), fav.ERR_UNSUPPORTED),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_REFUSALS))
+def test_backward_host_validation_refuses(name):
+    changes, code = BWD_REFUSALS[name]
+    p = _valid_bwd_params()
+    for k, v in changes.items():
+        setattr(p, k, v)
+    with pytest.raises(fav.MiAttnError) as ei:
+        fav.mi_attn_varlen_bwd(p, 0)
+    assert ei.value.code == code, fav.mi_attn_last_error()
