@@ -170,7 +170,7 @@ def cpu_baseline(inp: workloads.Inputs, heads, cores: int):
                       f"sequences ({len(units)} (sequence, head) units, "
                       f"{pairs:.3e} useful pairs), {dt:.1f} s wall on {cores} processes with "
                       f"1 BLAS thread each",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "seconds_exact": dt}
 
 
 # ----------------------------------------------------------------- GPU timing
@@ -233,6 +233,10 @@ def main():
         print(f"# CPU oracle baseline on {cores} processes, heads {heads} ...", file=sys.stderr,
               flush=True)
         cpu = cpu_baseline(inp, heads, cores)
+        if w.name.startswith("decode"):
+            frac = len(heads) / w.hq
+            cpu["value"] = algorithmic_bytes(w, 2) * frac / cpu["seconds_exact"] / 1e9
+            cpu["unit"] = "GB/s"
         cpu["host_cores_visible"] = visible
         cpu["cores_note"] = (f"{cores} worker processes: all {visible} cores this process may use"
                              if cores == visible else
@@ -261,6 +265,14 @@ def main():
     # read of the bias), then the forward skips the -inf tiles outside them.
     use_ranges = bias is not None and not args.no_bias_ranges
 
+    is_decode = w.name.startswith("decode")
+    if is_decode:
+        ws = torch.empty(16 << 20, dtype=torch.uint8, device=dev)  # grown below if too small
+        p_probe = fav._fwd_params(q, k, v, cq, ck, w.max_seqlen_q, w.softmax_scale, w.causal,
+                                  w.window, out, lse, out_dtype)
+        need = fav.mi_attn_decode_workspace_size(p_probe, w.max_seqlen_kv, 0)
+        if need > ws.numel():
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
     if args.backward:
         if bias is not None or w.dtype == "f32" or w.d_qk != w.d_v or w.d_qk not in (64, 128):
             print("the backward takes bf16/fp16, head dims 64 or 128, no bias", file=sys.stderr)
@@ -273,6 +285,13 @@ def main():
         torch.cuda.synchronize()
 
     def step(mid_event=None):
+        if is_decode:
+            if mid_event is not None:
+                mid_event.record(stream)
+            fav.varlen_decode(q, k, v, cq, ck, w.max_seqlen_q, w.max_seqlen_kv,
+                              scale=w.softmax_scale, causal=w.causal, window=w.window, out=out,
+                              lse=lse, out_dtype=out_dtype, workspace=ws, stream=stream)
+            return
         if args.backward:
             if mid_event is not None:
                 mid_event.record(stream)
@@ -334,6 +353,12 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     achieved = flops / (kernel_ms * 1e-3) / 1e12
+    if is_decode:
+        # decode is bound by HBM: every K/V byte of the visible ranges read once
+        alg_bytes = algorithmic_bytes(w, out.element_size())
+        value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+        peak = HBM_GBPS
+        achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
     out_bytes = out.element_size()
     # stored counter readings belong to the workload as defined (not to an overridden window)
     traffic = stored_traffic(args.workload) if args.window is None and not args.backward else None
@@ -371,10 +396,12 @@ def main():
               file=sys.stderr, flush=True)
 
     result = {
-        "metric": METRIC if not args.backward else
-        "attn bwd useful TFLOP/s (2.5x the forward's useful FLOPs) + % of MI355X bf16 MFMA peak",
+        "metric": ("attn split-KV decode GB/s (q, k, v, out, lse moved once) + % of MI355X HBM peak"
+                   if is_decode else METRIC if not args.backward else
+                   "attn bwd useful TFLOP/s (2.5x the forward's useful FLOPs) + % of MI355X bf16 "
+                   "MFMA peak"),
         "value": round(value, 2),
-        "unit": "TFLOP/s",
+        "unit": "GB/s" if is_decode else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -400,14 +427,15 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "bound": "mfma",
+            "bound": "hbm" if is_decode else "mfma",
             "achieved": round(achieved, 2),
             "peak": peak,
-            "unit": "TFLOP/s",
+            "unit": "GB/s" if is_decode else "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "algorithmic_bytes": algorithmic_bytes(w, out_bytes),
-            "kernel": ("delta_kernel + dkdv_kernel + dq_kernel" if args.backward else
+            "kernel": ("decode_kernel + decode_merge_kernel" if is_decode else
+                       "delta_kernel + dkdv_kernel + dq_kernel" if args.backward else
                        "attn_fwd_kernel" if w.dtype == "f32" else "attn_fwd16p_kernel"),
             "kernel_ms": round(kernel_ms, 4),
         },
@@ -418,8 +446,9 @@ def main():
     if args.backward:
         result["config"]["pass"] = "backward"
         result["cpu_baseline"] = None  # the oracle baseline is timed for the forward only
-    print(f"# GPU: {ms_per_step:.4f} ms/step, {value:.1f} useful TFLOP/s "
-          f"({100 * value / peak:.1f}% of {peak} TFLOP/s)", file=sys.stderr, flush=True)
+    unit = "GB/s" if is_decode else "useful TFLOP/s"
+    print(f"# GPU: {ms_per_step:.4f} ms/step, {value:.1f} {unit} "
+          f"({100 * value / peak:.1f}% of {peak})", file=sys.stderr, flush=True)
 
     print(json.dumps(result), flush=True)
 

@@ -22,7 +22,8 @@ from typing import Optional
 
 __all__ = ["mi_attn_varlen_fwd", "mi_attn_varlen_bwd", "mi_attn_last_error", "mi_attn_version",
            "mi_attn_tile_shape", "mi_attn_bias_key_ranges", "bias_key_ranges", "varlen_attention",
-           "varlen_attention_backward", "MiAttnBwdParams", "MiAttnFwdParams", "MiAttnError", "load_library", "LIB_PATH",
+           "varlen_attention_backward", "varlen_decode", "mi_attn_varlen_decode",
+           "mi_attn_decode_workspace_size", "MiAttnBwdParams", "MiAttnFwdParams", "MiAttnError", "load_library", "LIB_PATH",
            "F32", "F16", "BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi_attn.so")
@@ -115,6 +116,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mi_attn_bias_key_ranges.restype = ctypes.c_int
     lib.mi_attn_varlen_bwd.argtypes = [ctypes.POINTER(MiAttnBwdParams), ctypes.c_void_p]
     lib.mi_attn_varlen_bwd.restype = ctypes.c_int
+    lib.mi_attn_decode_workspace_size.argtypes = [ctypes.POINTER(MiAttnFwdParams), ctypes.c_int64,
+                                                  ctypes.c_int32]
+    lib.mi_attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.mi_attn_varlen_decode.argtypes = [ctypes.POINTER(MiAttnFwdParams), ctypes.c_int64,
+                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_void_p]
+    lib.mi_attn_varlen_decode.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -149,6 +157,24 @@ def mi_attn_varlen_bwd(params: MiAttnBwdParams, stream: int = 0) -> None:
     """Call the C entry point; raise MiAttnError on a non-OK return."""
     params.struct_size = ctypes.sizeof(MiAttnBwdParams)
     rc = load_library().mi_attn_varlen_bwd(ctypes.byref(params), ctypes.c_void_p(stream))
+    if rc != OK:
+        raise MiAttnError(rc, mi_attn_last_error())
+
+
+def mi_attn_decode_workspace_size(params: MiAttnFwdParams, max_seqlen_kv: int, num_splits: int = 0) -> int:
+    """Workspace bytes mi_attn_varlen_decode needs (0: nothing to compute, or refused)."""
+    params.struct_size = ctypes.sizeof(MiAttnFwdParams)
+    return int(load_library().mi_attn_decode_workspace_size(ctypes.byref(params), max_seqlen_kv,
+                                                            num_splits))
+
+
+def mi_attn_varlen_decode(params: MiAttnFwdParams, max_seqlen_kv: int, num_splits: int,
+                          workspace_ptr: int, workspace_bytes: int, stream: int = 0) -> None:
+    """Call the C entry point; raise MiAttnError on a non-OK return."""
+    params.struct_size = ctypes.sizeof(MiAttnFwdParams)
+    rc = load_library().mi_attn_varlen_decode(ctypes.byref(params), max_seqlen_kv, num_splits,
+                                              ctypes.c_void_p(workspace_ptr), workspace_bytes,
+                                              ctypes.c_void_p(stream))
     if rc != OK:
         raise MiAttnError(rc, mi_attn_last_error())
 
@@ -451,3 +477,61 @@ def _differentiable_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q
             if cu_seqlens_kv.numel() > 1 else 0
     return _FN.apply(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, scale,
                      causal, window)
+
+
+# ---------------------------------------------------------------- split-KV decode
+def _fwd_params(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, scale, causal, window, out,
+                lse, out_dtype):
+    p = MiAttnFwdParams()
+    tq, hq, dqk = q.shape
+    tk, hkv, _ = k.shape
+    p.q, p.k, p.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    p.out = out.data_ptr()
+    p.lse = lse.data_ptr() if lse is not None else None
+    p.cu_seqlens_q, p.cu_seqlens_kv = cu_seqlens_q.data_ptr(), cu_seqlens_kv.data_ptr()
+    p.num_seqs = cu_seqlens_q.numel() - 1
+    p.max_seqlen_q = int(max_seqlen_q)
+    p.total_q, p.total_kv = tq, tk
+    p.hq, p.hkv, p.d_qk, p.d_v = hq, hkv, dqk, v.shape[2]
+    p.q_stride_tok, p.q_stride_head = q.stride(0), q.stride(1)
+    p.k_stride_tok, p.k_stride_head = k.stride(0), k.stride(1)
+    p.v_stride_tok, p.v_stride_head = v.stride(0), v.stride(1)
+    p.out_stride_tok, p.out_stride_head = out.stride(0), out.stride(1)
+    p.in_dtype = _dtype_code(q.dtype)
+    p.out_dtype = _dtype_code(out_dtype)
+    p.scale = float(scale)
+    p.causal = 1 if causal else 0
+    p.window = int(window)
+    return p
+
+
+def varlen_decode(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int, max_seqlen_kv: int,
+                  scale: Optional[float] = None, causal: bool = False, window: int = 0,
+                  num_splits: int = 0, out_dtype=None, return_lse: bool = False, out=None,
+                  lse=None, workspace=None, stream=None):
+    """Split-KV decode (``mi_attn_varlen_decode``): the forward for few query
+    rows per sequence against long key/value caches.  Same arguments and
+    results as ``varlen_attention`` (bf16 / fp16, head dims 64 / 128, no
+    bias), plus ``max_seqlen_kv``, ``num_splits`` (0 = auto) and an optional
+    preallocated uint8 ``workspace`` (else allocated on the stream)."""
+    import torch
+    tq, hq, dqk = q.shape
+    dv = v.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    s_obj = _stream_of(stream, q.device)
+    with torch.cuda.stream(s_obj):
+        if out is None:
+            out = torch.empty(tq, hq, dv, dtype=out_dtype, device=q.device)
+        if return_lse and lse is None:
+            lse = torch.empty(hq, tq, dtype=torch.float32, device=q.device)
+        p = _fwd_params(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, scale, causal, window,
+                        out, lse, out_dtype)
+        need = mi_attn_decode_workspace_size(p, int(max_seqlen_kv), int(num_splits))
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        mi_attn_varlen_decode(p, int(max_seqlen_kv), int(num_splits), workspace.data_ptr(),
+                              workspace.numel(), int(s_obj.cuda_stream))
+    return (out, lse) if return_lse else out
+

@@ -31,8 +31,9 @@
 // accumulate in fp32.
 #pragma once
 
-#include "attn_fwd_kernels.h"
 #include "attn_bwd.h"
+#include "attn_fwd_kernels.h"
+#include "tile_lds.h"
 
 namespace mi_attn {
 namespace {
@@ -67,82 +68,6 @@ __global__ __launch_bounds__(256) void delta_kernel(const BwdArgs a) {
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (ok && sub == 0) a.delta[(int64_t)h * a.total_q + t] = acc;
-}
-
-// ----------------------------------------------------------------------------
-// LDS tiles shared by the two gradient kernels.  A tile is `ROWS` rows of D
-// 16-bit elements, row-major, with the 16-byte chunks of row r XOR-swizzled
-// by VSwz<D>::f(r) (the layout the transposing read below expects).
-// ----------------------------------------------------------------------------
-
-// Per-lane byte offsets (from the tile's first row in global memory) of the
-// chunks this thread copies, for LOADS copies of 256 x 16 bytes.
-template <int D, int LOADS>
-__device__ __forceinline__ void tile_offsets(uint32_t (&off)[LOADS], int64_t st_b, int tid) {
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int pos = i * kThreads + tid;
-    const int row = pos / CPR;
-    const int c = (pos % CPR) ^ VSwz<D>::f(row);
-    off[i] = (uint32_t)(row * st_b + c * 16);
-  }
-}
-
-// Copy `rows` rows of a [tokens, D] tensor view (first row at `base`, token
-// stride st_b bytes) into the tile at `dst`; tile rows at or past `rows` read
-// as zeros (rows <= 0: the whole tile is zero).
-template <int D, int LOADS>
-__device__ __forceinline__ void load_tile(const char* base, int64_t st_b, int rows, lds_char* dst,
-                                          const uint32_t* off, int wave) {
-  const uint32_t bytes = rows > 0 ? (uint32_t)((rows - 1) * st_b + D * 2) : 0u;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(base), bytes);
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + wave * 1024 + i * kThreads * 16),
-                                             16, off[i], 0, 0, 0);
-}
-
-// 8 consecutive elements of tile row `row` starting at column 16 ks + 8 hf
-// (an MFMA operand row fragment).
-template <int D>
-__device__ __forceinline__ u32x4_t row_frag(const lds_char* tile, int row, int ks, int hf) {
-  const int c = (2 * ks + hf) ^ VSwz<D>::f(row);
-  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(tile + row * (D * 2) + c * 16);
-}
-
-// Transposed fragment: rows 16 ks + {0..3, 8..11} + 4 hf of column
-// 32 db + lane % 32, through two ds_read_b64_tr_b16 (the A operand of a
-// product whose reduction runs over the tile's rows).
-template <int D>
-__device__ __forceinline__ u32x4_t tr_frag(const lds_char* tile, int ks, int db, int lane) {
-  const int hf = lane >> 5;
-  const int key_lane = 4 * hf + ((lane & 15) >> 2);
-  const int chunk_lane = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int byte_lane = (lane & 1) * 8;
-  u32x4_t r;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = 16 * ks + 8 * h + key_lane;
-    const int c = (4 * db + chunk_lane) ^ VSwz<D>::f(row);
-    const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16_t*)(tile + row * (D * 2) + c * 16 + byte_lane));
-    const u32x2_t xw = __builtin_bit_cast(u32x2_t, x);
-    r[2 * h] = xw[0];
-    r[2 * h + 1] = xw[1];
-  }
-  return r;
-}
-
-// B-operand fragment of k-step kk (16 rows of the accumulator's M axis) from
-// a 32x32 fp32 accumulator block: the lane's entries 8 kk .. 8 kk + 7, i.e.
-// M rows 16 kk + {0..3, 8..11} + 4 hf, rounded to T (RNE).
-template <typename T>
-__device__ __forceinline__ u32x4_t pack_b(const f32x16_t& x, int kk) {
-  u32x4_t r;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) r[w] = Elem<T>::pack(x[8 * kk + 2 * w], x[8 * kk + 2 * w + 1]);
-  return r;
 }
 
 // Four consecutive gradient values of one row.

@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "attn_bwd.h"
+#include "attn_decode.h"
 #include "attn_fwd.h"
 #include "bias_ranges.h"
 
@@ -108,31 +109,10 @@ int validate_cu(const int32_t* cu_dev, int64_t n, int64_t total, int64_t max_len
   return MI_ATTN_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* mi_attn_last_error(void) { return g_last_error.c_str(); }
-
-int mi_attn_version(void) { return MI_ATTN_VERSION; }
-
-int mi_attn_tile_shape(int32_t in_dtype, int32_t d_qk, int32_t d_v, int32_t* bm, int32_t* bn) {
-  if (in_dtype != MI_ATTN_F32 && in_dtype != MI_ATTN_F16 && in_dtype != MI_ATTN_BF16)
-    return fail(MI_ATTN_ERR_UNSUPPORTED, "unknown dtype %d", in_dtype);
-  if (!dims_supported(in_dtype, d_qk, d_v))
-    return fail(MI_ATTN_ERR_UNSUPPORTED, "head dims (%d, %d) unsupported for dtype %d", d_qk, d_v,
-                in_dtype);
-  if (bm) *bm = mi_attn::tile_bm(in_dtype, d_qk, d_v);
-  if (bn) *bn = mi_attn::tile_bn(in_dtype, d_qk, d_v);
-  return MI_ATTN_OK;
-}
-
-int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
-  g_last_error.clear();
-  mi_attn_fwd_params local;
-  const int rc_copy = copy_params(p_in, &local);
-  if (rc_copy != MI_ATTN_OK) return rc_copy;
-  const mi_attn_fwd_params* p = &local;
+// Checks of a forward call shared by the forward and the decode entry points
+// (correct-or-refuse); *empty is set when there is nothing to compute.
+int check_fwd_params(const mi_attn_fwd_params* p, bool* empty) {
+  *empty = false;
   const int32_t dt = p->in_dtype;
   if (dt != MI_ATTN_F32 && dt != MI_ATTN_F16 && dt != MI_ATTN_BF16)
     return fail(MI_ATTN_ERR_UNSUPPORTED, "unknown in_dtype %d", dt);
@@ -162,7 +142,10 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
   if (p->total_q > INT32_MAX || p->total_kv > INT32_MAX)
     return fail(MI_ATTN_ERR_UNSUPPORTED, "total token counts must fit in int32 (cu_seqlens)");
 
-  if (p->num_seqs == 0 || p->max_seqlen_q == 0 || p->total_q == 0) return MI_ATTN_OK;
+  if (p->num_seqs == 0 || p->max_seqlen_q == 0 || p->total_q == 0) {
+    *empty = true;
+    return MI_ATTN_OK;
+  }
 
   if (!p->q || !p->k || !p->v || !p->out || !p->cu_seqlens_q || !p->cu_seqlens_kv)
     return fail(MI_ATTN_ERR_INVALID_ARG, "q, k, v, out, cu_seqlens_q and cu_seqlens_kv are required");
@@ -215,6 +198,124 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
     if (p->bias_ranges != nullptr && (reinterpret_cast<uintptr_t>(p->bias_ranges) & 7u) != 0)
       return fail(MI_ATTN_ERR_INVALID_ARG, "bias_ranges must be 8-byte aligned");
   }
+
+  return MI_ATTN_OK;
+}
+
+// Chunking of a split-KV decode call.
+struct DecodePlan {
+  int nb;           // 32-row blocks of packed rows (group * max_seqlen_q <= 32 nb)
+  int chunk_tiles;  // 32-key tiles per chunk
+  int n_chunks;
+  size_t ws_o_bytes, ws_bytes;
+};
+
+constexpr int kDecodeTileKeys = 32;
+constexpr int64_t kDecodeTargetWaves = 4096;  // 16 one-wave workgroups per CU
+
+// Checks a decode call and plans its chunks: num_splits chunks per (sequence,
+// kv head) if > 0, else enough for kDecodeTargetWaves workgroups; at most
+// max_ws bytes of workspace (fewer, longer chunks when it would not fit).
+int plan_decode(const mi_attn_fwd_params* p, int64_t max_seqlen_kv, int32_t num_splits,
+                size_t max_ws, DecodePlan* plan, bool* empty) {
+  const int rc = check_fwd_params(p, empty);
+  if (rc != MI_ATTN_OK) return rc;
+  if (p->in_dtype == MI_ATTN_F32)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode takes bf16 or fp16 inputs");
+  if (!((p->d_qk == 64 && p->d_v == 64) || (p->d_qk == 128 && p->d_v == 128)))
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode head dims: (64,64) or (128,128)");
+  if (p->bias != nullptr) return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode takes no bias");
+  if (num_splits < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "num_splits must be >= 0 (0 = auto)");
+  if (max_seqlen_kv < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "max_seqlen_kv must be >= 0");
+  const int64_t group = p->hq / p->hkv;
+  if (group * p->max_seqlen_q > 64)
+    return fail(MI_ATTN_ERR_UNSUPPORTED,
+                "split-KV decode packs (hq / hkv) * max_seqlen_q <= 64 rows per kv head (got %lld); "
+                "use mi_attn_varlen_fwd",
+                (long long)(group * p->max_seqlen_q));
+  if (*empty) return MI_ATTN_OK;
+  int64_t vis = max_seqlen_kv;
+  if (p->window > 0 && vis > (int64_t)p->window + p->max_seqlen_q - 1)
+    vis = (int64_t)p->window + p->max_seqlen_q - 1;
+  const int64_t tiles = (vis + kDecodeTileKeys - 1) / kDecodeTileKeys + 1;  // +1: unaligned start
+  const int64_t units = (int64_t)p->num_seqs * p->hkv;
+  if (units > INT32_MAX) return fail(MI_ATTN_ERR_UNSUPPORTED, "too many (sequence, kv head) units");
+  int64_t splits = num_splits > 0 ? num_splits : (kDecodeTargetWaves + units - 1) / units;
+  splits = std::max<int64_t>(1, std::min<int64_t>(splits, tiles));
+  const size_t row_bytes = (size_t)p->total_q * (size_t)p->hq * (size_t)(p->d_v + 2) * 4;
+  if (row_bytes > max_ws) return fail(MI_ATTN_ERR_UNSUPPORTED, "decode workspace limit too small");
+  const int64_t fit = (int64_t)(max_ws / row_bytes);
+  if (splits > fit) splits = fit;
+  plan->chunk_tiles = (int)((tiles + splits - 1) / splits);
+  plan->n_chunks = (int)((tiles + plan->chunk_tiles - 1) / plan->chunk_tiles);
+  if (plan->n_chunks > 65535) return fail(MI_ATTN_ERR_UNSUPPORTED, "too many chunks");
+  plan->nb = group * p->max_seqlen_q <= 32 ? 1 : 2;
+  plan->ws_o_bytes = (size_t)plan->n_chunks * p->total_q * p->hq * p->d_v * 4;
+  plan->ws_bytes = plan->ws_o_bytes + (size_t)plan->n_chunks * p->total_q * p->hq * 2 * 4;
+  return MI_ATTN_OK;
+}
+
+int launch_decode(const mi_attn_fwd_params* p, const DecodePlan& plan, void* ws, void* stream) {
+  mi_attn::DecodeArgs a{};
+  a.q = p->q; a.k = p->k; a.v = p->v;
+  a.cu_q = p->cu_seqlens_q; a.cu_kv = p->cu_seqlens_kv;
+  a.ws_o = reinterpret_cast<float*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + plan.ws_o_bytes);
+  a.out = p->out; a.lse = p->lse;
+  a.q_st = p->q_stride_tok; a.q_sh = p->q_stride_head;
+  a.k_st = p->k_stride_tok; a.k_sh = p->k_stride_head;
+  a.v_st = p->v_stride_tok; a.v_sh = p->v_stride_head;
+  a.o_st = p->out_stride_tok; a.o_sh = p->out_stride_head;
+  a.total_q = p->total_q;
+  a.num_seqs = (int32_t)p->num_seqs;
+  a.hq = p->hq; a.hkv = p->hkv; a.group = p->hq / p->hkv;
+  a.causal = p->causal; a.window = p->window;
+  a.chunk_tiles = plan.chunk_tiles;
+  a.n_chunks = plan.n_chunks;
+  a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  a.split_l = p->in_dtype == MI_ATTN_BF16 ? kSplitLBf16 : kSplitLF16;
+  if (env_flag("MI_ATTN_VALIDATE")) {
+    int rc = validate_cu(p->cu_seqlens_q, p->num_seqs, p->total_q, p->max_seqlen_q, "cu_seqlens_q");
+    if (rc != MI_ATTN_OK) return rc;
+    rc = validate_cu(p->cu_seqlens_kv, p->num_seqs, p->total_kv, -1, "cu_seqlens_kv");
+    if (rc != MI_ATTN_OK) return rc;
+  }
+  hipError_t e = mi_attn::launch_attn_decode(a, p->in_dtype, p->out_dtype == MI_ATTN_F32, p->d_qk,
+                                             plan.nb, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return MI_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mi_attn_last_error(void) { return g_last_error.c_str(); }
+
+int mi_attn_version(void) { return MI_ATTN_VERSION; }
+
+int mi_attn_tile_shape(int32_t in_dtype, int32_t d_qk, int32_t d_v, int32_t* bm, int32_t* bn) {
+  if (in_dtype != MI_ATTN_F32 && in_dtype != MI_ATTN_F16 && in_dtype != MI_ATTN_BF16)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "unknown dtype %d", in_dtype);
+  if (!dims_supported(in_dtype, d_qk, d_v))
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "head dims (%d, %d) unsupported for dtype %d", d_qk, d_v,
+                in_dtype);
+  if (bm) *bm = mi_attn::tile_bm(in_dtype, d_qk, d_v);
+  if (bn) *bn = mi_attn::tile_bn(in_dtype, d_qk, d_v);
+  return MI_ATTN_OK;
+}
+
+int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
+  g_last_error.clear();
+  mi_attn_fwd_params local;
+  const int rc_copy = copy_params(p_in, &local);
+  if (rc_copy != MI_ATTN_OK) return rc_copy;
+  const mi_attn_fwd_params* p = &local;
+  const int32_t dt = p->in_dtype;
+  bool empty = false;
+  const int rc_check = check_fwd_params(p, &empty);
+  if (rc_check != MI_ATTN_OK || empty) return rc_check;
+  const bool has_bias = p->bias != nullptr;
 
   int32_t bm = 0, bn = 0;
   if (mi_attn_tile_shape(dt, p->d_qk, p->d_v, &bm, &bn) != MI_ATTN_OK) return MI_ATTN_ERR_UNSUPPORTED;
@@ -388,6 +489,35 @@ int mi_attn_varlen_bwd(const mi_attn_bwd_params* p, void* stream) {
                                           reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return MI_ATTN_OK;
+}
+
+size_t mi_attn_decode_workspace_size(const mi_attn_fwd_params* p_in, int64_t max_seqlen_kv,
+                                     int32_t num_splits) {
+  g_last_error.clear();
+  mi_attn_fwd_params local;
+  if (copy_params(p_in, &local) != MI_ATTN_OK) return 0;
+  DecodePlan plan{};
+  bool empty = false;
+  if (plan_decode(&local, max_seqlen_kv, num_splits, SIZE_MAX, &plan, &empty) != MI_ATTN_OK) return 0;
+  return empty ? 0 : plan.ws_bytes;
+}
+
+int mi_attn_varlen_decode(const mi_attn_fwd_params* p_in, int64_t max_seqlen_kv, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  mi_attn_fwd_params local;
+  const int rc_copy = copy_params(p_in, &local);
+  if (rc_copy != MI_ATTN_OK) return rc_copy;
+  DecodePlan plan{};
+  bool empty = false;
+  int rc = plan_decode(&local, max_seqlen_kv, num_splits, SIZE_MAX, &plan, &empty);
+  if (rc != MI_ATTN_OK || empty) return rc;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "workspace must be a 16-byte aligned device pointer");
+  if (workspace_bytes < plan.ws_bytes)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                plan.ws_bytes);
+  return launch_decode(&local, plan, workspace, stream);
 }
 
 int mi_attn_bias_key_ranges(const mi_attn_fwd_params* p_in, int32_t* ranges, void* stream) {

@@ -1,6 +1,7 @@
 /*
  * mi_attn — fused variable-length attention for AMD MI355X (gfx950): the
- * forward, its backward, and the bias key-range pass.
+ * forward, a split-KV decode form of it, its backward, and the bias
+ * key-range pass.
  *
  * C ABI.  No HIP or PyTorch types appear in the signatures: device buffers
  * are plain pointers, sizes and strides are integers, the stream is an
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_VERSION 120 /* 1.2.0 */
+#define MI_ATTN_VERSION 130 /* 1.3.0 */
 
 /* Return codes.  On any error nothing is launched and out / lse are untouched. */
 enum {
@@ -229,6 +230,32 @@ typedef struct mi_attn_bwd_params {
  * forward.
  */
 int mi_attn_varlen_bwd(const mi_attn_bwd_params* p, void* stream);
+
+/*
+ * Split-KV decode: the forward above for calls with few query rows per
+ * sequence and long key/value caches (cached decode, end-aligned causal
+ * rule: the mtlattn 0.3.0 project page, section "Use", notes that this
+ * convention makes self-attention and cached decode both hold).  The visible
+ * key range of every (sequence, kv head) is cut into chunks computed by
+ * separate workgroups; all query heads of a kv head's group and all query
+ * rows of a sequence share each K/V read.  The chunks' unnormalised outputs
+ * and running max / sum go to `workspace`, and a second kernel merges them
+ * with the log-sum-exp rule: M = max m_c, L = sum l_c 2^(m_c - M),
+ * out = sum O_c 2^(m_c - M) / L, lse = (M + log2 L) ln 2.
+ *
+ * Takes the forward's params (same meaning, same results to rounding), plus
+ * max_seqlen_kv >= every sequence's key length and num_splits (chunks per
+ * (sequence, kv head); 0 = enough to fill the GPU).  Supported: bf16 / fp16,
+ * (d_qk, d_v) in {(64,64), (128,128)}, no bias, (hq / hkv) * max_seqlen_q
+ * <= 64; anything else is refused (use mi_attn_varlen_fwd).
+ * workspace: caller-owned device memory of at least
+ * mi_attn_decode_workspace_size(p, max_seqlen_kv, num_splits) bytes, 16-byte
+ * aligned; overwritten.  Asynchronous on `stream`, deterministic.
+ */
+size_t mi_attn_decode_workspace_size(const mi_attn_fwd_params* p, int64_t max_seqlen_kv,
+                                     int32_t num_splits);
+int mi_attn_varlen_decode(const mi_attn_fwd_params* p, int64_t max_seqlen_kv, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Reason for the last non-OK return on the calling thread ("" if none). */
 const char* mi_attn_last_error(void);

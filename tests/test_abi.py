@@ -23,8 +23,9 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["mi_attn_bias_key_ranges", "mi_attn_last_error", "mi_attn_tile_shape",
-                     "mi_attn_varlen_bwd", "mi_attn_varlen_fwd", "mi_attn_version"]
+    assert names == ["mi_attn_bias_key_ranges", "mi_attn_decode_workspace_size", "mi_attn_last_error",
+                     "mi_attn_tile_shape", "mi_attn_varlen_bwd", "mi_attn_varlen_decode",
+                     "mi_attn_varlen_fwd", "mi_attn_version"]
     lib = fav.load_library()
     for n in names:
         assert hasattr(lib, n), n
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_tile_shape():
-    assert fav.mi_attn_version() == 120
+    assert fav.mi_attn_version() == 130
     for dt in (fav.BF16, fav.F16):
         for dqk, dv in ((64, 64), (128, 128), (192, 128)):
             bm, bn = fav.mi_attn_tile_shape(dt, dqk, dv)
@@ -218,3 +219,38 @@ def test_backward_host_validation_refuses(name):
     with pytest.raises(fav.MiAttnError) as ei:
         fav.mi_attn_varlen_bwd(p, 0)
     assert ei.value.code == code, fav.mi_attn_last_error()
+
+
+DECODE_REFUSALS = {
+    "fp32": (dict(in_dtype=fav.F32, out_dtype=fav.F32), 1 << 20, fav.ERR_UNSUPPORTED),
+    "latent_dims": (dict(d_qk=192, d_v=128), 1 << 20, fav.ERR_UNSUPPORTED),
+    "bias": (dict(bias=1 << 20, bias_heads=1, bias_cols=64, bias_stride_tok=64, bias_stride_head=64),
+             1 << 20, fav.ERR_UNSUPPORTED),
+    "too_many_rows": (dict(max_seqlen_q=17), 1 << 20, fav.ERR_UNSUPPORTED),  # 4 heads x 17 > 64
+    "misaligned_workspace": (dict(max_seqlen_q=1), (1 << 20) + 8, fav.ERR_INVALID_ARG),
+    "null_workspace": (dict(max_seqlen_q=1), 0, fav.ERR_INVALID_ARG),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DECODE_REFUSALS))
+def test_decode_host_validation_refuses(name):
+    changes, ws, code = DECODE_REFUSALS[name]
+    p = _valid_params()
+    for k, v in changes.items():
+        setattr(p, k, v)
+    with pytest.raises(fav.MiAttnError) as ei:
+        fav.mi_attn_varlen_decode(p, 4096, 0, ws, 1 << 30, 0)
+    assert ei.value.code == code, fav.mi_attn_last_error()
+
+
+def test_decode_workspace_size_and_short_workspace():
+    """The size query matches the plan (chunks x rows x heads x (d_v + 2)
+    floats) and a workspace one byte short is refused."""
+    p = _valid_params()
+    p.max_seqlen_q, p.total_q = 1, 2
+    n = fav.mi_attn_decode_workspace_size(p, 4096, 8)
+    chunks = -(-(4096 // 32 + 1) // -(-(4096 // 32 + 1) // 8))
+    assert n == chunks * 2 * 8 * (128 + 2) * 4
+    with pytest.raises(fav.MiAttnError) as ei:
+        fav.mi_attn_varlen_decode(p, 4096, 8, 1 << 20, n - 1, 0)
+    assert ei.value.code == fav.ERR_INVALID_ARG and "workspace" in fav.mi_attn_last_error()

@@ -40,3 +40,7 @@ def test_bf16_cast_is_round_to_nearest_even():
     rne = ((bits + 0x7FFF + lsb) >> 16) & 0xFFFF
     got = x.q.view(torch.int16).to(torch.int64) & 0xFFFF
     assert torch.equal(got, rne)
+
+
+def test_decode_lengths_are_the_seeded_draw():
+    assert list(workloads.DECODE_BF16.seqlens_kv) == workloads.decode_lengths()

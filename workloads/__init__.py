@@ -120,6 +120,19 @@ MLA_BF16 = Workload(
     scale=1.0 / math.sqrt(192), seed=5, nope_rope=(128, 64),
     description="bf16 latent-attention shape, 4x4096 tokens, H=128, Dqk=192 (128+64), Dv=128")
 
+def decode_lengths() -> list:
+    """Eight key-cache lengths uniform in [4096, 65536], drawn first from seed 6."""
+    g = torch.Generator().manual_seed(6)
+    return torch.randint(4096, 65537, (8,), generator=g).tolist()
+
+
+DECODE_BF16 = Workload(
+    name="decode_bf16_8seq_q1_hq32_hkv8_d128", seqlens_q=(1,) * 8,
+    seqlens_kv=(30652, 22545, 46653, 24230, 12843, 44002, 50669, 10330), hq=32, hkv=8, d_qk=128,
+    d_v=128, dtype="bf16", causal=True, scale=1.0 / math.sqrt(128), seed=6,
+    description="bf16 cached decode: 8 sequences, 1 query row each, key caches of 4K-64K keys "
+                "(seed 6), Hq=32, Hkv=8, D=128, causal (end-aligned)")
+
 ALL = {
     "tiny_f32": TINY_F32,
     "gqa_causal_bf16": GQA_CAUSAL_BF16,
@@ -131,6 +144,7 @@ ALL = {
     "dense_f16_d64_prefix_lm": dense_f16(64, False, bias=True),
     "swa_bf16": SWA_BF16,
     "mla_bf16": MLA_BF16,
+    "decode_bf16": DECODE_BF16,
 }
 
 
