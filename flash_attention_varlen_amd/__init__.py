@@ -535,3 +535,32 @@ def varlen_decode(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int, max_s
                               workspace.numel(), int(s_obj.cuda_stream))
     return (out, lse) if return_lse else out
 
+
+def mi_attn_varlen_decode_noalloc(params: MiAttnFwdParams, max_seqlen_kv: int, num_splits: int,
+                                  stream: int = 0) -> None:
+    """Call the non-allocating decode entry point; raise MiAttnError on a non-OK return."""
+    lib = load_library()
+    fn = lib.mi_attn_varlen_decode_noalloc
+    fn.argtypes = [ctypes.POINTER(MiAttnFwdParams), ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    params.struct_size = ctypes.sizeof(MiAttnFwdParams)
+    rc = fn(ctypes.byref(params), max_seqlen_kv, num_splits, ctypes.c_void_p(stream))
+    if rc != OK:
+        raise MiAttnError(rc, mi_attn_last_error())
+
+
+def varlen_decode_noalloc(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
+                          max_seqlen_kv: int, out, lse=None, scale: Optional[float] = None,
+                          causal: bool = False, window: int = 0, num_splits: int = 0,
+                          stream=None):
+    """``varlen_decode`` through ``mi_attn_varlen_decode_noalloc``: the caller
+    passes ``out`` (and ``lse``); the library allocates nothing (its workspace
+    is a fixed device array, so calls that overlap on one GPU race)."""
+    import torch
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[2])
+    s_obj = _stream_of(stream, q.device)
+    p = _fwd_params(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, scale, causal, window, out,
+                    lse, out.dtype)
+    mi_attn_varlen_decode_noalloc(p, int(max_seqlen_kv), int(num_splits), int(s_obj.cuda_stream))
+    return out

@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -286,6 +287,33 @@ int launch_decode(const mi_attn_fwd_params* p, const DecodePlan& plan, void* ws,
   return MI_ATTN_OK;
 }
 
+// Device scratch of the non-allocating decode entry point: one array per
+// GPU, alive until the process ends.  Host code never passes its name to a
+// kernel (on the host the name is not a device address): the address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kDecodeScratchBytes = 16u << 20;  // 16 MiB
+__device__ __attribute__((aligned(256))) char scratch[kDecodeScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device id, filled on first use
+
+int scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (g_scratch_ptr[(size_t)dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MI_ATTN_ERR_LAUNCH, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[(size_t)dev] = p;
+  }
+  *ptr = g_scratch_ptr[(size_t)dev];
+  return MI_ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -518,6 +546,22 @@ int mi_attn_varlen_decode(const mi_attn_fwd_params* p_in, int64_t max_seqlen_kv,
     return fail(MI_ATTN_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes,
                 plan.ws_bytes);
   return launch_decode(&local, plan, workspace, stream);
+}
+
+int mi_attn_varlen_decode_noalloc(const mi_attn_fwd_params* p_in, int64_t max_seqlen_kv,
+                                  int32_t num_splits, void* stream) {
+  g_last_error.clear();
+  mi_attn_fwd_params local;
+  const int rc_copy = copy_params(p_in, &local);
+  if (rc_copy != MI_ATTN_OK) return rc_copy;
+  DecodePlan plan{};
+  bool empty = false;
+  int rc = plan_decode(&local, max_seqlen_kv, num_splits, kDecodeScratchBytes, &plan, &empty);
+  if (rc != MI_ATTN_OK || empty) return rc;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != MI_ATTN_OK) return rc;
+  return launch_decode(&local, plan, ws, stream);
 }
 
 int mi_attn_bias_key_ranges(const mi_attn_fwd_params* p_in, int32_t* ranges, void* stream) {

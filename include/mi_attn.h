@@ -257,6 +257,23 @@ size_t mi_attn_decode_workspace_size(const mi_attn_fwd_params* p, int64_t max_se
 int mi_attn_varlen_decode(const mi_attn_fwd_params* p, int64_t max_seqlen_kv, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * mi_attn_varlen_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the partial results go to a fixed device
+ * array of 16 MiB that the library holds on every GPU it runs on until the
+ * process ends (no hipMalloc, hipFree or allocating call, ever).  When the
+ * requested (or automatic) number of chunks would not fit, fewer and longer
+ * chunks are used; when even one chunk per (sequence, kv head) needs more
+ * than 16 MiB (total_q * hq * (d_v + 2) * 4 bytes), the call is refused with
+ * MI_ATTN_ERR_UNSUPPORTED.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (two streams, two threads) race and must be
+ * ordered by the caller.  Nothing in the array needs clearing between calls.
+ * Same arguments, checks and results as mi_attn_varlen_decode.
+ */
+int mi_attn_varlen_decode_noalloc(const mi_attn_fwd_params* p, int64_t max_seqlen_kv,
+                                  int32_t num_splits, void* stream);
+
 /* Reason for the last non-OK return on the calling thread ("" if none). */
 const char* mi_attn_last_error(void);
 

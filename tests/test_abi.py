@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == ["mi_attn_bias_key_ranges", "mi_attn_decode_workspace_size", "mi_attn_last_error",
                      "mi_attn_tile_shape", "mi_attn_varlen_bwd", "mi_attn_varlen_decode",
-                     "mi_attn_varlen_fwd", "mi_attn_version"]
+                     "mi_attn_varlen_decode_noalloc", "mi_attn_varlen_fwd", "mi_attn_version"]
     lib = fav.load_library()
     for n in names:
         assert hasattr(lib, n), n
