@@ -23,7 +23,9 @@ from typing import Optional
 __all__ = ["mi_attn_varlen_fwd", "mi_attn_varlen_bwd", "mi_attn_last_error", "mi_attn_version",
            "mi_attn_tile_shape", "mi_attn_bias_key_ranges", "bias_key_ranges", "varlen_attention",
            "varlen_attention_backward", "varlen_decode", "mi_attn_varlen_decode",
-           "mi_attn_decode_workspace_size", "MiAttnBwdParams", "MiAttnFwdParams", "MiAttnError", "load_library", "LIB_PATH",
+           "mi_attn_decode_workspace_size", "MiAttnBwdParams", "flash_attn_varlen_qkvpacked_func",
+           "flash_attn_varlen_kvpacked_func", "varlen_decode_noalloc",
+           "mi_attn_varlen_decode_noalloc", "MiAttnFwdParams", "MiAttnError", "load_library", "LIB_PATH",
            "F32", "F16", "BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi_attn.so")
@@ -87,6 +89,8 @@ class MiAttnBwdParams(ctypes.Structure):
         ("dv_stride_tok", ctypes.c_int64), ("dv_stride_head", ctypes.c_int64),
         ("in_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
         ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("bias", ctypes.c_void_p), ("bias_heads", ctypes.c_int32), ("bias_cols", ctypes.c_int64),
+        ("bias_stride_tok", ctypes.c_int64), ("bias_stride_head", ctypes.c_int64),
     ]
 
 
@@ -210,8 +214,9 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     ``torch.float32`` is also accepted); ``lse`` is ``[Hq, Tq]`` fp32
     (natural log).  If q, k or v require grad (and grad mode is on), the call
     is differentiable: ``out``'s gradient flows back through
-    ``mi_attn_varlen_bwd`` (bf16 / fp16, head dims 64 / 128, no bias;
-    ``max_seqlen_kv`` is read from ``cu_seqlens_kv`` when not given).
+    ``mi_attn_varlen_bwd`` (bf16 / fp16, head dims 64 / 128;
+    ``max_seqlen_kv`` is read from ``cu_seqlens_kv`` when not given; a bias
+    enters as a constant, and one that requires grad is refused).
 
     ``stream`` (a ``torch.cuda.Stream``, a raw ``hipStream_t`` handle, or
     None for the current stream) is where the kernel runs; outputs and the
@@ -246,15 +251,18 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     if torch.is_grad_enabled() and (q.requires_grad or k.requires_grad or v.requires_grad):
         # differentiable path (mtlattn page, "Drop-in for scaled_dot_product_attention":
         # inputs that require grad route through the backward kernel)
-        if attn_bias is not None or out_dtype != q.dtype or q.dtype == torch.float32 or \
-                out is not None or lse is not None or tile_counts is not None:
+        if attn_bias is not None and attn_bias.requires_grad:
+            raise MiAttnError(ERR_UNSUPPORTED, "the bias is a constant: a bias that requires grad "
+                                               "is refused")
+        if out_dtype != q.dtype or q.dtype == torch.float32 or out is not None or \
+                lse is not None or tile_counts is not None:
             raise MiAttnError(ERR_UNSUPPORTED,
-                              "the differentiable path takes bf16/fp16 inputs, no bias, the default "
-                              "output dtype and no preallocated outputs")
+                              "the differentiable path takes bf16/fp16 inputs, the default output "
+                              "dtype and no preallocated outputs")
         s_obj = _stream_of(stream, q.device)
         with torch.cuda.stream(s_obj):
             o, l = _differentiable_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
-                                             max_seqlen_kv, scale, causal, window)
+                                             max_seqlen_kv, scale, causal, window, attn_bias)
         return (o, l) if return_lse else o
     s_obj = _stream_of(stream, q.device)
     if bias_ranges is not None:
@@ -385,11 +393,12 @@ def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen
 def varlen_attention_backward(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_kv,
                               max_seqlen_q: int, max_seqlen_kv: int, scale: Optional[float] = None,
                               causal: bool = False, window: int = 0, dq=None, dk=None, dv=None,
-                              grad_dtype=None, stream=None):
+                              grad_dtype=None, attn_bias=None, stream=None):
     """Gradients ``(dq, dk, dv)`` of the forward from its inputs, its output
     ``out`` and ``lse`` and the output gradient ``dout`` (bf16 / fp16,
-    head dims 64 or 128, no bias).  Outputs (and the fp32 [Hq, Tq] delta
-    workspace) are allocated on ``stream`` unless given."""
+    head dims 64 or 128; ``attn_bias``, the forward's additive bias, enters as
+    a constant).  Outputs (and the fp32 [Hq, Tq] delta workspace) are
+    allocated on ``stream`` unless given."""
     import torch
     tq, hq, dqk = q.shape
     tk, hkv, _ = k.shape
@@ -424,6 +433,11 @@ def varlen_attention_backward(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_
                         ("dk", dk), ("dv", dv)):
             setattr(p, f"{name}_stride_tok", t.stride(0))
             setattr(p, f"{name}_stride_head", t.stride(1))
+        if attn_bias is not None:
+            bias = _aligned_bias(attn_bias)
+            p.bias = bias.data_ptr()
+            p.bias_heads, p.bias_cols = bias.shape[1], bias.shape[2]
+            p.bias_stride_tok, p.bias_stride_head = bias.stride(0), bias.stride(1)
         p.in_dtype = _dtype_code(q.dtype)
         p.grad_dtype = _dtype_code(gdt)
         p.scale = float(scale)
@@ -442,11 +456,14 @@ def _autograd_fn():
 
         @staticmethod
         def forward(ctx, q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, scale,
-                    causal, window):
+                    causal, window, bias):
             with torch.no_grad():
+                if bias is not None:
+                    bias = _aligned_bias(bias)  # one fp32 layout for both passes
                 out, lse = varlen_attention(q.detach(), k.detach(), v.detach(), cu_seqlens_q,
                                             cu_seqlens_kv, max_seqlen_q, scale=scale, causal=causal,
-                                            window=window, return_lse=True)
+                                            window=window, attn_bias=bias, return_lse=True)
+            ctx.bias = bias
             ctx.save_for_backward(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv)
             ctx.args = (max_seqlen_q, max_seqlen_kv, scale, causal, window)
             ctx.mark_non_differentiable(lse)
@@ -458,8 +475,8 @@ def _autograd_fn():
             max_seqlen_q, max_seqlen_kv, scale, causal, window = ctx.args
             dq, dk, dv = varlen_attention_backward(q, k, v, out, lse, dout.contiguous(), cq, ck,
                                                    max_seqlen_q, max_seqlen_kv, scale, causal,
-                                                   window)
-            return dq, dk, dv, None, None, None, None, None, None, None
+                                                   window, attn_bias=ctx.bias)
+            return dq, dk, dv, None, None, None, None, None, None, None, None
 
     return VarlenAttentionFn
 
@@ -468,7 +485,7 @@ _FN = None
 
 
 def _differentiable_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
-                              scale, causal, window):
+                              scale, causal, window, bias=None):
     global _FN
     if _FN is None:
         _FN = _autograd_fn()
@@ -476,7 +493,7 @@ def _differentiable_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q
         max_seqlen_kv = int((cu_seqlens_kv[1:] - cu_seqlens_kv[:-1]).max().item()) \
             if cu_seqlens_kv.numel() > 1 else 0
     return _FN.apply(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, scale,
-                     causal, window)
+                     causal, window, bias)
 
 
 # ---------------------------------------------------------------- split-KV decode
@@ -564,3 +581,34 @@ def varlen_decode_noalloc(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: in
                     lse, out.dtype)
     mi_attn_varlen_decode_noalloc(p, int(max_seqlen_kv), int(num_splits), int(s_obj.cuda_stream))
     return out
+
+
+# ---------------------------------------------------------------- packed layouts
+def flash_attn_varlen_qkvpacked_func(qkv, cu_seqlens, max_seqlen: int, scale: Optional[float] = None,
+                                     causal: bool = False, window: int = 0, attn_bias=None,
+                                     return_lse: bool = False, out_dtype=None, stream=None):
+    """Self-attention on a packed ``[T, 3, H, D]`` tensor (q, k, v along dim 1),
+    the wrapper the mtlattn 0.3.0 page lists in section "Use".  The three
+    views go to the C ABI as they are (token stride 3 H D, no copy);
+    differentiable like ``varlen_attention`` (the gradient lands in ``qkv``)."""
+    if qkv.dim() != 4 or qkv.shape[1] != 3:
+        raise MiAttnError(ERR_INVALID_ARG, "qkv must be [T, 3, H, D]")
+    q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    return varlen_attention(q, k, v, cu_seqlens, cu_seqlens, max_seqlen, scale=scale,
+                            causal=causal, window=window, attn_bias=attn_bias,
+                            return_lse=return_lse, out_dtype=out_dtype, stream=stream,
+                            max_seqlen_kv=max_seqlen)
+
+
+def flash_attn_varlen_kvpacked_func(q, kv, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
+                                    max_seqlen_kv: int, scale: Optional[float] = None,
+                                    causal: bool = False, window: int = 0, attn_bias=None,
+                                    return_lse: bool = False, out_dtype=None, stream=None):
+    """Attention with k and v packed as ``[Tk, 2, Hkv, D]`` (mtlattn 0.3.0
+    page, section "Use"); views, no copy; differentiable."""
+    if kv.dim() != 4 or kv.shape[1] != 2:
+        raise MiAttnError(ERR_INVALID_ARG, "kv must be [Tk, 2, Hkv, D]")
+    return varlen_attention(q, kv[:, 0], kv[:, 1], cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
+                            scale=scale, causal=causal, window=window, attn_bias=attn_bias,
+                            return_lse=return_lse, out_dtype=out_dtype, stream=stream,
+                            max_seqlen_kv=max_seqlen_kv)

@@ -32,6 +32,11 @@ struct BwdArgs {
   int32_t window;
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
+  // optional constant additive bias [total_q, bias_heads, bias_cols] (fp32)
+  const float* bias;
+  int64_t b_st, b_sh;
+  int32_t bias_heads;  // 1 or hq
+  int32_t bias_cols;   // keys at or past it read a bias of 0
 };
 
 // The backward instances, one per (element type, head dim), compiled in
@@ -39,12 +44,12 @@ struct BwdArgs {
 #define MI_ATTN_BWD_INSTANCES(X) X(bf16, __bf16, 64) X(bf16, __bf16, 128) X(f16, _Float16, 64) X(f16, _Float16, 128)
 #define MI_ATTN_BWD_INSTANCE_NAME(tag, d) launch_bwd_##tag##_##d
 #define MI_ATTN_BWD_DECLARE(tag, T, d)                                                         \
-  hipError_t MI_ATTN_BWD_INSTANCE_NAME(tag, d)(const BwdArgs& a, bool grad_f32, int max_seqlen_q, \
-                                               int max_seqlen_kv, hipStream_t s);
+  hipError_t MI_ATTN_BWD_INSTANCE_NAME(tag, d)(const BwdArgs& a, bool grad_f32, bool bias,     \
+                                               int max_seqlen_q, int max_seqlen_kv, hipStream_t s);
 MI_ATTN_BWD_INSTANCES(MI_ATTN_BWD_DECLARE)
 
 // delta, then dK/dV, then dQ, all on `stream`; grad_f32: fp32 gradients.
-hipError_t launch_attn_bwd(const BwdArgs& a, int in_dtype, bool grad_f32, int d, int max_seqlen_q,
-                           int max_seqlen_kv, hipStream_t stream);
+hipError_t launch_attn_bwd(const BwdArgs& a, int in_dtype, bool grad_f32, bool bias, int d,
+                           int max_seqlen_q, int max_seqlen_kv, hipStream_t stream);
 
 }  // namespace mi_attn

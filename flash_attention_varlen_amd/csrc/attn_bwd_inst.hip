@@ -12,9 +12,10 @@
 namespace mi_attn {
 
 hipError_t MI_ATTN_EXPAND_BWD_NAME(MI_ATTN_INST_TAG, MI_ATTN_INST_D)(const BwdArgs& a, bool grad_f32,
-                                                                    int max_seqlen_q, int max_seqlen_kv,
-                                                                    hipStream_t s) {
-  return launch_bwd_dims<MI_ATTN_INST_T, MI_ATTN_INST_D>(a, grad_f32, max_seqlen_q, max_seqlen_kv, s);
+                                                                    bool bias, int max_seqlen_q,
+                                                                    int max_seqlen_kv, hipStream_t s) {
+  return launch_bwd_dims<MI_ATTN_INST_T, MI_ATTN_INST_D>(a, grad_f32, bias, max_seqlen_q, max_seqlen_kv,
+                                                         s);
 }
 
 }  // namespace mi_attn

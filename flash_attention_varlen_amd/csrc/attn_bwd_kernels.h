@@ -79,7 +79,7 @@ __device__ __forceinline__ void store_grad4(T* p, float a, float b, float c, flo
 // ----------------------------------------------------------------------------
 // dkdv_kernel
 // ----------------------------------------------------------------------------
-template <typename T, int D, typename GradT>
+template <typename T, int D, typename GradT, bool BIAS>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
   constexpr int BK = 128;              // keys per workgroup (32 per wave)
   constexpr int BQ = 64;               // query rows per step (two 32-row blocks)
@@ -190,6 +190,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
   auto compute = [&](int it, auto S) __attribute__((device)) {
     constexpr int s = decltype(S)::value;
     const int q0 = q_lo + (it / a.group) * BQ;
+    const int h = g * a.group + it % a.group;
+    // bias column of this lane's key (keys at or past the bias columns read 0)
+    const float* bcol = nullptr;
+    const bool bkey = BIAS && my_key < min(lk, a.bias_cols);
+    if constexpr (BIAS)
+      bcol = a.bias + (int64_t)(a.bias_heads == 1 ? 0 : h) * a.b_sh + (bkey ? my_key : 0);
     if (!wave_keys || q0 >= wq_hi || q0 + BQ <= wq_lo) return;  // no visible pair for this wave
     const lds_char* qt = (const lds_char*)(s == 0 ? qt_0 : qt_1);
     const lds_char* gt = (const lds_char*)(s == 0 ? gt_0 : gt_1);
@@ -216,7 +222,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = 4 * j + i;
-          float p = fast_exp2(__builtin_fmaf(sc[e], c_scale, -l2[i]));
+          float x = sc[e] * c_scale;
+          if constexpr (BIAS) {
+            // logit = scale s + bias, in log2 units
+            const int row = q0 + r + i;
+            const float b = (bkey && row < lq) ? bcol[(int64_t)(cq0 + row) * a.b_st] : 0.0f;
+            x = __builtin_fmaf(b, kLog2e, x);
+          }
+          float p = fast_exp2(x - l2[i]);
           if (need_mask) {
             const int row = q0 + r + i;
             const bool vis = (!causal || my_key <= row + off) && (W == 0 || my_key > row + off - W);
@@ -283,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
 // ----------------------------------------------------------------------------
 // dq_kernel
 // ----------------------------------------------------------------------------
-template <typename T, int D, typename GradT>
+template <typename T, int D, typename GradT, bool BIAS>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdArgs a) {
   constexpr int BM = 128;              // query rows per workgroup (32 per wave)
   constexpr int BN = 32;               // keys per tile
@@ -354,6 +367,11 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdArgs a) {
       gf[ks] = __builtin_amdgcn_raw_buffer_load_b128(rg, (int)(l32 * g_st_b) + 32 * ks + 16 * hf, 0, 0);
     }
   }
+  const float* brow = nullptr;
+  if constexpr (BIAS)
+    brow = a.bias + (int64_t)(cq0 + (row_ok ? my_row : 0)) * a.b_st +
+           (int64_t)(a.bias_heads == 1 ? 0 : head) * a.b_sh;
+  const int blim = BIAS ? min(lk, a.bias_cols) : 0;
   float l2 = __builtin_inff(), dd = 0.0f;
   if (row_ok) {
     const float l = a.lse[(int64_t)head * a.total_q + cq0 + my_row];
@@ -402,9 +420,24 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdArgs a) {
                            (W > 0 && kb <= w1 - 1 + off - W);
     const int hi = causal ? my_row + off : lk - 1;
     const int lo = W > 0 ? my_row + off - W : -1;
+    f32x4_t bv[4];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key0 = kb + 8 * j + 4 * hf;
+        if (row_ok && key0 + 3 < blim) {
+          bv[j] = *reinterpret_cast<const f32x4_t*>(brow + key0);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bv[j][i] = (row_ok && key0 + i < blim) ? brow[key0 + i] : 0.0f;
+        }
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float p = fast_exp2(__builtin_fmaf(sc[e], c_scale, -l2));
+      float x = sc[e] * c_scale;
+      if constexpr (BIAS) x = __builtin_fmaf(bv[e >> 2][e & 3], kLog2e, x);
+      float p = fast_exp2(x - l2);
       if (need_mask) {
         const int key = kb + 8 * (e >> 2) + 4 * hf + (e & 3);
         p = (key < lk && key <= hi && key > lo) ? p : 0.0f;
@@ -452,7 +485,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdArgs a) {
     }
 }
 
-template <typename T, int D, typename GradT>
+template <typename T, int D, typename GradT, bool BIAS>
 hipError_t launch_bwd_grad(const BwdArgs& a, int max_seqlen_q, int max_seqlen_kv, hipStream_t stream) {
   // delta
   const int64_t items = a.total_q * a.hq;
@@ -465,21 +498,25 @@ hipError_t launch_bwd_grad(const BwdArgs& a, int max_seqlen_q, int max_seqlen_kv
   if (e != hipSuccess) return e;
   const unsigned n_kt = (unsigned)((max_seqlen_kv + 127) / 128);
   const unsigned n_qt = (unsigned)((max_seqlen_q + 127) / 128);
-  hipLaunchKernelGGL((dkdv_kernel<T, D, GradT>), dim3((unsigned)(a.hkv * a.num_seqs), n_kt),
+  hipLaunchKernelGGL((dkdv_kernel<T, D, GradT, BIAS>), dim3((unsigned)(a.hkv * a.num_seqs), n_kt),
                      dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dq_kernel<T, D, GradT>), dim3((unsigned)(a.hq * a.num_seqs), n_qt),
+  hipLaunchKernelGGL((dq_kernel<T, D, GradT, BIAS>), dim3((unsigned)(a.hq * a.num_seqs), n_qt),
                      dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-// grad_f32: dq, dk, dv stored as fp32 instead of the input type
+// grad_f32: dq, dk, dv stored as fp32 instead of the input type; bias: a
+// constant additive bias enters the logits
 template <typename T, int D>
-hipError_t launch_bwd_dims(const BwdArgs& a, bool grad_f32, int max_seqlen_q, int max_seqlen_kv,
-                           hipStream_t stream) {
-  return grad_f32 ? launch_bwd_grad<T, D, float>(a, max_seqlen_q, max_seqlen_kv, stream)
-                  : launch_bwd_grad<T, D, T>(a, max_seqlen_q, max_seqlen_kv, stream);
+hipError_t launch_bwd_dims(const BwdArgs& a, bool grad_f32, bool bias, int max_seqlen_q,
+                           int max_seqlen_kv, hipStream_t stream) {
+  if (bias)
+    return grad_f32 ? launch_bwd_grad<T, D, float, true>(a, max_seqlen_q, max_seqlen_kv, stream)
+                    : launch_bwd_grad<T, D, T, true>(a, max_seqlen_q, max_seqlen_kv, stream);
+  return grad_f32 ? launch_bwd_grad<T, D, float, false>(a, max_seqlen_q, max_seqlen_kv, stream)
+                  : launch_bwd_grad<T, D, T, false>(a, max_seqlen_q, max_seqlen_kv, stream);
 }
 
 }  // namespace

@@ -422,12 +422,17 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
   return MI_ATTN_OK;
 }
 
-int mi_attn_varlen_bwd(const mi_attn_bwd_params* p, void* stream) {
+int mi_attn_varlen_bwd(const mi_attn_bwd_params* p_in, void* stream) {
   g_last_error.clear();
-  if (p == nullptr) return fail(MI_ATTN_ERR_INVALID_ARG, "params is NULL");
-  if (p->struct_size < sizeof(mi_attn_bwd_params))
-    return fail(MI_ATTN_ERR_INVALID_ARG, "struct_size %zu < %zu", p->struct_size,
-                sizeof(mi_attn_bwd_params));
+  if (p_in == nullptr) return fail(MI_ATTN_ERR_INVALID_ARG, "params is NULL");
+  // the params of a 1.2 / 1.3 caller end before bias; later fields read as 0
+  constexpr size_t kBwdSizeV1 = offsetof(mi_attn_bwd_params, bias);
+  if (p_in->struct_size < kBwdSizeV1)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "struct_size %zu < %zu", p_in->struct_size, kBwdSizeV1);
+  mi_attn_bwd_params local;
+  std::memset(&local, 0, sizeof(local));
+  std::memcpy(&local, p_in, p_in->struct_size < sizeof(local) ? p_in->struct_size : sizeof(local));
+  const mi_attn_bwd_params* p = &local;
   const int32_t dt = p->in_dtype;
   if (dt != MI_ATTN_F16 && dt != MI_ATTN_BF16)
     return fail(MI_ATTN_ERR_UNSUPPORTED, "the backward takes bf16 or fp16 inputs (got dtype %d)", dt);
@@ -484,6 +489,16 @@ int mi_attn_varlen_bwd(const mi_attn_bwd_params* p, void* stream) {
       !layout_disjoint(p->dk_stride_tok, p->total_kv, p->dk_stride_head, p->hkv, d) ||
       !layout_disjoint(p->dv_stride_tok, p->total_kv, p->dv_stride_head, p->hkv, d))
     return fail(MI_ATTN_ERR_UNSUPPORTED, "dq / dk / dv strides make their rows overlap");
+  const bool has_bias = p->bias != nullptr;
+  if (has_bias) {
+    if (p->bias_heads != 1 && p->bias_heads != p->hq)
+      return fail(MI_ATTN_ERR_UNSUPPORTED, "bias_heads must be 1 or hq (got %d)", p->bias_heads);
+    if (!aligned16(p->bias) || p->bias_stride_tok < 0 || p->bias_stride_head < 0 ||
+        p->bias_stride_tok % 4 != 0 || p->bias_stride_head % 4 != 0)
+      return fail(MI_ATTN_ERR_INVALID_ARG,
+                  "bias must be 16-byte aligned with strides that are multiples of 4");
+    if (p->bias_cols <= 0) return fail(MI_ATTN_ERR_INVALID_ARG, "bias_cols must be > 0");
+  }
   const int64_t n_kt = (p->max_seqlen_kv + 127) / 128, n_qt = (p->max_seqlen_q + 127) / 128;
   if ((int64_t)p->hq * p->num_seqs > INT32_MAX || n_kt > 65535 || n_qt > 65535 ||
       (int64_t)p->total_q * p->hq * (d / 8) > INT32_MAX)
@@ -512,7 +527,14 @@ int mi_attn_varlen_bwd(const mi_attn_bwd_params* p, void* stream) {
   a.causal = p->causal; a.window = p->window;
   a.scale = p->scale;
   a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
-  hipError_t e = mi_attn::launch_attn_bwd(a, dt, p->grad_dtype == MI_ATTN_F32, (int)d,
+  if (has_bias) {
+    a.bias = p->bias;
+    a.b_st = p->bias_stride_tok;
+    a.b_sh = p->bias_stride_head;
+    a.bias_heads = p->bias_heads;
+    a.bias_cols = (int32_t)(p->bias_cols < INT32_MAX ? p->bias_cols : INT32_MAX);
+  }
+  hipError_t e = mi_attn::launch_attn_bwd(a, dt, p->grad_dtype == MI_ATTN_F32, has_bias, (int)d,
                                           (int)p->max_seqlen_q, (int)p->max_seqlen_kv,
                                           reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));

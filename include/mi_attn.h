@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_VERSION 130 /* 1.3.0 */
+#define MI_ATTN_VERSION 140 /* 1.4.0 */
 
 /* Return codes.  On any error nothing is launched and out / lse are untouched. */
 enum {
@@ -178,12 +178,13 @@ int mi_attn_bias_key_ranges(const mi_attn_fwd_params* p, int32_t* ranges, void* 
  * tiled FlashAttention-2 backward the triton-msl part-2 post describes
  * (section "Beyond softmax: linear attention and a trainable backward"); the
  * mtlattn 0.3.0 page (section "Drop-in for scaled_dot_product_attention")
- * composes it with causal, GQA/MQA and the sliding window, as here.  p is
- * recomputed from the forward's lse, tile by tile.
+ * composes it with causal, GQA/MQA and the sliding window, as here, and
+ * with a constant additive bias.  p is recomputed from the forward's lse,
+ * tile by tile.
  *
  * Supported: in_dtype BF16 or F16 (q, k, v, out, dout), dq / dk / dv in
  * in_dtype or fp32, (d_qk, d_v) in {(64,64), (128,128)}, hq % hkv == 0, window > 0 only
- * with causal; no bias.  Anything else is refused (MI_ATTN_ERR_UNSUPPORTED).
+ * with causal.  Anything else is refused (MI_ATTN_ERR_UNSUPPORTED).
  */
 typedef struct mi_attn_bwd_params {
   size_t struct_size; /* sizeof(mi_attn_bwd_params) */
@@ -218,6 +219,15 @@ typedef struct mi_attn_bwd_params {
   float scale;        /* the forward's softmax scale */
   int32_t causal;   /* the forward's flags */
   int32_t window;
+  /* Added in version 1.4 (a smaller struct_size reads these as NULL / 0): the
+   * forward's additive bias, same layout and rules as in mi_attn_fwd_params,
+   * treated as a constant (its gradient is not computed; the mtlattn page,
+   * section "Use", applies the bias in forward and backward this way).
+   * NULL: no bias. */
+  const float* bias;
+  int32_t bias_heads;
+  int64_t bias_cols;
+  int64_t bias_stride_tok, bias_stride_head;
 } mi_attn_bwd_params;
 
 /*

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_tile_shape():
-    assert fav.mi_attn_version() == 130
+    assert fav.mi_attn_version() == 140
     for dt in (fav.BF16, fav.F16):
         for dqk, dv in ((64, 64), (128, 128), (192, 128)):
             bm, bn = fav.mi_attn_tile_shape(dt, dqk, dv)

@@ -152,3 +152,78 @@ def test_full_size_backward_sampled():
     got = (g32[0].cpu()[rows][:, heads], g32[1].cpu()[keys][:, kvh], g32[2].cpu()[keys][:, kvh])
     want = (ref[0][rows][:, heads], ref[1][keys][:, kvh], ref[2][keys][:, kvh])
     _check("gqa_causal_bf16", got, want, "bf16")
+
+
+@pytest.mark.parametrize("bias_heads", [1, "hq"])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+def test_backward_with_constant_bias(dtype, d, bias_heads):
+    """A constant additive bias with -inf entries (and a row that sees
+    nothing), shared by all heads or one per query head."""
+    w = W(name=f"bwd_bias_{dtype}_{d}_{bias_heads}", seqlens_q=(190, 75), seqlens_kv=(260, 75),
+          hq=4, hkv=2, d_qk=d, d_v=d, dtype=dtype, causal=True, seed=95)
+    inp, dout = _inputs(w, seed=96)
+    nb = w.hq if bias_heads == "hq" else 1
+    bias = workloads.random_bias(w.seqlens_q, nb, 272, seed=97, neg_inf_frac=0.2)
+    bias[7] = float("-inf")
+    say(f"[bwd bias] {w.name}")
+    dev = "cuda"
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    cq, ck = inp.cu_seqlens_q.to(dev), inp.cu_seqlens_kv.to(dev)
+    b = bias.to(dev)
+    out, lse = fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, causal=True, attn_bias=b,
+                                    return_lse=True)
+    g32 = fav.varlen_attention_backward(q, k, v, out, lse, dout.to(dev), cq, ck, w.max_seqlen_q,
+                                        w.max_seqlen_kv, causal=True, attn_bias=b,
+                                        grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.varlen_attention_backward(inp.q.double().numpy(), inp.k.double().numpy(),
+                                           inp.v.double().numpy(), dout.double().numpy(),
+                                           inp.cu_seqlens_q.numpy(), inp.cu_seqlens_kv.numpy(),
+                                           w.softmax_scale, True, 0, bias.double().numpy())
+    _check(w.name, g32, ref, dtype)
+    # the same through autograd, with the bias as a bool mask where it is 0 / -inf
+    qg, kg, vg = (t.clone().requires_grad_() for t in (q, k, v))
+    o = fav.varlen_attention(qg, kg, vg, cq, ck, w.max_seqlen_q, causal=True, attn_bias=b)
+    gq, gk, gv = torch.autograd.grad(o, (qg, kg, vg), dout.to(dev))
+    g16 = fav.varlen_attention_backward(q, k, v, out, lse, dout.to(dev), cq, ck, w.max_seqlen_q,
+                                        w.max_seqlen_kv, causal=True, attn_bias=b)
+    for x, y in zip((gq, gk, gv), g16):
+        assert torch.equal(x, y)
+
+
+def test_bias_that_requires_grad_is_refused():
+    w = W(name="bwd_bias_grad", seqlens_q=(20,), seqlens_kv=(20,), hq=2, hkv=2, d_qk=64, d_v=64,
+          dtype="bf16", causal=False, seed=98)
+    inp = workloads.make_inputs(w)
+    dev = "cuda"
+    q = inp.q.to(dev).requires_grad_()
+    b = torch.zeros(20, 1, 20, device=dev, requires_grad=True)
+    with pytest.raises(fav.MiAttnError):
+        fav.varlen_attention(q, inp.k.to(dev), inp.v.to(dev), inp.cu_seqlens_q.to(dev),
+                             inp.cu_seqlens_kv.to(dev), 20, attn_bias=b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_packed_wrappers_forward_and_backward(dtype):
+    """flash_attn_varlen_qkvpacked_func / _kvpacked_func: views of one packed
+    tensor go to the C ABI as they are; the outputs equal the unpacked call
+    and the gradients land in the packed tensors."""
+    lens = (130, 1, 67)
+    w = W(name="packed_bwd", seqlens_q=lens, seqlens_kv=lens, hq=4, hkv=4, d_qk=64, d_v=64,
+          dtype=dtype, causal=True, seed=99)
+    inp, dout = _inputs(w, seed=100)
+    dev = "cuda"
+    cu = inp.cu_seqlens_q.to(dev)
+    qkv = torch.stack([inp.q, inp.k, inp.v], dim=1).to(dev).requires_grad_()
+    out = fav.flash_attn_varlen_qkvpacked_func(qkv, cu, w.max_seqlen_q, causal=True)
+    (g_qkv,) = torch.autograd.grad(out, (qkv,), dout.to(dev))
+    ref = _run(inp, dout, inp.q.dtype)
+    assert torch.equal(g_qkv[:, 0], ref[0]) and torch.equal(g_qkv[:, 1], ref[1])
+    assert torch.equal(g_qkv[:, 2], ref[2])
+    q = inp.q.to(dev).requires_grad_()
+    kv = torch.stack([inp.k, inp.v], dim=1).to(dev).requires_grad_()
+    out2 = fav.flash_attn_varlen_kvpacked_func(q, kv, cu, cu, w.max_seqlen_q, w.max_seqlen_kv,
+                                               causal=True)
+    assert torch.equal(out2, out)
+    gq, gkv = torch.autograd.grad(out2, (q, kv), dout.to(dev))
+    assert torch.equal(gq, ref[0]) and torch.equal(gkv[:, 0], ref[1]) and torch.equal(gkv[:, 1], ref[2])
