@@ -62,6 +62,9 @@ class MiAttnFwdParams(ctypes.Structure):
         ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
         ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
         ("bias_ranges", ctypes.c_void_p),
+        ("q_rope", ctypes.c_void_p), ("k_rope", ctypes.c_void_p),
+        ("q_rope_stride_tok", ctypes.c_int64), ("q_rope_stride_head", ctypes.c_int64),
+        ("k_rope_stride_tok", ctypes.c_int64), ("k_rope_stride_head", ctypes.c_int64),
     ]
 
 
@@ -205,7 +208,7 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
                      scale: Optional[float] = None, causal: bool = False, window: int = 0,
                      attn_bias=None, out_dtype=None, return_lse: bool = False, out=None,
                      lse=None, tile_counts=None, stream=None, bias_ranges=None,
-                     max_seqlen_kv=None):
+                     max_seqlen_kv=None, q_rope=None, k_rope=None):
     """Fused varlen attention forward.  Returns ``out`` or ``(out, lse)``.
 
     q ``[Tq, Hq, Dqk]``, k ``[Tk, Hkv, Dqk]``, v ``[Tk, Hkv, Dv]`` (device,
@@ -226,6 +229,11 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     fp32 bias whose strides are not multiples of 4 elements is copied into
     such a layout.  ``bias_ranges`` (from ``bias_key_ranges`` on the same
     bias) lets the kernels skip key tiles that are -inf for all their rows.
+
+    Latent-attention head: with ``q_rope`` ``[Tq, Hq, 64]`` and ``k_rope``
+    ``[Tk, Hkv, 64]`` (bf16 / fp16, ``v`` 128 wide), q and k are the 128-wide
+    nope parts and the scores are ``q.k + q_rope.k_rope``, as for one call on
+    the concatenations, without forming them (forward only).
     """
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -245,6 +253,17 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     dv = v.shape[2]
     if k.shape[2] != dqk or v.shape[0] != tk or v.shape[1] != hkv:
         raise MiAttnError(ERR_INVALID_ARG, "k/v shapes do not match q")
+    if (q_rope is None) != (k_rope is None):
+        raise MiAttnError(ERR_INVALID_ARG, "q_rope and k_rope go together")
+    if q_rope is not None:
+        for name, t, rows, heads in (("q_rope", q_rope, tq, hq), ("k_rope", k_rope, tk, hkv)):
+            if (not t.is_cuda or t.dtype != q.dtype or t.dim() != 3 or t.stride(-1) != 1
+                    or tuple(t.shape) != (rows, heads, 64)):
+                raise MiAttnError(ERR_INVALID_ARG, f"{name} must be [{rows}, {heads}, 64] "
+                                                   f"{q.dtype}, last dim contiguous")
+        if torch.is_grad_enabled() and any(t.requires_grad for t in (q, k, v, q_rope, k_rope)):
+            raise MiAttnError(ERR_UNSUPPORTED, "split q_rope / k_rope operands are forward only")
+        dqk = dqk + 64  # the contraction width
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
@@ -275,7 +294,7 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
         return _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
                                            scale, causal, window, attn_bias, out_dtype,
                                            return_lse, out, lse, tile_counts, s_obj, tq, hq, dqk,
-                                           tk, hkv, dv, bias_ranges)
+                                           tk, hkv, dv, bias_ranges, q_rope, k_rope)
 
 
 def _stream_of(stream, device):
@@ -339,7 +358,8 @@ def _aligned_bias(bias):
 
 def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, scale, causal,
                                 window, attn_bias, out_dtype, return_lse, out, lse, tile_counts,
-                                s_obj, tq, hq, dqk, tk, hkv, dv, bias_ranges=None):
+                                s_obj, tq, hq, dqk, tk, hkv, dv, bias_ranges=None, q_rope=None,
+                                k_rope=None):
     import torch
     bias = attn_bias
     if bias is not None:
@@ -367,6 +387,10 @@ def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen
     p.cu_seqlens_q, p.cu_seqlens_kv = cu_seqlens_q.data_ptr(), cu_seqlens_kv.data_ptr()
     p.bias = bias.data_ptr() if bias is not None else None
     p.bias_ranges = bias_ranges.data_ptr() if bias_ranges is not None else None
+    if q_rope is not None:
+        p.q_rope, p.k_rope = q_rope.data_ptr(), k_rope.data_ptr()
+        p.q_rope_stride_tok, p.q_rope_stride_head = q_rope.stride(0), q_rope.stride(1)
+        p.k_rope_stride_tok, p.k_rope_stride_head = k_rope.stride(0), k_rope.stride(1)
     p.tile_counts = tile_counts.data_ptr() if tile_counts is not None else None
     p.num_seqs = cu_seqlens_q.numel() - 1
     p.max_seqlen_q = int(max_seqlen_q)

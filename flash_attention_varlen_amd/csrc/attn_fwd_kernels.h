@@ -766,10 +766,15 @@ struct WaveBlocks {
   static constexpr int kReportBN = 32 * (DQK > 128 ? 1 : DQK == 64 ? 4 : 2);
 };
 
-template <typename T, int DQK, int DV, bool BIAS, typename OutT>
+// ROPE: the query-key contraction's last 64 dims come from separate q_rope /
+// k_rope tensors (the latent-attention head without concatenation); the K
+// tile then holds a 128-wide "nope" part and a 64-wide "rope" part.
+template <typename T, int DQK, int DV, bool BIAS, typename OutT, bool ROPE = false>
 __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void attn_fwd16p_kernel(
     const KernelArgs a) {
   using E = Elem<T>;
+  static_assert(!ROPE || DQK == 192, "split nope / rope operands only for the 192-wide head");
+  constexpr int DN = ROPE ? DQK - 64 : DQK;  // width of the q / k operand (the nope part)
   // A row's running max m lags the true row max by less than
   // 2^kRescaleThreshold: O and l are rescaled between tiles only when a row's
   // max grows by more than that, so most steps skip the O rescale.  The
@@ -785,7 +790,6 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   constexpr int NKS = BN / 16; // PV k-steps per tile
   constexpr int KRB = DQK * 2;
   constexpr int VRB = DV * 2;
-  constexpr int KCPR = DQK / 8;
   constexpr int VCPR = DV / 8;
   constexpr int K_BYTES = BN * KRB;
   constexpr int V_BYTES = BN * VRB;
@@ -961,15 +965,26 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   const char* vbase = reinterpret_cast<const char*>(a.v) + ((int64_t)ck0 * a.v_st + (int64_t)g * a.v_sh) * 2;
 
   // Per-lane byte offsets (within a tile, from its first key) of the chunks
-  // this lane copies; the same for every tile.
+  // this lane copies; the same for every tile.  With ROPE the first KN
+  // copies fill the nope part of the tile and the rest the rope part, so
+  // that every copy reads from one tensor.
+  constexpr int KN = ROPE ? BN * DN * 2 / (kThreads * 16) : KLOADS;
+  const int64_t kr_st_b = a.kr_st * 2;
   uint32_t koff[KLOADS];
   uint32_t voff[VLOADS];
 #pragma unroll
   for (int i = 0; i < KLOADS; ++i) {
-    const int pos = i * kThreads + tid;  // 16-byte slot in the LDS tile
-    const int key = pos / KCPR;
-    const int c = (pos % KCPR) ^ KSwz<DQK>::f(key);
-    koff[i] = (uint32_t)(key * k_st_b + c * 16);
+    if (i < KN) {
+      const int pos = i * kThreads + tid;  // 16-byte slot in the LDS tile
+      const int key = pos / (DN / 8);
+      const int c = (pos % (DN / 8)) ^ KSwz<DN>::f(key);
+      koff[i] = (uint32_t)(key * k_st_b + c * 16);
+    } else {
+      const int pos = (i - KN) * kThreads + tid;
+      const int key = pos / 8;
+      const int c = (pos % 8) ^ KSwz<64>::f(key);
+      koff[i] = (uint32_t)(key * kr_st_b + c * 16);
+    }
   }
 #pragma unroll
   for (int i = 0; i < VLOADS; ++i) {
@@ -995,8 +1010,28 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     else if constexpr (i == 2) return (lds_char*)vbuf_2;
     else return (lds_char*)vbuf_3;
   };
+  const char* krbase = nullptr;
+  if constexpr (ROPE)
+    krbase = reinterpret_cast<const char*>(a.k_rope) + ((int64_t)ck0 * a.kr_st + (int64_t)g * a.kr_sh) * 2;
   auto load_k = [&](int t, auto S) __attribute__((device)) {
-    load_tile_part<DQK, KLOADS>(kbase, k_st_b, t * BN, min(lk - t * BN, BN), kbuf(S) + wave * 1024, koff);
+    load_tile_part<DN, KN>(kbase, k_st_b, t * BN, min(lk - t * BN, BN), kbuf(S) + wave * 1024, koff);
+    if constexpr (ROPE)
+      load_tile_part<64, KLOADS - KN>(krbase, kr_st_b, t * BN, min(lk - t * BN, BN),
+                                      kbuf(S) + KN * kThreads * 16 + wave * 1024, koff + KN);
+  };
+  // LDS address of K fragment (k-step kk: head dims 16 kk .. 16 kk + 15) of key
+  auto kaddr = [&](const lds_char* kt, int key, int kk) __attribute__((device)) -> const lds_char* {
+    if constexpr (ROPE) {
+      if (kk < DN / 16) {
+        const int c = (2 * kk + hf) ^ KSwz<DN>::f(key);
+        return kt + key * (DN * 2) + c * 16;
+      }
+      const int c = (2 * (kk - DN / 16) + hf) ^ KSwz<64>::f(key);
+      return kt + BN * DN * 2 + key * 128 + c * 16;
+    } else {
+      const int c = (2 * kk + hf) ^ KSwz<DQK>::f(key);
+      return kt + key * KRB + c * 16;
+    }
   };
   auto load_v = [&](int t, auto S) __attribute__((device)) {
     load_tile_part<DV, VLOADS>(vbase, v_st_b, t * BN, min(lk - t * BN, BN), vbuf(S) + wave * 1024, voff);
@@ -1012,11 +1047,22 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     const char* qb = uniform_ptr(reinterpret_cast<const char*>(a.q) +
                                  ((int64_t)(cq0 + w0 + 32 * n) * a.q_st + (int64_t)head * a.q_sh) * 2);
     const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(qb, rows > 0 ? (uint32_t)((rows - 1) * q_st_b + DQK * 2) : 0u);
+        make_rsrc(qb, rows > 0 ? (uint32_t)((rows - 1) * q_st_b + DN * 2) : 0u);
     const int qoff = (int)(l32 * q_st_b) + 16 * hf;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
+    for (int ks = 0; ks < DN / 16; ++ks)
       qf[n][ks] = __builtin_amdgcn_raw_buffer_load_b128(r, qoff + 32 * ks, 0, 0);
+    if constexpr (ROPE) {
+      const int64_t qr_st_b = a.qr_st * 2;
+      const char* qrb = uniform_ptr(reinterpret_cast<const char*>(a.q_rope) +
+                                    ((int64_t)(cq0 + w0 + 32 * n) * a.qr_st + (int64_t)head * a.qr_sh) * 2);
+      const __amdgpu_buffer_rsrc_t rr =
+          make_rsrc(qrb, rows > 0 ? (uint32_t)((rows - 1) * qr_st_b + 128) : 0u);
+      const int qroff = (int)(l32 * qr_st_b) + 16 * hf;
+#pragma unroll
+      for (int ks = DN / 16; ks < KSTEPS; ++ks)
+        qf[n][ks] = __builtin_amdgcn_raw_buffer_load_b128(rr, qroff + 32 * (ks - DN / 16), 0, 0);
+    }
   }
 
   // V^T fragment (A operand of O^T += V^T P^T): two transposing reads of the
@@ -1078,10 +1124,8 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
-        const int key = 32 * mb + l32;
-        const int c = (2 * kk + hf) ^ KSwz<DQK>::f(key);
         const u32x4_t kf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
-            kt + key * KRB + c * 16);
+            kaddr(kt, 32 * mb + l32, kk));
 #pragma unroll
         for (int n = 0; n < NB; ++n) s[n][mb] = E::mma(kf, qf[n][kk], s[n][mb]);
       }
@@ -1254,9 +1298,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     // K fragment fi: d-step fi / NMB, key block fi % NMB
     auto kread = [&](int fi) __attribute__((device)) -> u32x4_t {
       const int kk = fi / NMB, mb = fi % NMB;
-      const int key = 32 * mb + l32;
-      const int c = (2 * kk + hf) ^ KSwz<DQK>::f(key);
-      return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(kt + key * KRB + c * 16);
+      return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(kaddr(kt, 32 * mb + l32, kk));
     };
     u32x4_t kf[3];
     u32x4_t vf[3];
@@ -1549,24 +1591,35 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   }
 }
 
-template <typename T, int DQK, int DV, bool BIAS, typename OutT>
+template <typename T, int DQK, int DV, bool BIAS, typename OutT, bool ROPE>
 hipError_t launch_one(const KernelArgs& a, dim3 grid, hipStream_t stream) {
   if constexpr (Elem<T>::kWide) {
     hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, BIAS, OutT>), grid, dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((attn_fwd16p_kernel<T, DQK, DV, BIAS, OutT>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd16p_kernel<T, DQK, DV, BIAS, OutT, ROPE>), grid, dim3(kThreads), 0,
+                       stream, a);
   }
   return hipGetLastError();
 }
 
+template <typename T, int DQK, int DV, bool ROPE>
+hipError_t launch_rope(const KernelArgs& a, bool bias, bool out_f32, dim3 grid, hipStream_t s) {
+  if (bias) {
+    return out_f32 ? launch_one<T, DQK, DV, true, float, ROPE>(a, grid, s)
+                   : launch_one<T, DQK, DV, true, T, ROPE>(a, grid, s);
+  }
+  return out_f32 ? launch_one<T, DQK, DV, false, float, ROPE>(a, grid, s)
+                 : launch_one<T, DQK, DV, false, T, ROPE>(a, grid, s);
+}
+
+// rope: q / k hold the nope part and a.q_rope / a.k_rope the last 64 dims
+// (16-bit types, the 192-wide head only)
 template <typename T, int DQK, int DV>
 hipError_t launch_dims(const KernelArgs& a, bool bias, bool out_f32, dim3 grid, hipStream_t s) {
-  if (bias) {
-    return out_f32 ? launch_one<T, DQK, DV, true, float>(a, grid, s)
-                   : launch_one<T, DQK, DV, true, T>(a, grid, s);
+  if constexpr (!Elem<T>::kWide && DQK == 192) {
+    if (a.q_rope != nullptr) return launch_rope<T, DQK, DV, true>(a, bias, out_f32, grid, s);
   }
-  return out_f32 ? launch_one<T, DQK, DV, false, float>(a, grid, s)
-                 : launch_one<T, DQK, DV, false, T>(a, grid, s);
+  return launch_rope<T, DQK, DV, false>(a, bias, out_f32, grid, s);
 }
 
 }  // namespace

@@ -137,6 +137,14 @@ int check_fwd_params(const mi_attn_fwd_params* p, bool* empty) {
   if (p->window > 0 && !p->causal)
     return fail(MI_ATTN_ERR_UNSUPPORTED,
                 "a sliding window is defined relative to the causal diagonal; set causal=1");
+  const bool rope = p->q_rope != nullptr || p->k_rope != nullptr;
+  if (rope) {
+    if (p->q_rope == nullptr || p->k_rope == nullptr)
+      return fail(MI_ATTN_ERR_INVALID_ARG, "q_rope and k_rope must be given together");
+    if (dt == MI_ATTN_F32 || p->d_qk != 192 || p->d_v != 128)
+      return fail(MI_ATTN_ERR_UNSUPPORTED,
+                  "split nope / rope operands need 16-bit inputs with d_qk = 192, d_v = 128");
+  }
   if (!std::isfinite(p->scale)) return fail(MI_ATTN_ERR_INVALID_ARG, "scale is not finite");
   if (!(p->scale > 0.0f))
     return fail(MI_ATTN_ERR_UNSUPPORTED, "scale must be > 0 (got %g)", (double)p->scale);
@@ -161,10 +169,27 @@ int check_fwd_params(const mi_attn_fwd_params* p, bool* empty) {
       return fail(MI_ATTN_ERR_INVALID_ARG,
                   "q/k/v strides must be non-negative multiples of %lld elements (got %lld)",
                   (long long)in_mult, (long long)s);
-  if (p->q_stride_tok < p->d_qk || p->k_stride_tok < p->d_qk || p->v_stride_tok < p->d_v)
+  const int64_t dqk_main = rope ? p->d_qk - 64 : p->d_qk;  // width q and k hold
+  if (p->q_stride_tok < dqk_main || p->k_stride_tok < dqk_main || p->v_stride_tok < p->d_v)
     return fail(MI_ATTN_ERR_UNSUPPORTED,
                 "q/k/v token strides must cover a full head row (q_stride_tok, k_stride_tok >= d_qk, "
-                "v_stride_tok >= d_v)");
+                "or 128 with q_rope / k_rope; v_stride_tok >= d_v)");
+  if (rope) {
+    if (!aligned16(p->q_rope) || !aligned16(p->k_rope))
+      return fail(MI_ATTN_ERR_INVALID_ARG, "q_rope and k_rope must be 16-byte aligned");
+    const int64_t rs[4] = {p->q_rope_stride_tok, p->q_rope_stride_head, p->k_rope_stride_tok,
+                           p->k_rope_stride_head};
+    for (int64_t s : rs)
+      if (s < 0 || s % 8 != 0)
+        return fail(MI_ATTN_ERR_INVALID_ARG,
+                    "q_rope/k_rope strides must be non-negative multiples of 8 elements (got %lld)",
+                    (long long)s);
+    if (p->q_rope_stride_tok < 64 || p->k_rope_stride_tok < 64)
+      return fail(MI_ATTN_ERR_UNSUPPORTED, "q_rope/k_rope token strides must be >= 64");
+    if (p->q_rope_stride_tok * 2 * 64 > INT32_MAX || p->k_rope_stride_tok * 2 * 64 > INT32_MAX)
+      return fail(MI_ATTN_ERR_UNSUPPORTED,
+                  "q_rope/k_rope token strides too large (more than 32 MiB per token)");
+  }
   // 16-bit Q rows and K/V tiles are fetched through 32-bit buffer offsets
   // spanning at most 64 tokens.
   if (dt != MI_ATTN_F32 &&
@@ -226,6 +251,8 @@ int plan_decode(const mi_attn_fwd_params* p, int64_t max_seqlen_kv, int32_t num_
   if (!((p->d_qk == 64 && p->d_v == 64) || (p->d_qk == 128 && p->d_v == 128)))
     return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode head dims: (64,64) or (128,128)");
   if (p->bias != nullptr) return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode takes no bias");
+  if (p->q_rope != nullptr || p->k_rope != nullptr)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode takes no q_rope / k_rope");
   if (num_splits < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "num_splits must be >= 0 (0 = auto)");
   if (max_seqlen_kv < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "max_seqlen_kv must be >= 0");
   const int64_t group = p->hq / p->hkv;
@@ -371,6 +398,12 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
   a.cu_kv = p->cu_seqlens_kv;
   a.bias = p->bias;
   a.bias_ranges = has_bias ? p->bias_ranges : nullptr;
+  a.q_rope = p->q_rope;
+  a.k_rope = p->k_rope;
+  a.qr_st = p->q_rope_stride_tok;
+  a.qr_sh = p->q_rope_stride_head;
+  a.kr_st = p->k_rope_stride_tok;
+  a.kr_sh = p->k_rope_stride_head;
   a.tile_counts = p->tile_counts;
   a.q_st = p->q_stride_tok;
   a.q_sh = p->q_stride_head;

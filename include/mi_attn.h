@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_VERSION 140 /* 1.4.0 */
+#define MI_ATTN_VERSION 150 /* 1.5.0 */
 
 /* Return codes.  On any error nothing is launched and out / lse are untouched. */
 enum {
@@ -90,7 +90,7 @@ enum { MI_ATTN_F32 = 0, MI_ATTN_F16 = 1, MI_ATTN_BF16 = 2 };
  * Strides are in elements (not bytes); *_stride_tok between consecutive
  * tokens, *_stride_head between consecutive heads; each must be a multiple
  * of 8 elements for 16-bit types and of 4 for fp32.  q/k token strides must
- * be >= d_qk and v's and out's >= d_v; for 16-bit types 64 q/k/v token
+ * be >= d_qk (>= 128 with q_rope / k_rope) and v's and out's >= d_v; for 16-bit types 64 q/k/v token
  * strides and 32 out token strides must fit in 2^31 bytes; the out strides
  * must keep the [total_q, hq, d_v] rows disjoint.  Anything else is refused
  * with MI_ATTN_ERR_UNSUPPORTED.
@@ -135,6 +135,23 @@ typedef struct mi_attn_fwd_params {
    * skip, exactly, the key tiles in which every bias value of a workgroup's
    * (or a wave's) rows is -inf.  NULL: no skipping.  Ignored without a bias. */
   const int32_t* bias_ranges;
+  /* Added in version 1.5 (NULL for older callers):
+   * split operands of the latent-attention head (d_qk = 192, d_v = 128,
+   * 16-bit inputs).  The triton-msl part-2 post (section "Latent attention,
+   * the 2026 frontier") describes that head's score as the sum of two
+   * query-key products: a 128-wide part without position encoding ("nope")
+   * and a 64-wide rotary part ("rope").  With q_rope and k_rope
+   * set, q and k hold only the nope part (their first 128 dims are read)
+   * and q_rope / k_rope the rope part, [total_q, hq, 64] and
+   * [total_kv, hkv, 64] addressed with the strides below (elements,
+   * multiples of 8, token strides >= 64 and within 32 MiB); the result is
+   * that of one call on the concatenation [nope | rope] of each.  Both set
+   * or both NULL; 16-byte aligned.  Only mi_attn_varlen_fwd reads them
+   * (the decode and backward entry points refuse them). */
+  const void* q_rope;
+  const void* k_rope;
+  int64_t q_rope_stride_tok, q_rope_stride_head;
+  int64_t k_rope_stride_tok, k_rope_stride_head;
 } mi_attn_fwd_params;
 
 /*

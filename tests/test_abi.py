@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_tile_shape():
-    assert fav.mi_attn_version() == 140
+    assert fav.mi_attn_version() == 150
     for dt in (fav.BF16, fav.F16):
         for dqk, dv in ((64, 64), (128, 128), (192, 128)):
             bm, bn = fav.mi_attn_tile_shape(dt, dqk, dv)
@@ -114,6 +114,27 @@ REFUSALS = {
                               fav.ERR_UNSUPPORTED),
     # token rows overlap the next token's heads (token stride below hq * d_v)
     "overlapping_out_tokens": (dict(out_stride_tok=512, out_stride_head=128), fav.ERR_UNSUPPORTED),
+    # split nope / rope operands: both pointers, the latent head, 16-bit, aligned strides
+    "rope_without_k_rope": (dict(d_qk=192, q_rope=1 << 20, q_rope_stride_tok=8 * 64,
+                                 q_rope_stride_head=64), fav.ERR_INVALID_ARG),
+    "rope_square_head": (dict(q_rope=1 << 20, k_rope=1 << 20, q_rope_stride_tok=8 * 64,
+                              q_rope_stride_head=64, k_rope_stride_tok=2 * 64,
+                              k_rope_stride_head=64), fav.ERR_UNSUPPORTED),
+    "rope_f32": (dict(in_dtype=fav.F32, out_dtype=fav.F32, d_qk=192, q_rope=1 << 20,
+                      k_rope=1 << 20, q_rope_stride_tok=8 * 64, q_rope_stride_head=64,
+                      k_rope_stride_tok=2 * 64, k_rope_stride_head=64), fav.ERR_UNSUPPORTED),
+    "rope_misaligned": (dict(d_qk=192, q_rope=1 << 20, k_rope=(1 << 20) + 8,
+                             q_rope_stride_tok=8 * 64, q_rope_stride_head=64,
+                             k_rope_stride_tok=2 * 64, k_rope_stride_head=64), fav.ERR_INVALID_ARG),
+    "rope_odd_stride": (dict(d_qk=192, q_rope=1 << 20, k_rope=1 << 20, q_rope_stride_tok=8 * 64 + 4,
+                             q_rope_stride_head=64, k_rope_stride_tok=2 * 64,
+                             k_rope_stride_head=64), fav.ERR_INVALID_ARG),
+    "rope_short_row": (dict(d_qk=192, q_rope=1 << 20, k_rope=1 << 20, q_rope_stride_tok=8 * 64,
+                            q_rope_stride_head=64, k_rope_stride_tok=56,
+                            k_rope_stride_head=0), fav.ERR_UNSUPPORTED),
+    # with split operands q / k hold 128 dims; without them a 128-wide stride is short of 192
+    "latent_short_q_stride": (dict(d_qk=192, q_stride_tok=128, q_stride_head=0, hq=2, hkv=2,
+                                   out_stride_tok=2 * 128), fav.ERR_UNSUPPORTED),
 }
 
 
@@ -224,6 +245,8 @@ def test_backward_host_validation_refuses(name):
 DECODE_REFUSALS = {
     "fp32": (dict(in_dtype=fav.F32, out_dtype=fav.F32), 1 << 20, fav.ERR_UNSUPPORTED),
     "latent_dims": (dict(d_qk=192, d_v=128), 1 << 20, fav.ERR_UNSUPPORTED),
+    "rope": (dict(q_rope=1 << 20, k_rope=1 << 20, q_rope_stride_tok=8 * 64, q_rope_stride_head=64,
+                  k_rope_stride_tok=2 * 64, k_rope_stride_head=64), 1 << 20, fav.ERR_UNSUPPORTED),
     "bias": (dict(bias=1 << 20, bias_heads=1, bias_cols=64, bias_stride_tok=64, bias_stride_head=64),
              1 << 20, fav.ERR_UNSUPPORTED),
     "too_many_rows": (dict(max_seqlen_q=17), 1 << 20, fav.ERR_UNSUPPORTED),  # 4 heads x 17 > 64
