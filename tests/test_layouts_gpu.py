@@ -76,7 +76,8 @@ def test_split_nope_rope_full_latent_shape():
     say(f"[rope] full {w.name}")
     inp = workloads.make_inputs(w)
     q, k, v, cq, ck, b = to_device(inp)
-    out, lse, cat_out, cat_lse = _pair(w, q, k, v, cq, ck, b, "separate", torch.bfloat16)
+    # fp32 output: the tolerance covers the kernel's arithmetic, not a final bf16 rounding
+    out, lse, cat_out, cat_lse = _pair(w, q, k, v, cq, ck, b, "separate", torch.float32)
     assert torch.equal(out, cat_out) and torch.equal(lse, cat_lse)
     del cat_out, cat_lse, q, k, v
     check_sampled(inp, out, lse, heads=[0, 63, 127], rows_per_seq=8, seed=3)
