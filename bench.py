@@ -200,6 +200,9 @@ def main():
                     help="with a bias, do not compute the bias key ranges (visit every tile)")
     ap.add_argument("--window", type=int, default=None,
                     help="override the window width of a sliding-window workload (cost vs W)")
+    ap.add_argument("--split-rope", action="store_true",
+                    help="latent workload: pass q, k as 128-wide nope tensors plus 64-wide "
+                         "q_rope / k_rope tensors instead of the concatenation")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -256,6 +259,14 @@ def main():
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     cq, ck = inp.cu_seqlens_q.to(dev), inp.cu_seqlens_kv.to(dev)
     bias = inp.bias.to(dev) if inp.bias is not None else None
+    rope_kw = {}
+    if args.split_rope:
+        if w.nope_rope is None:
+            print("--split-rope applies to the latent-attention workload", file=sys.stderr)
+            sys.exit(2)
+        dn = w.nope_rope[0]
+        rope_kw = dict(q_rope=q[..., dn:].contiguous(), k_rope=k[..., dn:].contiguous())
+        q, k = q[..., :dn].contiguous(), k[..., :dn].contiguous()
     out_dtype = q.dtype if args.out_dtype == "input" else torch.float32
     out = torch.empty(w.total_q, w.hq, w.d_v, dtype=out_dtype, device=dev)
     lse = torch.empty(w.hq, w.total_q, dtype=torch.float32, device=dev)
@@ -306,7 +317,7 @@ def main():
             mid_event.record(stream)
         fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, scale=w.softmax_scale,
                              causal=w.causal, window=w.window, attn_bias=bias, out=out, lse=lse,
-                             out_dtype=out_dtype, stream=stream, bias_ranges=rg)
+                             out_dtype=out_dtype, stream=stream, bias_ranges=rg, **rope_kw)
 
     # GPU clocks depend on the load state: a cold GPU reads well below its
     # warmed rate (the mtlattn 0.3.0 page, section "Performance", gives the
@@ -418,6 +429,7 @@ def main():
             "hq": w.hq, "hkv": w.hkv, "d_qk": w.d_qk, "d_v": w.d_v,
             "causal": w.causal, "window": w.window,
             "bias": w.bias, "out_dtype": str(out_dtype).replace("torch.", ""),
+            "operands": "split nope / rope" if args.split_rope else "concatenated",
             "useful_flops_per_step": flops,
             "pct_of_peak": round(100.0 * value / peak, 2),
             "median_launch_ms": round(per[len(per) // 2], 4),
