@@ -636,3 +636,228 @@ def flash_attn_varlen_kvpacked_func(q, kv, cu_seqlens_q, cu_seqlens_kv, max_seql
                             scale=scale, causal=causal, window=window, attn_bias=attn_bias,
                             return_lse=return_lse, out_dtype=out_dtype, stream=stream,
                             max_seqlen_kv=max_seqlen_kv)
+
+
+# ---------------------------------------------------------------- key-padding front end
+class MiAttnPackParams(ctypes.Structure):
+    """Field-for-field mirror of ``mi_attn_pack_params``."""
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("padded", ctypes.c_void_p), ("packed", ctypes.c_void_p),
+        ("ranks", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+        ("heads", ctypes.c_int32), ("dim", ctypes.c_int32), ("elem_bytes", ctypes.c_int32),
+        ("padded_stride_batch", ctypes.c_int64), ("padded_stride_tok", ctypes.c_int64),
+        ("padded_stride_head", ctypes.c_int64),
+        ("packed_stride_tok", ctypes.c_int64), ("packed_stride_head", ctypes.c_int64),
+    ]
+
+
+def mi_attn_padding_to_varlen(mask_ptr: int, batch: int, seqlen: int, mask_stride_batch: int,
+                              ranks_ptr: int, cu_ptr: int, stats_ptr: int, stream: int = 0) -> None:
+    """Call the C entry point; raise MiAttnError on a non-OK return."""
+    lib = load_library()
+    f = lib.mi_attn_padding_to_varlen
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    rc = f(mask_ptr, batch, seqlen, mask_stride_batch, ranks_ptr, cu_ptr, stats_ptr,
+           ctypes.c_void_p(stream))
+    if rc != OK:
+        raise MiAttnError(rc, mi_attn_last_error())
+
+
+def _pack_call(name: str, params: MiAttnPackParams, stream: int) -> None:
+    f = getattr(load_library(), name)
+    f.argtypes = [ctypes.POINTER(MiAttnPackParams), ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    params.struct_size = ctypes.sizeof(MiAttnPackParams)
+    rc = f(ctypes.byref(params), ctypes.c_void_p(stream))
+    if rc != OK:
+        raise MiAttnError(rc, mi_attn_last_error())
+
+
+def mi_attn_pack_tokens(params: MiAttnPackParams, stream: int = 0) -> None:
+    _pack_call("mi_attn_pack_tokens", params, stream)
+
+
+def mi_attn_unpack_tokens(params: MiAttnPackParams, stream: int = 0) -> None:
+    _pack_call("mi_attn_unpack_tokens", params, stream)
+
+
+def padding_to_varlen(mask, stream=None, sync: bool = True):
+    """Key-padding mask -> varlen form.  ``mask`` bool (or uint8) ``[B, N]``
+    on the device, True = valid token (the last dim may be a view with a
+    batch stride).  Returns ``(ranks, cu_seqlens, total, longest)``: int32
+    ``[B, N]`` ranks (-1 at padding), int32 ``[B + 1]`` cumulative counts,
+    and, with ``sync`` (one device-to-host read), the total valid tokens and
+    the longest row as ints (else the int32 ``[2]`` device tensor)."""
+    import torch
+    if mask.dim() != 2 or not mask.is_cuda or mask.dtype not in (torch.bool, torch.uint8):
+        raise MiAttnError(ERR_INVALID_ARG, "mask must be a bool / uint8 [B, N] device tensor")
+    if mask.shape[1] > 1 and mask.stride(1) != 1:
+        mask = mask.contiguous()
+    bsz, n = mask.shape
+    s_obj = _stream_of(stream, mask.device)
+    with torch.cuda.stream(s_obj):
+        ranks = torch.empty(bsz, n, dtype=torch.int32, device=mask.device)
+        cu = torch.empty(bsz + 1, dtype=torch.int32, device=mask.device)
+        stats = torch.empty(2, dtype=torch.int32, device=mask.device)
+        mi_attn_padding_to_varlen(mask.data_ptr(), bsz, n, mask.stride(0) if bsz > 1 else n,
+                                  ranks.data_ptr(), cu.data_ptr(), stats.data_ptr(),
+                                  int(s_obj.cuda_stream))
+    if not sync:
+        return ranks, cu, stats
+    total, longest = (int(x) for x in stats.tolist())
+    return ranks, cu, total, longest
+
+
+def _pack_params(padded, packed, ranks, cu, bsz, n):
+    p = MiAttnPackParams()
+    p.padded, p.packed = padded.data_ptr(), packed.data_ptr()
+    p.ranks = ranks.data_ptr() if ranks is not None else None
+    p.cu_seqlens = cu.data_ptr() if cu is not None else None
+    p.batch, p.seqlen = bsz, n
+    p.heads, p.dim = padded.shape[2], padded.shape[3]
+    p.elem_bytes = padded.element_size()
+    p.padded_stride_batch, p.padded_stride_tok, p.padded_stride_head = (
+        padded.stride(0), padded.stride(1), padded.stride(2))
+    p.packed_stride_tok, p.packed_stride_head = packed.stride(0), packed.stride(1)
+    return p
+
+
+def pack_tokens(padded, ranks=None, cu_seqlens=None, total=None, out=None, stream=None):
+    """Gather ``padded`` ``[B, N, H, D]`` (any strides, last dim contiguous)
+    into packed ``[total, H, D]``; ``ranks=None`` packs every token."""
+    import torch
+    bsz, n, h, d = padded.shape
+    if padded.stride(-1) != 1:
+        raise MiAttnError(ERR_INVALID_ARG, "padded must have a contiguous last dim")
+    if total is None:
+        total = bsz * n
+    if ranks is not None and tuple(ranks.shape) != (bsz, n):
+        raise MiAttnError(ERR_INVALID_ARG, "ranks must be [B, N]")
+    s_obj = _stream_of(stream, padded.device)
+    with torch.cuda.stream(s_obj):
+        if out is None:
+            out = torch.empty(total, h, d, dtype=padded.dtype, device=padded.device)
+        elif tuple(out.shape) != (total, h, d) or out.dtype != padded.dtype:
+            raise MiAttnError(ERR_INVALID_ARG, "out has the wrong shape or dtype")
+        mi_attn_pack_tokens(_pack_params(padded, out, ranks, cu_seqlens, bsz, n),
+                            int(s_obj.cuda_stream))
+    return out
+
+
+def unpack_tokens(packed, out, ranks=None, cu_seqlens=None, stream=None):
+    """Scatter packed ``[total, H, D]`` into ``out`` ``[B, N, H, D]`` (any
+    strides, last dim contiguous), zeros at padding; returns ``out``."""
+    import torch
+    bsz, n, h, d = out.shape
+    if out.stride(-1) != 1 or packed.dtype != out.dtype or tuple(packed.shape[1:]) != (h, d):
+        raise MiAttnError(ERR_INVALID_ARG, "out / packed shapes, dtypes or layout do not match")
+    if ranks is not None and tuple(ranks.shape) != (bsz, n):
+        raise MiAttnError(ERR_INVALID_ARG, "ranks must be [B, N]")
+    s_obj = _stream_of(stream, out.device)
+    with torch.cuda.stream(s_obj):
+        mi_attn_unpack_tokens(_pack_params(out, packed, ranks, cu_seqlens, bsz, n),
+                              int(s_obj.cuda_stream))
+    return out
+
+
+def _key_padding_of(attn_mask, bsz, nkv):
+    """The [B, Nkv] key mask if ``attn_mask`` is a bool key-padding mask
+    ``[B, 1, 1, Nkv]``, else None."""
+    import torch
+    if attn_mask is None or attn_mask.dtype != torch.bool or attn_mask.dim() != 4:
+        return None
+    if tuple(attn_mask.shape) == (bsz, 1, 1, nkv):
+        return attn_mask[:, 0, 0, :]
+    return None
+
+
+def sdpa(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: bool = False,
+         scale: Optional[float] = None, enable_gqa: bool = False, stream=None, out_dtype=None):
+    """``scaled_dot_product_attention`` on dense ``[B, H, N, D]`` tensors
+    through the varlen kernels (the adapter of the mtlattn 0.3.0 page,
+    section "Drop-in for scaled_dot_product_attention"), forward only.
+
+    * A boolean key-padding mask (``[B, 1, 1, Nkv]`` or ``[B, Nkv]``, True =
+      valid) is turned into varlen form: the valid keys (and, for
+      self-attention, the valid queries) are packed and padding is never
+      computed.  Output rows of padded queries are 0.
+    * Any other mask (bool or float, broadcastable to ``[B, H, Nq, Nkv]``)
+      becomes the kernel's additive bias (bool: True -> 0, False -> -inf).
+    * ``is_causal`` follows SDPA's top-left diagonal, which equals the
+      kernel's end-aligned one only when Nq == Nkv; other shapes are refused.
+    Rows that see no key are 0 (SDPA gives NaN there).  ``out_dtype``
+    (default: the input dtype) may be ``torch.float32``.
+    """
+    import torch
+    if dropout_p != 0.0:
+        raise MiAttnError(ERR_UNSUPPORTED, "dropout is not supported")
+    for name, t in (("query", query), ("key", key), ("value", value)):
+        if t.dim() != 4 or not t.is_cuda:
+            raise MiAttnError(ERR_INVALID_ARG, f"{name} must be a [B, H, N, D] device tensor")
+    bsz, hq, nq, d = query.shape
+    _, hkv, nkv, _ = key.shape
+    dv = value.shape[3]
+    if key.shape[0] != bsz or tuple(value.shape[:3]) != (bsz, hkv, nkv):
+        raise MiAttnError(ERR_INVALID_ARG, "query / key / value shapes do not match")
+    if hq != hkv and not enable_gqa:
+        raise MiAttnError(ERR_INVALID_ARG, "key / value have fewer heads: pass enable_gqa=True")
+    if is_causal and nq != nkv:
+        raise MiAttnError(ERR_UNSUPPORTED, "is_causal with Nq != Nkv (top-left diagonal) is not "
+                                           "the kernel's end-aligned rule")
+    if is_causal and attn_mask is not None and _key_padding_of(attn_mask, bsz, nkv) is None:
+        raise MiAttnError(ERR_INVALID_ARG, "is_causal together with a general attn_mask")
+    if torch.is_grad_enabled() and any(t.requires_grad for t in (query, key, value)):
+        raise MiAttnError(ERR_UNSUPPORTED, "sdpa is forward only; use varlen_attention for "
+                                           "gradients")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s_obj = _stream_of(stream, query.device)
+    dev = query.device
+    with torch.cuda.stream(s_obj):
+        # token-major views [B, N, H, D] of the head-major inputs: no copy
+        qv, kv_, vv = query.transpose(1, 2), key.transpose(1, 2), value.transpose(1, 2)
+        out_dtype = query.dtype if out_dtype is None else out_dtype
+        out = torch.empty(bsz, hq, nq, dv, dtype=out_dtype, device=dev)
+        ov = out.transpose(1, 2)
+        keymask = _key_padding_of(attn_mask, bsz, nkv)
+        if keymask is not None:
+            rk, cu_k, tot_k, max_k = padding_to_varlen(keymask, stream=s_obj)
+            if nq == nkv:
+                rq, cu_q, tot_q, max_q = rk, cu_k, tot_k, max_k
+            else:
+                rq, cu_q, tot_q, max_q = None, None, bsz * nq, nq
+            bias = None
+        else:
+            rk = rq = None
+            cu_k = torch.arange(0, bsz + 1, dtype=torch.int32, device=dev) * nkv
+            cu_q = torch.arange(0, bsz + 1, dtype=torch.int32, device=dev) * nq
+            tot_k, tot_q, max_q = bsz * nkv, bsz * nq, nq
+            bias = None
+            if attn_mask is not None:
+                m = attn_mask
+                while m.dim() < 4:
+                    m = m.unsqueeze(0)
+                if m.dim() != 4 or m.shape[1] not in (1, hq):
+                    raise MiAttnError(ERR_INVALID_ARG, "attn_mask must broadcast to [B, H or 1, "
+                                                       "Nq, Nkv]")
+                m = m.expand(bsz, m.shape[1], nq, nkv)
+                if m.dtype == torch.bool:
+                    bias = torch.zeros(m.shape, dtype=torch.float32, device=dev).masked_fill_(
+                        ~m, float("-inf"))
+                else:
+                    bias = m.to(torch.float32)
+                # [B, Hb, Nq, Nkv] -> rows of global query tokens [B * Nq, Hb, Nkv]
+                bias = bias.permute(0, 2, 1, 3).reshape(bsz * nq, m.shape[1], nkv)
+        pq = pack_tokens(qv, rq, cu_q, tot_q, stream=s_obj)
+        pk = pack_tokens(kv_, rk, cu_k, tot_k, stream=s_obj)
+        pv = pack_tokens(vv, rk, cu_k, tot_k, stream=s_obj)
+        if cu_q is None:
+            cu_q = torch.arange(0, bsz + 1, dtype=torch.int32, device=dev) * nq
+        po = varlen_attention(pq, pk, pv, cu_q, cu_k, max_q, scale=scale, causal=is_causal,
+                              attn_bias=bias, out_dtype=out_dtype, stream=s_obj)
+        unpack_tokens(po, ov, rq, cu_q, stream=s_obj)
+    return out

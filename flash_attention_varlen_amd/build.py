@@ -26,7 +26,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wall", "-Wno-pass-failed", "-Wno-unused-function",
          "-Wno-cuda-compat", "-I", INCLUDE, "-I", CSRC]
 # Sources compiled once each.
-PLAIN = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "bias_ranges.hip", "mi_attn.cpp"]
+PLAIN = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "bias_ranges.hip", "padding.hip", "mi_attn.cpp"]
 
 
 def hipcc() -> str:

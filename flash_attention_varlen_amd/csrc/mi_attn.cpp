@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdarg>
@@ -15,12 +16,14 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "attn_bwd.h"
 #include "attn_decode.h"
 #include "attn_fwd.h"
 #include "bias_ranges.h"
+#include "padding.h"
 
 namespace {
 
@@ -86,6 +89,20 @@ bool layout_disjoint(int64_t st, int64_t n_tok, int64_t sh, int64_t n_head, int6
   const int64_t s_in = tok_inner ? st : sh, n_in = tok_inner ? n_tok : n_head;
   const int64_t s_out = tok_inner ? sh : st;
   return s_in >= width && s_out >= s_in * (n_in - 1) + width;
+}
+
+// Rows of `width` bytes at sum_i idx_i * st[i] (0 <= idx_i < n[i]) never
+// overlap: taken by increasing stride, each stride clears the extent of the
+// levels inside it (sufficient, the usual nesting of a strided view).
+bool nested_disjoint(std::vector<std::pair<int64_t, int64_t>> lv, int64_t width) {
+  std::sort(lv.begin(), lv.end());
+  int64_t extent = width;
+  for (const auto& l : lv) {
+    if (l.second <= 1) continue;
+    if (l.first < extent) return false;
+    extent = l.first * (l.second - 1) + extent;
+  }
+  return true;
 }
 
 int validate_cu(const int32_t* cu_dev, int64_t n, int64_t total, int64_t max_len,
@@ -617,6 +634,109 @@ int mi_attn_varlen_decode_noalloc(const mi_attn_fwd_params* p_in, int64_t max_se
   rc = scratch_address(&ws);
   if (rc != MI_ATTN_OK) return rc;
   return launch_decode(&local, plan, ws, stream);
+}
+
+int mi_attn_padding_to_varlen(const uint8_t* mask, int64_t batch, int64_t seqlen,
+                              int64_t mask_stride_batch, int32_t* ranks, int32_t* cu_seqlens,
+                              int32_t* stats, void* stream) {
+  g_last_error.clear();
+  if (batch < 0 || seqlen < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "negative size");
+  if (batch >= INT32_MAX || seqlen > INT32_MAX || batch * seqlen > INT32_MAX)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "batch * seqlen must fit in int32 (cu_seqlens)");
+  if (cu_seqlens == nullptr) return fail(MI_ATTN_ERR_INVALID_ARG, "cu_seqlens is required");
+  const bool any = batch * seqlen > 0;
+  if (any && (mask == nullptr || ranks == nullptr))
+    return fail(MI_ATTN_ERR_INVALID_ARG, "mask and ranks are required");
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(ranks) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(stats) & 3u) != 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "ranks, cu_seqlens and stats must be 4-byte aligned");
+  if (mask_stride_batch < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "negative mask stride");
+  mi_attn::PadRankArgs a{};
+  a.mask = mask;
+  a.mask_st = mask_stride_batch;
+  a.ranks = ranks;
+  a.cu = cu_seqlens;
+  a.stats = stats;
+  a.batch = (int32_t)batch;
+  a.seqlen = (int32_t)seqlen;
+  hipError_t e = mi_attn::launch_padding_ranks(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return MI_ATTN_OK;
+}
+
+namespace {
+
+int pack_common(const mi_attn_pack_params* p_in, int unpack, void* stream) {
+  g_last_error.clear();
+  if (p_in == nullptr) return fail(MI_ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (p_in->struct_size < sizeof(mi_attn_pack_params))
+    return fail(MI_ATTN_ERR_INVALID_ARG, "struct_size %zu < %zu (not an mi_attn_pack_params)",
+                p_in->struct_size, sizeof(mi_attn_pack_params));
+  const mi_attn_pack_params& p = *p_in;
+  if (p.elem_bytes != 2 && p.elem_bytes != 4)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "elem_bytes must be 2 or 4 (got %d)", p.elem_bytes);
+  if (p.batch < 0 || p.seqlen < 0 || p.heads <= 0 || p.dim <= 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "sizes must be >= 0 (heads, dim > 0)");
+  if (p.batch * p.seqlen > INT32_MAX || p.seqlen > INT32_MAX)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "batch * seqlen must fit in int32");
+  const int64_t row_bytes = (int64_t)p.dim * p.elem_bytes;
+  if (row_bytes % 16 != 0)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "dim * elem_bytes must be a multiple of 16 bytes");
+  const int64_t chunks = (int64_t)p.heads * (row_bytes / 16);
+  if (chunks > INT32_MAX) return fail(MI_ATTN_ERR_UNSUPPORTED, "heads * dim too large");
+  const int64_t tokens = p.batch * p.seqlen;
+  if (tokens == 0) return MI_ATTN_OK;
+  if (p.padded == nullptr || p.packed == nullptr)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "padded and packed are required");
+  if (p.ranks != nullptr && p.cu_seqlens == nullptr)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "ranks need the cu_seqlens they were computed with");
+  if (!aligned16(p.padded) || !aligned16(p.packed))
+    return fail(MI_ATTN_ERR_INVALID_ARG, "padded and packed must be 16-byte aligned");
+  const int64_t mult = 16 / p.elem_bytes;
+  const int64_t strides[5] = {p.padded_stride_batch, p.padded_stride_tok, p.padded_stride_head,
+                              p.packed_stride_tok, p.packed_stride_head};
+  for (int64_t st : strides)
+    if (st < 0 || st % mult != 0)
+      return fail(MI_ATTN_ERR_INVALID_ARG,
+                  "strides must be non-negative multiples of %lld elements", (long long)mult);
+  const int64_t eb = p.elem_bytes;
+  // the side that is written must not overlap itself
+  const bool ok = unpack
+      ? nested_disjoint({{p.padded_stride_batch * eb, p.batch}, {p.padded_stride_tok * eb, p.seqlen},
+                         {p.padded_stride_head * eb, p.heads}}, row_bytes)
+      : nested_disjoint({{p.packed_stride_tok * eb, tokens}, {p.packed_stride_head * eb, p.heads}},
+                        row_bytes);
+  if (!ok)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "the %s strides make its rows overlap",
+                unpack ? "padded" : "packed");
+  mi_attn::PackArgs a{};
+  a.padded = reinterpret_cast<char*>(p.padded);
+  a.packed = reinterpret_cast<char*>(p.packed);
+  a.ranks = p.ranks;
+  a.cu = p.cu_seqlens;
+  a.pd_sb = p.padded_stride_batch * eb;
+  a.pd_st = p.padded_stride_tok * eb;
+  a.pd_sh = p.padded_stride_head * eb;
+  a.pk_st = p.packed_stride_tok * eb;
+  a.pk_sh = p.packed_stride_head * eb;
+  a.seqlen = (int32_t)p.seqlen;
+  a.tokens = (int32_t)tokens;
+  a.chunks = (int32_t)chunks;
+  a.row_chunks = (int32_t)(row_bytes / 16);
+  a.tok_per_wg = chunks >= 256 ? 1 : (int32_t)(256 / chunks);
+  a.unpack = unpack;
+  hipError_t e = mi_attn::launch_pack_tokens(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return MI_ATTN_OK;
+}
+
+}  // namespace
+
+int mi_attn_pack_tokens(const mi_attn_pack_params* p, void* stream) { return pack_common(p, 0, stream); }
+
+int mi_attn_unpack_tokens(const mi_attn_pack_params* p, void* stream) {
+  return pack_common(p, 1, stream);
 }
 
 int mi_attn_bias_key_ranges(const mi_attn_fwd_params* p_in, int32_t* ranges, void* stream) {

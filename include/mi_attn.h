@@ -184,6 +184,58 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream);
 int mi_attn_bias_key_ranges(const mi_attn_fwd_params* p, int32_t* ranges, void* stream);
 
 /*
+ * Key-padding front end (added in version 1.5).  The mtlattn 0.3.0 page
+ * (section "Drop-in for scaled_dot_product_attention") turns a
+ * self-attention key-padding mask into varlen form: the valid tokens are
+ * packed and the padding is never computed.  Packing keeps the order of a
+ * row's valid tokens, so causal visibility between valid tokens is the same
+ * before and after.
+ *
+ * mi_attn_padding_to_varlen: mask is uint8 [batch, seqlen] (nonzero = valid
+ * token; row b at mask + b * mask_stride_batch bytes, tokens contiguous).
+ * Writes ranks, int32 [batch * seqlen]: the rank of token (b, n) among row
+ * b's valid tokens, -1 for padding; cu_seqlens, int32 [batch + 1], the
+ * cumulative valid counts (cu_seqlens[0] = 0); and, if stats is not NULL,
+ * stats[0] = total valid tokens, stats[1] = the longest row (what a forward
+ * call needs as total_q and max_seqlen_q; reading them on the host means a
+ * synchronisation the caller chooses).  batch * seqlen must fit in int32.
+ * All buffers are device memory owned by the caller; int32 outputs 4-byte
+ * aligned.  Asynchronous on `stream`.
+ */
+int mi_attn_padding_to_varlen(const uint8_t* mask, int64_t batch, int64_t seqlen,
+                              int64_t mask_stride_batch, int32_t* ranks, int32_t* cu_seqlens,
+                              int32_t* stats, void* stream);
+
+/*
+ * Gather (mi_attn_pack_tokens) the valid tokens of a padded view
+ * [batch, seqlen, heads, dim] into packed rows [total, heads, dim], or
+ * scatter (mi_attn_unpack_tokens) packed rows back into the padded view,
+ * writing zeros at padding.  Valid token (b, n) is packed row
+ * cu_seqlens[b] + ranks[b * seqlen + n] (arrays from
+ * mi_attn_padding_to_varlen); with ranks = NULL every token is valid and
+ * its packed row is b * seqlen + n.  Pure data movement: bit-exact copies of
+ * elem_bytes-wide elements (2 or 4), dim * elem_bytes a multiple of 16,
+ * pointers 16-byte aligned, strides in elements and multiples of
+ * 16 / elem_bytes, last dim contiguous; the written side's rows must not
+ * overlap.  Set struct_size = sizeof(mi_attn_pack_params).
+ */
+typedef struct mi_attn_pack_params {
+  size_t struct_size;
+  void* padded;             /* read by pack, written by unpack */
+  void* packed;             /* written by pack, read by unpack */
+  const int32_t* ranks;     /* [batch * seqlen] or NULL (all valid) */
+  const int32_t* cu_seqlens; /* [batch + 1]; required with ranks */
+  int64_t batch, seqlen;
+  int32_t heads, dim;
+  int32_t elem_bytes;
+  int64_t padded_stride_batch, padded_stride_tok, padded_stride_head;
+  int64_t packed_stride_tok, packed_stride_head;
+} mi_attn_pack_params;
+
+int mi_attn_pack_tokens(const mi_attn_pack_params* p, void* stream);
+int mi_attn_unpack_tokens(const mi_attn_pack_params* p, void* stream);
+
+/*
  * Backward of the forward above: the gradients dq, dk, dv of a loss with
  * respect to q, k, v, given its gradient dout with respect to out (the LSE
  * output is not differentiated).  From the forward's definition, with p the

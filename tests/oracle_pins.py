@@ -466,9 +466,90 @@ def pin_backward_closed_forms():
         _close(dk[cu_kv[s]:cu_kv[s + 1]].sum(axis=0), np.zeros(dk.shape[1:]), 1e-12)
 
 
+# ---------------------------------------------------------------- key-padding front end
+PAD_MASK = np.array([[1, 1, 0, 1], [0, 0, 0, 0], [0, 1, 1, 1]], dtype=bool)
+
+
+def pin_padding_hand_worked():
+    """Ranks, cumulative counts and the gather / scatter on a 3 x 4 mask
+    worked by hand: row 0 keeps tokens 0, 1, 3; row 1 is all padding; row 2
+    keeps 1, 2, 3."""
+    ranks, cu, stats = oracle.padding_to_varlen(PAD_MASK)
+    assert ranks.tolist() == [[0, 1, -1, 2], [-1, -1, -1, -1], [-1, 0, 1, 2]], ranks
+    assert cu.tolist() == [0, 3, 3, 6], cu
+    assert stats == (6, 3), stats
+    padded = (10.0 * np.arange(3)[:, None] + np.arange(4)[None, :])[:, :, None, None] + \
+        np.array([0.0, 0.5])[None, None, :, None]  # [3, 4, 2 heads, 1]
+    packed = oracle.pack_tokens(padded, PAD_MASK)
+    assert packed[:, 0, 0].tolist() == [0.0, 1.0, 3.0, 21.0, 22.0, 23.0], packed[:, 0, 0]
+    assert packed[:, 1, 0].tolist() == [0.5, 1.5, 3.5, 21.5, 22.5, 23.5]
+    back = oracle.unpack_tokens(packed, PAD_MASK)
+    assert np.array_equal(back, np.where(PAD_MASK[:, :, None, None], padded, 0.0))
+    # all valid: ranks are the positions, cu the multiples of the row length
+    r2, cu2, st2 = oracle.padding_to_varlen(np.ones((2, 5), dtype=bool))
+    assert r2.tolist() == [list(range(5))] * 2 and cu2.tolist() == [0, 5, 10] and st2 == (10, 5)
+
+
+def _padded_case(rng, bsz=3, n=9, hq=4, hkv=2, d=8, dv=6):
+    mask = rng.random((bsz, n)) < 0.6
+    mask[0] = True           # a full row
+    mask[1, :] = False       # an empty row
+    mask[1, [2, 7]] = True   # ... with two valid tokens far apart
+    mask[2, 0] = False       # left padding
+    q = rng.standard_normal((bsz, hq, n, d))
+    k = rng.standard_normal((bsz, hkv, n, d))
+    v = rng.standard_normal((bsz, hkv, n, dv))
+    return mask, q, k, v
+
+
+def pin_masked_attention_sdpa():
+    """The dense key-padding definition against torch's float64 CPU SDPA with
+    a boolean mask: on valid rows that see a key they agree; padded rows are
+    0 by definition."""
+    import torch.nn.functional as F
+    rng = np.random.default_rng(123)
+    for causal in (False, True):
+        mask, q, k, v = _padded_case(rng)
+        bsz, hq, n, d = q.shape
+        out = oracle.masked_attention(q, k, v, mask, 1.0 / math.sqrt(d), causal)
+        am = torch.from_numpy(mask)[:, None, None, :].expand(bsz, 1, n, n)
+        if causal:
+            am = am & torch.tril(torch.ones(n, n, dtype=torch.bool))
+        rep = hq // k.shape[1]
+        tk = torch.from_numpy(np.repeat(k, rep, axis=1))
+        tv = torch.from_numpy(np.repeat(v, rep, axis=1))
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q), tk, tv, attn_mask=am).numpy()
+        sees = am[:, 0].any(dim=-1).numpy() & mask  # [B, N]
+        for b in range(bsz):
+            for i in range(n):
+                if sees[b, i]:
+                    _close(out[b, :, i], ref[b, :, i], 1e-12)
+                else:
+                    assert np.all(out[b, :, i] == 0.0)
+
+
+def pin_packed_matches_masked():
+    """Packing, varlen attention on the packed rows and unpacking gives the
+    dense key-padding result: causal visibility survives packing because the
+    valid tokens keep their order."""
+    rng = np.random.default_rng(321)
+    for causal in (False, True):
+        mask, q, k, v = _padded_case(rng)
+        d = q.shape[3]
+        _, cu, _ = oracle.padding_to_varlen(mask)
+        pq = oracle.pack_tokens(q.transpose(0, 2, 1, 3), mask)
+        pk = oracle.pack_tokens(k.transpose(0, 2, 1, 3), mask)
+        pv = oracle.pack_tokens(v.transpose(0, 2, 1, 3), mask)
+        out, _ = oracle.varlen_attention(pq, pk, pv, cu, cu, 1.0 / math.sqrt(d), causal, 0, None)
+        dense = oracle.unpack_tokens(out, mask).transpose(0, 2, 1, 3)
+        ref = oracle.masked_attention(q, k, v, mask, 1.0 / math.sqrt(d), causal)
+        _close(dense, ref, 1e-12)
+
+
 ALL_PINS = [pin_brute_force_tiny, pin_sdpa_special_case, pin_rows_sum_to_one,
             pin_one_key_sequence, pin_zero_queries_mean, pin_key_permutation_invariance,
             pin_neg_inf_key_is_removed, pin_mask_counts_closed_form, pin_golden_hand_worked,
             pin_row_subset_matches_full, pin_bias_ranges_prefix_lm_closed_form,
             pin_bias_ranges_skip_is_exact, pin_backward_finite_differences,
-            pin_backward_sdpa_special_case, pin_backward_closed_forms]
+            pin_backward_sdpa_special_case, pin_backward_closed_forms, pin_padding_hand_worked,
+            pin_masked_attention_sdpa, pin_packed_matches_masked]

@@ -24,7 +24,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == ["mi_attn_bias_key_ranges", "mi_attn_decode_workspace_size", "mi_attn_last_error",
-                     "mi_attn_tile_shape", "mi_attn_varlen_bwd", "mi_attn_varlen_decode",
+                     "mi_attn_pack_tokens", "mi_attn_padding_to_varlen", "mi_attn_tile_shape",
+                     "mi_attn_unpack_tokens", "mi_attn_varlen_bwd", "mi_attn_varlen_decode",
                      "mi_attn_varlen_decode_noalloc", "mi_attn_varlen_fwd", "mi_attn_version"]
     lib = fav.load_library()
     for n in names:
@@ -49,7 +50,8 @@ def test_version_and_tile_shape():
 
 
 @pytest.mark.parametrize("cls,cname", [(fav.MiAttnFwdParams, "mi_attn_fwd_params"),
-                                       (fav.MiAttnBwdParams, "mi_attn_bwd_params")])
+                                       (fav.MiAttnBwdParams, "mi_attn_bwd_params"),
+                                       (fav.MiAttnPackParams, "mi_attn_pack_params")])
 def test_struct_layout_matches_header(cls, cname):
     fields = [f[0] for f in cls._fields_]
     src = "#include <stdio.h>\n#include <stddef.h>\n#include \"mi_attn.h\"\nint main(void){\n"
@@ -277,3 +279,86 @@ def test_decode_workspace_size_and_short_workspace():
     with pytest.raises(fav.MiAttnError) as ei:
         fav.mi_attn_varlen_decode(p, 4096, 8, 1 << 20, n - 1, 0)
     assert ei.value.code == fav.ERR_INVALID_ARG and "workspace" in fav.mi_attn_last_error()
+
+
+# ---------------------------------------------------------------- key-padding front end
+def _valid_pack():
+    p = fav.MiAttnPackParams()
+    fake = 1 << 20
+    p.padded = p.packed = p.ranks = p.cu_seqlens = fake
+    p.batch, p.seqlen, p.heads, p.dim, p.elem_bytes = 2, 10, 4, 64, 2
+    p.padded_stride_batch, p.padded_stride_tok, p.padded_stride_head = 4 * 10 * 64, 64, 10 * 64
+    p.packed_stride_tok, p.packed_stride_head = 4 * 64, 64
+    return p
+
+
+PACK_REFUSALS = {
+    "elem_bytes": (dict(elem_bytes=1), fav.ERR_UNSUPPORTED, "both"),
+    "row_not_16_bytes": (dict(dim=12), fav.ERR_UNSUPPORTED, "both"),
+    "zero_heads": (dict(heads=0), fav.ERR_INVALID_ARG, "both"),
+    "negative_batch": (dict(batch=-1), fav.ERR_INVALID_ARG, "both"),
+    "huge": (dict(batch=1 << 20, seqlen=1 << 12), fav.ERR_UNSUPPORTED, "both"),
+    "null_packed": (dict(packed=None), fav.ERR_INVALID_ARG, "both"),
+    "ranks_without_cu": (dict(cu_seqlens=None), fav.ERR_INVALID_ARG, "both"),
+    "misaligned": (dict(padded=(1 << 20) + 8), fav.ERR_INVALID_ARG, "both"),
+    "odd_stride": (dict(packed_stride_tok=4 * 64 + 4), fav.ERR_INVALID_ARG, "both"),
+    # the written side must not overlap itself
+    "packed_rows_overlap": (dict(packed_stride_tok=64), fav.ERR_UNSUPPORTED, "pack"),
+    "padded_rows_overlap": (dict(padded_stride_batch=64), fav.ERR_UNSUPPORTED, "unpack"),
+}
+
+
+@pytest.mark.parametrize("direction", ["pack", "unpack"])
+@pytest.mark.parametrize("name", sorted(PACK_REFUSALS))
+def test_pack_host_validation_refuses(name, direction):
+    changes, code, which = PACK_REFUSALS[name]
+    if which not in ("both", direction):
+        pytest.skip("checked for the other direction")
+    p = _valid_pack()
+    for k, v in changes.items():
+        setattr(p, k, v)
+    fn = fav.mi_attn_pack_tokens if direction == "pack" else fav.mi_attn_unpack_tokens
+    with pytest.raises(fav.MiAttnError) as ei:
+        fn(p, 0)
+    assert ei.value.code == code, fav.mi_attn_last_error()
+
+
+def test_empty_pack_is_a_no_op():
+    """No tokens: OK before any pointer is used."""
+    p = _valid_pack()
+    p.batch = 0
+    p.padded = p.packed = None
+    fav.mi_attn_pack_tokens(p, 0)
+    fav.mi_attn_unpack_tokens(p, 0)
+
+
+def test_short_pack_struct_is_refused():
+    p = _valid_pack()
+    p.struct_size = 8
+    lib = fav.load_library()
+    f = lib.mi_attn_pack_tokens
+    f.argtypes = [ctypes.POINTER(fav.MiAttnPackParams), ctypes.c_void_p]
+    assert f(ctypes.byref(p), None) == fav.ERR_INVALID_ARG
+
+
+PADDING_REFUSALS = {
+    "negative": (dict(batch=-1), fav.ERR_INVALID_ARG),
+    "too_many_tokens": (dict(batch=1 << 16, seqlen=1 << 16), fav.ERR_UNSUPPORTED),
+    "null_cu": (dict(cu=0), fav.ERR_INVALID_ARG),
+    "null_mask": (dict(mask=0), fav.ERR_INVALID_ARG),
+    "null_ranks": (dict(ranks=0), fav.ERR_INVALID_ARG),
+    "misaligned_ranks": (dict(ranks=(1 << 20) + 2), fav.ERR_INVALID_ARG),
+    "negative_stride": (dict(stride=-1), fav.ERR_INVALID_ARG),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PADDING_REFUSALS))
+def test_padding_to_varlen_refuses(name):
+    args = dict(mask=1 << 20, batch=2, seqlen=10, stride=10, ranks=1 << 20, cu=1 << 20,
+                stats=0)
+    changes, code = PADDING_REFUSALS[name]
+    args.update(changes)
+    with pytest.raises(fav.MiAttnError) as ei:
+        fav.mi_attn_padding_to_varlen(args["mask"], args["batch"], args["seqlen"], args["stride"],
+                                      args["ranks"], args["cu"], args["stats"], 0)
+    assert ei.value.code == code, fav.mi_attn_last_error()

@@ -12,7 +12,7 @@ import types
 import pytest
 
 import oracle
-from oracle import ref_attention, ref_backward, ref_masks
+from oracle import ref_attention, ref_backward, ref_masks, ref_padding
 from oracle_pins import ALL_PINS
 
 MUTATIONS = {
@@ -59,8 +59,23 @@ BACKWARD_MUTATIONS = {
     "bwd_mask_dropped": ("p, m, l = softmax_rows(z, mask)", "p, m, l = softmax_rows(z, mask | True)"),
 }
 
+# mutations of the key-padding oracle (oracle/ref_padding.py)
+PADDING_MUTATIONS = {
+    "pad_rank_from_one": ("                ranks[r, t] = c\n", "                ranks[r, t] = c + 1\n"),
+    "pad_cu_counts_not_summed": ("cu[1:] = np.cumsum(counts)", "cu[1:] = counts"),
+    "pad_longest_is_total": ("int(counts.max(initial=0))", "int(counts.sum())"),
+    "pad_pack_keeps_padding": ("if mask[b, t]]", "if mask[b, t] or t == 0]"),
+    "pad_unpack_shifted": ("                out[b, t] = packed[i]\n                i += 1",
+                           "                i += 1\n                out[b, t] = packed[i - 1 if t else i % len(packed)]"),
+    "pad_query_mask_ignored": ("seen = np.isfinite(m[:, 0]) & mask[b]", "seen = np.isfinite(m[:, 0])"),
+    "pad_key_mask_ignored": ("vis = np.broadcast_to(mask[b][None, :], (n, n))",
+                             "vis = np.ones((n, n), dtype=bool)"),
+    "pad_causal_flipped": ("vis = vis & (j <= i)", "vis = vis & (j >= i)"),
+    "pad_kv_head_modulo": ("g = h // (hq // hkv)", "g = h % hkv"),
+}
+
 SOURCES = {"attention": inspect.getsource(ref_attention), "masks": inspect.getsource(ref_masks),
-           "backward": inspect.getsource(ref_backward)}
+           "backward": inspect.getsource(ref_backward), "padding": inspect.getsource(ref_padding)}
 
 
 def _mutant(module_key, old, new):
@@ -74,7 +89,8 @@ def _mutant(module_key, old, new):
 
 ALL_MUTATIONS = {**{("attention", k): v for k, v in MUTATIONS.items()},
                  **{("masks", k): v for k, v in MASK_MUTATIONS.items()},
-                 **{("backward", k): v for k, v in BACKWARD_MUTATIONS.items()}}
+                 **{("backward", k): v for k, v in BACKWARD_MUTATIONS.items()},
+                 **{("padding", k): v for k, v in PADDING_MUTATIONS.items()}}
 
 
 @pytest.mark.parametrize("key", sorted(ALL_MUTATIONS), ids=lambda k: f"{k[0]}-{k[1]}")
