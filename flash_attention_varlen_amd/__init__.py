@@ -65,6 +65,7 @@ class MiAttnFwdParams(ctypes.Structure):
         ("q_rope", ctypes.c_void_p), ("k_rope", ctypes.c_void_p),
         ("q_rope_stride_tok", ctypes.c_int64), ("q_rope_stride_head", ctypes.c_int64),
         ("k_rope_stride_tok", ctypes.c_int64), ("k_rope_stride_head", ctypes.c_int64),
+        ("alibi_slopes", ctypes.c_void_p), ("alibi_stride_seq", ctypes.c_int64),
     ]
 
 
@@ -94,6 +95,7 @@ class MiAttnBwdParams(ctypes.Structure):
         ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
         ("bias", ctypes.c_void_p), ("bias_heads", ctypes.c_int32), ("bias_cols", ctypes.c_int64),
         ("bias_stride_tok", ctypes.c_int64), ("bias_stride_head", ctypes.c_int64),
+        ("alibi_slopes", ctypes.c_void_p), ("alibi_stride_seq", ctypes.c_int64),
     ]
 
 
@@ -208,7 +210,7 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
                      scale: Optional[float] = None, causal: bool = False, window: int = 0,
                      attn_bias=None, out_dtype=None, return_lse: bool = False, out=None,
                      lse=None, tile_counts=None, stream=None, bias_ranges=None,
-                     max_seqlen_kv=None, q_rope=None, k_rope=None):
+                     max_seqlen_kv=None, q_rope=None, k_rope=None, alibi_slopes=None):
     """Fused varlen attention forward.  Returns ``out`` or ``(out, lse)``.
 
     q ``[Tq, Hq, Dqk]``, k ``[Tk, Hkv, Dqk]``, v ``[Tk, Hkv, Dv]`` (device,
@@ -234,6 +236,10 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     ``[Tk, Hkv, 64]`` (bf16 / fp16, ``v`` 128 wide), q and k are the 128-wide
     nope parts and the scores are ``q.k + q_rope.k_rope``, as for one call on
     the concatenations, without forming them (forward only).
+
+    ``alibi_slopes`` (fp32 ``[Hq]`` or ``[num_seqs, Hq]``, device): the
+    kernels add ``-slope * |i + (Lk - Lq) - j|`` to the logit of query row i
+    and key j (no bias tensor with it); differentiable like a bias.
     """
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -264,6 +270,15 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
         if torch.is_grad_enabled() and any(t.requires_grad for t in (q, k, v, q_rope, k_rope)):
             raise MiAttnError(ERR_UNSUPPORTED, "split q_rope / k_rope operands are forward only")
         dqk = dqk + 64  # the contraction width
+    if alibi_slopes is not None:
+        nseq = cu_seqlens_q.numel() - 1
+        if (alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_cuda
+                or alibi_slopes.stride(-1) != 1
+                or tuple(alibi_slopes.shape) not in ((hq,), (nseq, hq))):
+            raise MiAttnError(ERR_INVALID_ARG, "alibi_slopes must be fp32 [Hq] or [num_seqs, Hq] "
+                                               "on the device, last dim contiguous")
+        if attn_bias is not None:
+            raise MiAttnError(ERR_UNSUPPORTED, "alibi_slopes and attn_bias together")
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
@@ -281,7 +296,8 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
         s_obj = _stream_of(stream, q.device)
         with torch.cuda.stream(s_obj):
             o, l = _differentiable_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
-                                             max_seqlen_kv, scale, causal, window, attn_bias)
+                                             max_seqlen_kv, scale, causal, window, attn_bias,
+                                             alibi_slopes)
         return (o, l) if return_lse else o
     s_obj = _stream_of(stream, q.device)
     if bias_ranges is not None:
@@ -294,7 +310,8 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
         return _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
                                            scale, causal, window, attn_bias, out_dtype,
                                            return_lse, out, lse, tile_counts, s_obj, tq, hq, dqk,
-                                           tk, hkv, dv, bias_ranges, q_rope, k_rope)
+                                           tk, hkv, dv, bias_ranges, q_rope, k_rope,
+                                           alibi_slopes)
 
 
 def _stream_of(stream, device):
@@ -359,7 +376,7 @@ def _aligned_bias(bias):
 def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, scale, causal,
                                 window, attn_bias, out_dtype, return_lse, out, lse, tile_counts,
                                 s_obj, tq, hq, dqk, tk, hkv, dv, bias_ranges=None, q_rope=None,
-                                k_rope=None):
+                                k_rope=None, alibi_slopes=None):
     import torch
     bias = attn_bias
     if bias is not None:
@@ -391,6 +408,9 @@ def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen
         p.q_rope, p.k_rope = q_rope.data_ptr(), k_rope.data_ptr()
         p.q_rope_stride_tok, p.q_rope_stride_head = q_rope.stride(0), q_rope.stride(1)
         p.k_rope_stride_tok, p.k_rope_stride_head = k_rope.stride(0), k_rope.stride(1)
+    if alibi_slopes is not None:
+        p.alibi_slopes = alibi_slopes.data_ptr()
+        p.alibi_stride_seq = alibi_slopes.stride(0) if alibi_slopes.dim() == 2 else 0
     p.tile_counts = tile_counts.data_ptr() if tile_counts is not None else None
     p.num_seqs = cu_seqlens_q.numel() - 1
     p.max_seqlen_q = int(max_seqlen_q)
@@ -417,7 +437,7 @@ def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen
 def varlen_attention_backward(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_kv,
                               max_seqlen_q: int, max_seqlen_kv: int, scale: Optional[float] = None,
                               causal: bool = False, window: int = 0, dq=None, dk=None, dv=None,
-                              grad_dtype=None, attn_bias=None, stream=None):
+                              grad_dtype=None, attn_bias=None, stream=None, alibi_slopes=None):
     """Gradients ``(dq, dk, dv)`` of the forward from its inputs, its output
     ``out`` and ``lse`` and the output gradient ``dout`` (bf16 / fp16,
     head dims 64 or 128; ``attn_bias``, the forward's additive bias, enters as
@@ -462,6 +482,9 @@ def varlen_attention_backward(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_
             p.bias = bias.data_ptr()
             p.bias_heads, p.bias_cols = bias.shape[1], bias.shape[2]
             p.bias_stride_tok, p.bias_stride_head = bias.stride(0), bias.stride(1)
+        if alibi_slopes is not None:
+            p.alibi_slopes = alibi_slopes.data_ptr()
+            p.alibi_stride_seq = alibi_slopes.stride(0) if alibi_slopes.dim() == 2 else 0
         p.in_dtype = _dtype_code(q.dtype)
         p.grad_dtype = _dtype_code(gdt)
         p.scale = float(scale)
@@ -480,14 +503,16 @@ def _autograd_fn():
 
         @staticmethod
         def forward(ctx, q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, scale,
-                    causal, window, bias):
+                    causal, window, bias, alibi):
             with torch.no_grad():
                 if bias is not None:
                     bias = _aligned_bias(bias)  # one fp32 layout for both passes
                 out, lse = varlen_attention(q.detach(), k.detach(), v.detach(), cu_seqlens_q,
                                             cu_seqlens_kv, max_seqlen_q, scale=scale, causal=causal,
-                                            window=window, attn_bias=bias, return_lse=True)
+                                            window=window, attn_bias=bias, return_lse=True,
+                                            alibi_slopes=alibi)
             ctx.bias = bias
+            ctx.alibi = alibi
             ctx.save_for_backward(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv)
             ctx.args = (max_seqlen_q, max_seqlen_kv, scale, causal, window)
             ctx.mark_non_differentiable(lse)
@@ -499,8 +524,9 @@ def _autograd_fn():
             max_seqlen_q, max_seqlen_kv, scale, causal, window = ctx.args
             dq, dk, dv = varlen_attention_backward(q, k, v, out, lse, dout.contiguous(), cq, ck,
                                                    max_seqlen_q, max_seqlen_kv, scale, causal,
-                                                   window, attn_bias=ctx.bias)
-            return dq, dk, dv, None, None, None, None, None, None, None, None
+                                                   window, attn_bias=ctx.bias,
+                                                   alibi_slopes=ctx.alibi)
+            return dq, dk, dv, None, None, None, None, None, None, None, None, None
 
     return VarlenAttentionFn
 
@@ -509,7 +535,7 @@ _FN = None
 
 
 def _differentiable_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
-                              scale, causal, window, bias=None):
+                              scale, causal, window, bias=None, alibi=None):
     global _FN
     if _FN is None:
         _FN = _autograd_fn()
@@ -517,7 +543,7 @@ def _differentiable_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q
         max_seqlen_kv = int((cu_seqlens_kv[1:] - cu_seqlens_kv[:-1]).max().item()) \
             if cu_seqlens_kv.numel() > 1 else 0
     return _FN.apply(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, scale,
-                     causal, window, bias)
+                     causal, window, bias, alibi)
 
 
 # ---------------------------------------------------------------- split-KV decode

@@ -37,6 +37,9 @@ struct BwdArgs {
   int64_t b_st, b_sh;
   int32_t bias_heads;  // 1 or hq
   int32_t bias_cols;   // keys at or past it read a bias of 0
+  // optional ALiBi slopes alibi[seq * alibi_ss + head] (no bias tensor then)
+  const float* alibi;
+  int64_t alibi_ss;
 };
 
 // The backward instances, one per (element type, head dim), compiled in

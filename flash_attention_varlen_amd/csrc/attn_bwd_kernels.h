@@ -79,7 +79,8 @@ __device__ __forceinline__ void store_grad4(T* p, float a, float b, float c, flo
 // ----------------------------------------------------------------------------
 // dkdv_kernel
 // ----------------------------------------------------------------------------
-template <typename T, int D, typename GradT, bool BIAS>
+// ALIBI: the bias is -slope * |query position - key|, computed (BIAS set too).
+template <typename T, int D, typename GradT, bool BIAS, bool ALIBI = false>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
   constexpr int BK = 128;              // keys per workgroup (32 per wave)
   constexpr int BQ = 64;               // query rows per step (two 32-row blocks)
@@ -193,9 +194,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
     const int h = g * a.group + it % a.group;
     // bias column of this lane's key (keys at or past the bias columns read 0)
     const float* bcol = nullptr;
-    const bool bkey = BIAS && my_key < min(lk, a.bias_cols);
-    if constexpr (BIAS)
+    const bool bkey = BIAS && !ALIBI && my_key < min(lk, a.bias_cols);
+    if constexpr (BIAS && !ALIBI)
       bcol = a.bias + (int64_t)(a.bias_heads == 1 ? 0 : h) * a.b_sh + (bkey ? my_key : 0);
+    const float neg_slope = ALIBI ? -a.alibi[(int64_t)seq * a.alibi_ss + h] : 0.0f;
     if (!wave_keys || q0 >= wq_hi || q0 + BQ <= wq_lo) return;  // no visible pair for this wave
     const lds_char* qt = (const lds_char*)(s == 0 ? qt_0 : qt_1);
     const lds_char* gt = (const lds_char*)(s == 0 ? gt_0 : gt_1);
@@ -226,7 +228,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
           if constexpr (BIAS) {
             // logit = scale s + bias, in log2 units
             const int row = q0 + r + i;
-            const float b = (bkey && row < lq) ? bcol[(int64_t)(cq0 + row) * a.b_st] : 0.0f;
+            float b;
+            if constexpr (ALIBI)
+              b = neg_slope * __builtin_fabsf((float)(row + off - my_key));
+            else
+              b = (bkey && row < lq) ? bcol[(int64_t)(cq0 + row) * a.b_st] : 0.0f;
             x = __builtin_fmaf(b, kLog2e, x);
           }
           float p = fast_exp2(x - l2[i]);
@@ -296,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
 // ----------------------------------------------------------------------------
 // dq_kernel
 // ----------------------------------------------------------------------------
-template <typename T, int D, typename GradT, bool BIAS>
+template <typename T, int D, typename GradT, bool BIAS, bool ALIBI = false>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdArgs a) {
   constexpr int BM = 128;              // query rows per workgroup (32 per wave)
   constexpr int BN = 32;               // keys per tile
@@ -368,10 +374,11 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdArgs a) {
     }
   }
   const float* brow = nullptr;
-  if constexpr (BIAS)
+  if constexpr (BIAS && !ALIBI)
     brow = a.bias + (int64_t)(cq0 + (row_ok ? my_row : 0)) * a.b_st +
            (int64_t)(a.bias_heads == 1 ? 0 : head) * a.b_sh;
   const int blim = BIAS ? min(lk, a.bias_cols) : 0;
+  const float neg_slope = ALIBI ? -a.alibi[(int64_t)seq * a.alibi_ss + head] : 0.0f;
   float l2 = __builtin_inff(), dd = 0.0f;
   if (row_ok) {
     const float l = a.lse[(int64_t)head * a.total_q + cq0 + my_row];
@@ -425,7 +432,11 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int key0 = kb + 8 * j + 4 * hf;
-        if (row_ok && key0 + 3 < blim) {
+        if constexpr (ALIBI) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            bv[j][i] = neg_slope * __builtin_fabsf((float)(my_row + off - (key0 + i)));
+        } else if (row_ok && key0 + 3 < blim) {
           bv[j] = *reinterpret_cast<const f32x4_t*>(brow + key0);
         } else {
 #pragma unroll
@@ -485,7 +496,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdArgs a) {
     }
 }
 
-template <typename T, int D, typename GradT, bool BIAS>
+template <typename T, int D, typename GradT, bool BIAS, bool ALIBI = false>
 hipError_t launch_bwd_grad(const BwdArgs& a, int max_seqlen_q, int max_seqlen_kv, hipStream_t stream) {
   // delta
   const int64_t items = a.total_q * a.hq;
@@ -498,11 +509,11 @@ hipError_t launch_bwd_grad(const BwdArgs& a, int max_seqlen_q, int max_seqlen_kv
   if (e != hipSuccess) return e;
   const unsigned n_kt = (unsigned)((max_seqlen_kv + 127) / 128);
   const unsigned n_qt = (unsigned)((max_seqlen_q + 127) / 128);
-  hipLaunchKernelGGL((dkdv_kernel<T, D, GradT, BIAS>), dim3((unsigned)(a.hkv * a.num_seqs), n_kt),
+  hipLaunchKernelGGL((dkdv_kernel<T, D, GradT, BIAS, ALIBI>), dim3((unsigned)(a.hkv * a.num_seqs), n_kt),
                      dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dq_kernel<T, D, GradT, BIAS>), dim3((unsigned)(a.hq * a.num_seqs), n_qt),
+  hipLaunchKernelGGL((dq_kernel<T, D, GradT, BIAS, ALIBI>), dim3((unsigned)(a.hq * a.num_seqs), n_qt),
                      dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -512,6 +523,9 @@ hipError_t launch_bwd_grad(const BwdArgs& a, int max_seqlen_q, int max_seqlen_kv
 template <typename T, int D>
 hipError_t launch_bwd_dims(const BwdArgs& a, bool grad_f32, bool bias, int max_seqlen_q,
                            int max_seqlen_kv, hipStream_t stream) {
+  if (a.alibi != nullptr)
+    return grad_f32 ? launch_bwd_grad<T, D, float, true, true>(a, max_seqlen_q, max_seqlen_kv, stream)
+                    : launch_bwd_grad<T, D, T, true, true>(a, max_seqlen_q, max_seqlen_kv, stream);
   if (bias)
     return grad_f32 ? launch_bwd_grad<T, D, float, true>(a, max_seqlen_q, max_seqlen_kv, stream)
                     : launch_bwd_grad<T, D, T, true>(a, max_seqlen_q, max_seqlen_kv, stream);

@@ -29,10 +29,12 @@ struct KernelArgs {
   const int32_t* bias_ranges;  // optional [bias_heads, total_q, 2] key ranges of the bias rows
   const void* q_rope;  // optional: last 64 dims of the 192-wide q / k (q, k then hold 128)
   const void* k_rope;
+  const float* alibi;  // optional ALiBi slopes, alibi[seq * alibi_ss + head]
   int32_t* tile_counts;
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
   int64_t b_st, b_sh;
   int64_t qr_st, qr_sh, kr_st, kr_sh;  // q_rope / k_rope strides
+  int64_t alibi_ss;
   int64_t total_q;
   int32_t num_seqs;
   int32_t hq;

@@ -98,6 +98,13 @@ __device__ __forceinline__ int wave_max_i32(int x) {
   return x;
 }
 
+// ALiBi bias of query position pos (in key coordinates) for key `key`:
+// minus the head's slope times their distance.  The distance is an exact
+// integer below 2^24, so the value is the product rounded once.
+__device__ __forceinline__ float alibi_bias(float neg_slope, int pos, int key) {
+  return neg_slope * __builtin_fabsf((float)(pos - key));
+}
+
 // Key hull of the bias rows [r0, r0 + rows) of one sequence and head: the
 // smallest lo and largest hi over the rows' ranges [lo, hi) of keys whose
 // bias is not -inf (empty ranges count for nothing), and the largest hi over
@@ -237,7 +244,9 @@ struct Geo {
 // ----------------------------------------------------------------------------
 // The kernel.
 // ----------------------------------------------------------------------------
-template <typename T, int DQK, int DV, bool BIAS, typename OutT>
+// ALIBI: the bias is computed from per-head slopes instead of read (BIAS
+// is then set too: the logits carry a bias either way).
+template <typename T, int DQK, int DV, bool BIAS, typename OutT, bool ALIBI = false>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs a) {
   using G = Geo<T, DQK, DV>;
   using E = Elem<T>;
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
   if (causal) kv_hi = min(lk, r1 - 1 + off + 1);
   int kv_lo = 0;
   if (W > 0) kv_lo = max(0, r0 + off - W + 1);
-  if constexpr (BIAS) {
+  if constexpr (BIAS && !ALIBI) {
     // keys outside the hull of the rows' bias ranges have a -inf bias
     if (a.bias_ranges != nullptr) {
       const int32_t* rg = a.bias_ranges +
@@ -430,7 +439,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
 
   const float c_scale = a.scale_log2;
   const float* brow = nullptr;
-  if constexpr (BIAS) {
+  const float neg_slope = ALIBI ? -a.alibi[(int64_t)seq * a.alibi_ss + head] : 0.0f;
+  if constexpr (BIAS && !ALIBI) {
     brow = a.bias + (int64_t)(cq0 + (row_ok ? my_row : 0)) * a.b_st +
            (int64_t)(a.bias_heads == 1 ? 0 : head) * a.b_sh;
   }
@@ -498,7 +508,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
             const int key0 = kb + 32 * mb + 8 * qd + 4 * hf;
             f32x4_t bv;
             const int blim = min(lk, a.bias_cols);  // bias columns read: below both
-            if (row_ok && key0 + 3 < blim) {
+            if constexpr (ALIBI) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) bv[e] = alibi_bias(neg_slope, my_row + off, key0 + e);
+            } else if (row_ok && key0 + 3 < blim) {
               bv = *reinterpret_cast<const f32x4_t*>(brow + key0);
             } else {
 #pragma unroll
@@ -769,11 +782,13 @@ struct WaveBlocks {
 // ROPE: the query-key contraction's last 64 dims come from separate q_rope /
 // k_rope tensors (the latent-attention head without concatenation); the K
 // tile then holds a 128-wide "nope" part and a 64-wide "rope" part.
-template <typename T, int DQK, int DV, bool BIAS, typename OutT, bool ROPE = false>
+template <typename T, int DQK, int DV, bool BIAS, typename OutT, bool ROPE = false,
+          bool ALIBI = false>
 __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void attn_fwd16p_kernel(
     const KernelArgs a) {
   using E = Elem<T>;
   static_assert(!ROPE || DQK == 192, "split nope / rope operands only for the 192-wide head");
+  static_assert(!ALIBI || BIAS, "ALiBi logits take the biased path");
   constexpr int DN = ROPE ? DQK - 64 : DQK;  // width of the q / k operand (the nope part)
   // A row's running max m lags the true row max by less than
   // 2^kRescaleThreshold: O and l are rescaled between tiles only when a row's
@@ -919,7 +934,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   // skipped exactly as masked tiles are; a wave also stops after the last
   // tile its own rows can see.
   int wave_bias_hi = lk;
-  if constexpr (BIAS) {
+  if constexpr (BIAS && !ALIBI) {
     if (a.bias_ranges != nullptr) {
       const int32_t* rg = a.bias_ranges +
           ((int64_t)(a.bias_heads == 1 ? 0 : head) * a.total_q + cq0) * 2;
@@ -1105,7 +1120,8 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   // the exponent's argument multiplies them by log2(e).
   const float c_nat = a.scale_log2 * (1.0f / kLog2e);
   const float* brow[NB];
-  if constexpr (BIAS) {
+  const float neg_slope = ALIBI ? -a.alibi[(int64_t)seq * a.alibi_ss + head] : 0.0f;
+  if constexpr (BIAS && !ALIBI) {
 #pragma unroll
     for (int n = 0; n < NB; ++n)
       brow[n] = a.bias + (int64_t)(cq0 + (row_ok[n] ? my_row[n] : 0)) * a.b_st +
@@ -1188,7 +1204,11 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           const int key0 = kb + 32 * mb + 8 * qd + 4 * hf;
-          if (row_ok[n] && key0 + 3 < blim) {
+          if constexpr (ALIBI) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              bv[n][mb][qd][e] = alibi_bias(neg_slope, my_row[n] + off, key0 + e);
+          } else if (row_ok[n] && key0 + 3 < blim) {
             bv[n][mb][qd] = *reinterpret_cast<const f32x4_t*>(brow[n] + key0);
           } else {
 #pragma unroll
@@ -1591,19 +1611,25 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   }
 }
 
-template <typename T, int DQK, int DV, bool BIAS, typename OutT, bool ROPE>
+template <typename T, int DQK, int DV, bool BIAS, typename OutT, bool ROPE, bool ALIBI = false>
 hipError_t launch_one(const KernelArgs& a, dim3 grid, hipStream_t stream) {
   if constexpr (Elem<T>::kWide) {
-    hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, BIAS, OutT>), grid, dim3(kThreads), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((attn_fwd16p_kernel<T, DQK, DV, BIAS, OutT, ROPE>), grid, dim3(kThreads), 0,
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, BIAS, OutT, ALIBI>), grid, dim3(kThreads), 0,
                        stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_fwd16p_kernel<T, DQK, DV, BIAS, OutT, ROPE, ALIBI>), grid,
+                       dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
 
+// a.alibi set: the bias comes from the slopes (a tensor bias is refused with it)
 template <typename T, int DQK, int DV, bool ROPE>
 hipError_t launch_rope(const KernelArgs& a, bool bias, bool out_f32, dim3 grid, hipStream_t s) {
+  if (a.alibi != nullptr) {
+    return out_f32 ? launch_one<T, DQK, DV, true, float, ROPE, true>(a, grid, s)
+                   : launch_one<T, DQK, DV, true, T, ROPE, true>(a, grid, s);
+  }
   if (bias) {
     return out_f32 ? launch_one<T, DQK, DV, true, float, ROPE>(a, grid, s)
                    : launch_one<T, DQK, DV, true, T, ROPE>(a, grid, s);

@@ -230,6 +230,13 @@ int check_fwd_params(const mi_attn_fwd_params* p, bool* empty) {
   if (dt != MI_ATTN_F32 && p->out_stride_tok * elem_size(p->out_dtype) * 32 > INT32_MAX)
     return fail(MI_ATTN_ERR_UNSUPPORTED, "out token stride too large (more than 64 MiB per token)");
   const bool has_bias = p->bias != nullptr;
+  if (p->alibi_slopes != nullptr) {
+    if (has_bias)
+      return fail(MI_ATTN_ERR_UNSUPPORTED, "ALiBi slopes and a bias tensor together are not supported");
+    if ((reinterpret_cast<uintptr_t>(p->alibi_slopes) & 3u) != 0 || p->alibi_stride_seq < 0)
+      return fail(MI_ATTN_ERR_INVALID_ARG,
+                  "alibi_slopes must be 4-byte aligned with a non-negative sequence stride");
+  }
   if (has_bias) {
     if (p->bias_heads != 1 && p->bias_heads != p->hq)
       return fail(MI_ATTN_ERR_UNSUPPORTED, "bias_heads must be 1 or hq (got %d)", p->bias_heads);
@@ -270,6 +277,8 @@ int plan_decode(const mi_attn_fwd_params* p, int64_t max_seqlen_kv, int32_t num_
   if (p->bias != nullptr) return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode takes no bias");
   if (p->q_rope != nullptr || p->k_rope != nullptr)
     return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode takes no q_rope / k_rope");
+  if (p->alibi_slopes != nullptr)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode takes no ALiBi slopes");
   if (num_splits < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "num_splits must be >= 0 (0 = auto)");
   if (max_seqlen_kv < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "max_seqlen_kv must be >= 0");
   const int64_t group = p->hq / p->hkv;
@@ -421,6 +430,8 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
   a.qr_sh = p->q_rope_stride_head;
   a.kr_st = p->k_rope_stride_tok;
   a.kr_sh = p->k_rope_stride_head;
+  a.alibi = p->alibi_slopes;
+  a.alibi_ss = p->alibi_stride_seq;
   a.tile_counts = p->tile_counts;
   a.q_st = p->q_stride_tok;
   a.q_sh = p->q_stride_head;
@@ -549,6 +560,13 @@ int mi_attn_varlen_bwd(const mi_attn_bwd_params* p_in, void* stream) {
                   "bias must be 16-byte aligned with strides that are multiples of 4");
     if (p->bias_cols <= 0) return fail(MI_ATTN_ERR_INVALID_ARG, "bias_cols must be > 0");
   }
+  if (p->alibi_slopes != nullptr) {
+    if (has_bias)
+      return fail(MI_ATTN_ERR_UNSUPPORTED, "ALiBi slopes and a bias tensor together are not supported");
+    if ((reinterpret_cast<uintptr_t>(p->alibi_slopes) & 3u) != 0 || p->alibi_stride_seq < 0)
+      return fail(MI_ATTN_ERR_INVALID_ARG,
+                  "alibi_slopes must be 4-byte aligned with a non-negative sequence stride");
+  }
   const int64_t n_kt = (p->max_seqlen_kv + 127) / 128, n_qt = (p->max_seqlen_q + 127) / 128;
   if ((int64_t)p->hq * p->num_seqs > INT32_MAX || n_kt > 65535 || n_qt > 65535 ||
       (int64_t)p->total_q * p->hq * (d / 8) > INT32_MAX)
@@ -584,6 +602,8 @@ int mi_attn_varlen_bwd(const mi_attn_bwd_params* p_in, void* stream) {
     a.bias_heads = p->bias_heads;
     a.bias_cols = (int32_t)(p->bias_cols < INT32_MAX ? p->bias_cols : INT32_MAX);
   }
+  a.alibi = p->alibi_slopes;
+  a.alibi_ss = p->alibi_stride_seq;
   hipError_t e = mi_attn::launch_attn_bwd(a, dt, p->grad_dtype == MI_ATTN_F32, has_bias, (int)d,
                                           (int)p->max_seqlen_q, (int)p->max_seqlen_kv,
                                           reinterpret_cast<hipStream_t>(stream));

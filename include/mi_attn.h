@@ -152,6 +152,19 @@ typedef struct mi_attn_fwd_params {
   const void* k_rope;
   int64_t q_rope_stride_tok, q_rope_stride_head;
   int64_t k_rope_stride_tok, k_rope_stride_head;
+  /* Added in version 1.5 (NULL for older callers): ALiBi computed in the
+   * kernels instead of read from a bias tensor.  The mtlattn 0.3.0 page
+   * (section "Use") lists ALiBi among the patterns its additive bias
+   * expresses; the pages give no formula, and the one used here is the
+   * usual linear distance penalty: the logit of query row i and key j of a
+   * sequence gains -slope * |i + (Lk - Lq) - j| (distance from the query's
+   * end-aligned position), slope = alibi_slopes[s * alibi_stride_seq + h]
+   * for sequence s and query head h (alibi_stride_seq = 0: one slope per
+   * head for every sequence).  fp32 device array, 4-byte aligned, finite
+   * values.  Composes with causal / window / GQA; refused together with a
+   * bias tensor. */
+  const float* alibi_slopes;
+  int64_t alibi_stride_seq;
 } mi_attn_fwd_params;
 
 /*
@@ -297,6 +310,10 @@ typedef struct mi_attn_bwd_params {
   int32_t bias_heads;
   int64_t bias_cols;
   int64_t bias_stride_tok, bias_stride_head;
+  /* Added in version 1.5: the forward's ALiBi slopes, same layout and rule
+   * as in mi_attn_fwd_params (not with a bias).  NULL: none. */
+  const float* alibi_slopes;
+  int64_t alibi_stride_seq;
 } mi_attn_bwd_params;
 
 /*

@@ -11,6 +11,11 @@ shares no code with the HIP path.
   kernels may skip every key outside these ranges; the triton-msl part-2
   post (section "FlashAttention: faster than PyTorch, competitive with MLX")
   makes the same point for tiles that are masked in full.
+* ``alibi_bias``: the ALiBi bias written out as a dense additive bias.  The
+  mtlattn 0.3.0 page (section "Use") names ALiBi as one of the patterns the
+  additive bias carries but gives no formula; the reading taken is the
+  linear distance penalty, minus the head's slope times the distance
+  between the query's end-aligned position and the key.
 """
 from __future__ import annotations
 
@@ -33,4 +38,24 @@ def bias_key_ranges(bias, cu_q, cu_kv):
                 keys = np.nonzero(bias[t, h, :lk] != -np.inf)[0]
                 if keys.size:
                     out[h, t] = (keys[0], keys[-1] + 1)
+    return out
+
+
+def alibi_bias(slopes, cu_q, cu_kv, hq, cols):
+    """fp64 ``[Tq, hq, cols]``: ``-slope[s, h] * |i + (Lk - Lq) - j|`` for
+    query row i and key j < Lk of sequence s (0 past Lk, where no key is).
+    ``slopes`` is ``[hq]`` (every sequence) or ``[num_seqs, hq]``."""
+    slopes = np.asarray(slopes, dtype=np.float64)
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_kv = np.asarray(cu_kv, dtype=np.int64)
+    out = np.zeros((int(cu_q[-1]), hq, cols), dtype=np.float64)
+    for s in range(len(cu_q) - 1):
+        lq = int(cu_q[s + 1] - cu_q[s])
+        lk = int(cu_kv[s + 1] - cu_kv[s])
+        sl = slopes if slopes.ndim == 1 else slopes[s]
+        for i in range(lq):
+            pos = i + lk - lq
+            for h in range(hq):
+                for j in range(min(lk, cols)):
+                    out[int(cu_q[s]) + i, h, j] = -sl[h] * abs(pos - j)
     return out

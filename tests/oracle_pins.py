@@ -546,10 +546,54 @@ def pin_packed_matches_masked():
         _close(dense, ref, 1e-12)
 
 
+# ---------------------------------------------------------------- ALiBi
+def pin_alibi_hand_worked():
+    """Two sequences (3 queries / 3 keys, 1 query / 4 keys) and slopes 0.5,
+    0.25, worked by hand: the query's end-aligned position minus the key,
+    in absolute value, times minus the slope."""
+    b = oracle.alibi_bias([0.5, 0.25], [0, 3, 4], [0, 3, 7], 2, 4)
+    assert b[0, 0].tolist() == [0.0, -0.5, -1.0, 0.0]       # row 0, position 0
+    assert b[2, 0].tolist() == [-1.0, -0.5, 0.0, 0.0]       # row 2, position 2
+    assert b[1, 1].tolist() == [-0.25, 0.0, -0.25, 0.0]     # slope 0.25, position 1
+    assert b[3, 0].tolist() == [-1.5, -1.0, -0.5, 0.0]      # decode row: position 3 of 4 keys
+    per_seq = oracle.alibi_bias([[0.5, 0.25], [2.0, 1.0]], [0, 3, 4], [0, 3, 7], 2, 4)
+    assert per_seq[3, 1].tolist() == [-3.0, -2.0, -1.0, 0.0]
+
+
+def pin_alibi_causal_is_a_linear_key_bias():
+    """Under the causal mask every visible key sits at or before the query's
+    position, so -slope * |pos - j| = slope * j - slope * pos: the output
+    equals that of the bias slope * j alone (a per-row constant cancels in
+    the softmax) and the LSE differs by exactly -slope * pos."""
+    rng = np.random.default_rng(17)
+    lens_q, lens_k = [5, 9, 1], [5, 12, 6]
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int64)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int64)
+    hq, hkv, d = 4, 2, 8
+    q = rng.standard_normal((int(cu_q[-1]), hq, d))
+    k = rng.standard_normal((int(cu_k[-1]), hkv, d))
+    v = rng.standard_normal((int(cu_k[-1]), hkv, d))
+    slopes = np.array([0.5, 0.25, 0.125, 1.0 / 3.0])
+    cols = max(lens_k)
+    out_a, lse_a = oracle.varlen_attention(q, k, v, cu_q, cu_k, None, True, 0,
+                                           oracle.alibi_bias(slopes, cu_q, cu_k, hq, cols))
+    lin = np.zeros((int(cu_q[-1]), hq, cols))
+    shift = np.zeros((hq, int(cu_q[-1])))
+    for s in range(len(lens_q)):
+        for i in range(lens_q[s]):
+            t = int(cu_q[s]) + i
+            lin[t] = slopes[:, None] * np.arange(cols)[None, :]
+            shift[:, t] = -slopes * (i + lens_k[s] - lens_q[s])
+    out_l, lse_l = oracle.varlen_attention(q, k, v, cu_q, cu_k, None, True, 0, lin)
+    _close(out_a, out_l, 1e-12)
+    _close(lse_a, lse_l + shift, 1e-12)
+
+
 ALL_PINS = [pin_brute_force_tiny, pin_sdpa_special_case, pin_rows_sum_to_one,
             pin_one_key_sequence, pin_zero_queries_mean, pin_key_permutation_invariance,
             pin_neg_inf_key_is_removed, pin_mask_counts_closed_form, pin_golden_hand_worked,
             pin_row_subset_matches_full, pin_bias_ranges_prefix_lm_closed_form,
             pin_bias_ranges_skip_is_exact, pin_backward_finite_differences,
             pin_backward_sdpa_special_case, pin_backward_closed_forms, pin_padding_hand_worked,
-            pin_masked_attention_sdpa, pin_packed_matches_masked]
+            pin_masked_attention_sdpa, pin_packed_matches_masked, pin_alibi_hand_worked,
+            pin_alibi_causal_is_a_linear_key_bias]

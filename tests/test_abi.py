@@ -134,6 +134,10 @@ REFUSALS = {
     "rope_short_row": (dict(d_qk=192, q_rope=1 << 20, k_rope=1 << 20, q_rope_stride_tok=8 * 64,
                             q_rope_stride_head=64, k_rope_stride_tok=56,
                             k_rope_stride_head=0), fav.ERR_UNSUPPORTED),
+    "alibi_with_bias": (dict(alibi_slopes=1 << 20, bias=1 << 20, bias_heads=1, bias_cols=64,
+                             bias_stride_tok=64, bias_stride_head=0), fav.ERR_UNSUPPORTED),
+    "alibi_misaligned": (dict(alibi_slopes=(1 << 20) + 2), fav.ERR_INVALID_ARG),
+    "alibi_negative_stride": (dict(alibi_slopes=1 << 20, alibi_stride_seq=-8), fav.ERR_INVALID_ARG),
     # with split operands q / k hold 128 dims; without them a 128-wide stride is short of 192
     "latent_short_q_stride": (dict(d_qk=192, q_stride_tok=128, q_stride_head=0, hq=2, hkv=2,
                                    out_stride_tok=2 * 128), fav.ERR_UNSUPPORTED),
@@ -223,6 +227,9 @@ BWD_REFUSALS = {
     "fp32_inputs": (dict(in_dtype=fav.F32, grad_dtype=fav.F32), fav.ERR_UNSUPPORTED),
     "latent_dims": (dict(d_qk=192, d_v=128), fav.ERR_UNSUPPORTED),
     "grad_dtype": (dict(grad_dtype=fav.F16), fav.ERR_UNSUPPORTED),
+    "alibi_with_bias": (dict(alibi_slopes=1 << 20, bias=1 << 20, bias_heads=1, bias_cols=64,
+                             bias_stride_tok=64, bias_stride_head=0), fav.ERR_UNSUPPORTED),
+    "alibi_misaligned": (dict(alibi_slopes=(1 << 20) + 1), fav.ERR_INVALID_ARG),
     "gqa_ratio": (dict(hq=6, hkv=4), fav.ERR_UNSUPPORTED),
     "window_without_causal": (dict(window=8), fav.ERR_UNSUPPORTED),
     "null_delta": (dict(delta=None), fav.ERR_INVALID_ARG),
@@ -247,6 +254,7 @@ def test_backward_host_validation_refuses(name):
 DECODE_REFUSALS = {
     "fp32": (dict(in_dtype=fav.F32, out_dtype=fav.F32), 1 << 20, fav.ERR_UNSUPPORTED),
     "latent_dims": (dict(d_qk=192, d_v=128), 1 << 20, fav.ERR_UNSUPPORTED),
+    "alibi": (dict(alibi_slopes=1 << 20), 1 << 20, fav.ERR_UNSUPPORTED),
     "rope": (dict(q_rope=1 << 20, k_rope=1 << 20, q_rope_stride_tok=8 * 64, q_rope_stride_head=64,
                   k_rope_stride_tok=2 * 64, k_rope_stride_head=64), 1 << 20, fav.ERR_UNSUPPORTED),
     "bias": (dict(bias=1 << 20, bias_heads=1, bias_cols=64, bias_stride_tok=64, bias_stride_head=64),

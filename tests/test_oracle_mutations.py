@@ -42,6 +42,12 @@ MASK_MUTATIONS = {
     "ranges_lo_zero": ("out[h, t] = (keys[0], keys[-1] + 1)", "out[h, t] = (0, keys[-1] + 1)"),
     "ranges_finite_test": ("keys = np.nonzero(bias[t, h, :lk] != -np.inf)[0]",
                            "keys = np.nonzero(bias[t, h, :lk] > 0)[0]"),
+    "alibi_sign": ("= -sl[h] * abs(pos - j)", "= sl[h] * abs(pos - j)"),
+    "alibi_start_aligned": ("pos = i + lk - lq", "pos = i"),
+    "alibi_no_abs": ("= -sl[h] * abs(pos - j)", "= -sl[h] * (pos - j)"),
+    "alibi_first_seq_slopes": ("sl = slopes if slopes.ndim == 1 else slopes[s]",
+                               "sl = slopes if slopes.ndim == 1 else slopes[0]"),
+    "alibi_head_reversed": ("= -sl[h] * abs(pos - j)", "= -sl[hq - 1 - h] * abs(pos - j)"),
 }
 
 # mutations of the backward oracle (oracle/ref_backward.py)
