@@ -137,6 +137,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     return lib
 
 
+def variant_library(name: str) -> ctypes.CDLL:
+    """A schedule variant of the library (``slots2``, ``synccopies``), built
+    beside it for the LDS race check; its results must equal the shipping
+    library's bit for bit."""
+    from .build import variant_path
+    return load_library(variant_path(name))
+
+
 def mi_attn_last_error() -> str:
     return load_library().mi_attn_last_error().decode()
 

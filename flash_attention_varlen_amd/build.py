@@ -26,7 +26,17 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wall", "-Wno-pass-failed", "-Wno-unused-function",
          "-Wno-cuda-compat", "-I", INCLUDE, "-I", CSRC]
 # Sources compiled once each.
-PLAIN = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "bias_ranges.hip", "padding.hip", "mi_attn.cpp"]
+PLAIN = ["attn_bwd.hip", "attn_decode.hip", "bias_ranges.hip", "padding.hip", "mi_attn.cpp"]
+# The forward (dispatcher + instances) is also built in schedule variants
+# that only the LDS race test loads: all 16-bit kernels with two K/V slots,
+# and every step waiting for its own copies behind a barrier before any
+# read.  Both must give results bitwise equal to the shipping library.
+VARIANTS = {"slots2": ["-DMI_ATTN_MAX_SLOTS=2"], "synccopies": ["-DMI_ATTN_SYNC_COPIES=1"]}
+VARIANT_DIR = os.path.join(PKG, "variants")
+
+
+def variant_path(name: str) -> str:
+    return os.path.join(VARIANT_DIR, f"libmi_attn_{name}.so")
 
 
 def hipcc() -> str:
@@ -53,18 +63,26 @@ def bwd_instances():
     return _instance_list("attn_bwd.h", "MI_ATTN_BWD_INSTANCES", r"X\((\w+), (\w+), (\d+)\)")
 
 
+def forward_jobs(objdir: str, tag_suffix: str = "", defines=()):
+    jobs = []
+    obj = os.path.join(objdir, f"attn_fwd{tag_suffix}.o")
+    jobs.append(([hipcc(), f"--offload-arch={ARCH}", *FLAGS, *defines, "-c", "-x", "hip",
+                  os.path.join(CSRC, "attn_fwd.hip"), "-o", obj], obj))
+    for tag, t, dqk, dv in instances():
+        obj = os.path.join(objdir, f"attn_fwd_inst_{tag}_{dqk}_{dv}{tag_suffix}.o")
+        jobs.append(([hipcc(), f"--offload-arch={ARCH}", *FLAGS, *defines,
+                      f"-DMI_ATTN_INST_TAG={tag}", f"-DMI_ATTN_INST_T={t}",
+                      f"-DMI_ATTN_INST_DQK={dqk}", f"-DMI_ATTN_INST_DV={dv}", "-c", "-x", "hip",
+                      os.path.join(CSRC, "attn_fwd_inst.hip"), "-o", obj], obj))
+    return jobs
+
+
 def compile_jobs(objdir: str):
     jobs = []
     for src in PLAIN:
         obj = os.path.join(objdir, src + ".o")
         jobs.append(([hipcc(), f"--offload-arch={ARCH}", *FLAGS, "-c", "-x", "hip",
                       os.path.join(CSRC, src), "-o", obj], obj))
-    for tag, t, dqk, dv in instances():
-        obj = os.path.join(objdir, f"attn_fwd_inst_{tag}_{dqk}_{dv}.o")
-        jobs.append(([hipcc(), f"--offload-arch={ARCH}", *FLAGS, f"-DMI_ATTN_INST_TAG={tag}",
-                      f"-DMI_ATTN_INST_T={t}", f"-DMI_ATTN_INST_DQK={dqk}",
-                      f"-DMI_ATTN_INST_DV={dv}", "-c", "-x", "hip",
-                      os.path.join(CSRC, "attn_fwd_inst.hip"), "-o", obj], obj))
     for tag, t, d in bwd_instances():
         obj = os.path.join(objdir, f"attn_bwd_inst_{tag}_{d}.o")
         jobs.append(([hipcc(), f"--offload-arch={ARCH}", *FLAGS, f"-DMI_ATTN_INST_TAG={tag}",
@@ -78,11 +96,24 @@ def _run(cmd):
     return r.returncode, [l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l]
 
 
-def build(verbose: bool = False, jobs: int = 0) -> str:
-    """Compile the shared library; returns its path.  Always recompiles."""
+def _link(objs, out):
+    tmp = out + ".tmp"
+    rc, lines = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    if rc != 0:
+        raise RuntimeError("link failed:\n" + "\n".join(lines))
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, jobs: int = 0, variants: bool = True) -> str:
+    """Compile the shared library (and, with ``variants``, the schedule
+    variants of the forward); returns the library's path.  Always recompiles."""
     jobs = jobs or min(16, os.cpu_count() or 1)
     with tempfile.TemporaryDirectory(prefix="mi_attn_build_") as objdir:
-        todo = compile_jobs(objdir)
+        shared = compile_jobs(objdir)
+        fwd = forward_jobs(objdir)
+        var = {name: forward_jobs(objdir, "_" + name, defs) for name, defs in VARIANTS.items()} \
+            if variants else {}
+        todo = shared + fwd + [j for js in var.values() for j in js]
         with ThreadPoolExecutor(jobs) as ex:
             results = list(ex.map(lambda j: _run(j[0]), todo))
         for (cmd, _), (rc, lines) in zip(todo, results):
@@ -92,13 +123,11 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
                 raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(lines))
             if verbose and lines:
                 print("\n".join(lines))
-        tmp = LIB + ".tmp"
-        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC",
-                *[obj for _, obj in todo], "-o", tmp]
-        rc, lines = _run(link)
-        if rc != 0:
-            raise RuntimeError("link failed:\n" + "\n".join(lines))
-    os.replace(tmp, LIB)
+        _link([obj for _, obj in shared + fwd], LIB)
+        if var:
+            os.makedirs(VARIANT_DIR, exist_ok=True)
+        for name, js in var.items():
+            _link([obj for _, obj in shared + js], variant_path(name))
     return LIB
 
 

@@ -37,6 +37,17 @@
 
 #include "attn_fwd.h"
 
+// Schedule switches for the LDS race check (the shipping build uses the
+// defaults): MI_ATTN_MAX_SLOTS=2 gives every 16-bit kernel two K/V slots;
+// MI_ATTN_SYNC_COPIES=1 makes each step wait for its tile copies behind a
+// barrier before it reads anything.
+#ifndef MI_ATTN_MAX_SLOTS
+#define MI_ATTN_MAX_SLOTS 4
+#endif
+#ifndef MI_ATTN_SYNC_COPIES
+#define MI_ATTN_SYNC_COPIES 0
+#endif
+
 namespace mi_attn {
 namespace {
 
@@ -773,7 +784,8 @@ struct WaveBlocks {
   // K/V buffer slots.  Where four of each fit the LDS of two workgroups per
   // CU (80 KB each) copies run one more step ahead and the workgroup
   // synchronises every second step instead of every step.
-  static constexpr int NSLOT = 4 * 32 * NMB * (DQK + DV) * 2 <= 80 * 1024 ? 4 : 2;
+  static constexpr int NSLOT =
+      MI_ATTN_MAX_SLOTS >= 4 && 4 * 32 * NMB * (DQK + DV) * 2 <= 80 * 1024 ? 4 : 2;
   // keys per tile as reported by mi_attn_tile_shape (tile counts are given
   // in these units): the bias-free tile
   static constexpr int kReportBN = 32 * (DQK > 128 ? 1 : DQK == 64 ? 4 : 2);
@@ -1304,6 +1316,10 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     constexpr bool BAR = NSLOT == 2 || (slot & 1) != 0;
     if (j + LV < nt) load_v(t + LV, VW{});
     if (j + LK < nt) load_k(t + LK, KW{});
+    if constexpr (MI_ATTN_SYNC_COPIES) {  // schedule check: copies land before any read
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+    }
     if (t >= wt_end) {  // nothing visible to this wave from here on
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       if constexpr (BAR) __syncthreads();
