@@ -38,7 +38,10 @@ METRIC = "attn fwd useful TFLOP/s + % of MI355X bf16 MFMA peak (causal GQA D=128
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 HBM_GBPS = 8000.0
 CPU_SHARE = 16  # host cores a one-GPU machine is given
-KERNEL_SOURCE = os.path.join(ROOT, "flash_attention_varlen_amd", "csrc", "attn_fwd_kernels.h")
+CSRC = os.path.join(ROOT, "flash_attention_varlen_amd", "csrc")
+# the sources of each pass's kernels (a stored counter reading is valid while they are unchanged)
+KERNEL_SOURCES = {"fwd": ("attn_fwd_kernels.h", "attn_fwd.h"), "bwd": ("attn_bwd_kernels.h", "attn_bwd.h"),
+                  "decode": ("attn_decode.hip", "attn_decode.h")}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -95,23 +98,23 @@ def algorithmic_bytes(w: workloads.Workload, out_bytes: int) -> float:
     return float(b)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(mode: str = "fwd") -> str:
     h = hashlib.sha256()
-    for p in (KERNEL_SOURCE, os.path.join(os.path.dirname(KERNEL_SOURCE), "attn_fwd.h")):
-        with open(p, "rb") as f:
+    for name in KERNEL_SOURCES[mode]:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload_key: str, launches: int = 1):
-    """HBM bytes per launch from the committed PMC summary, if it was taken
+def stored_traffic(workload_key: str, launches: int = 1, mode: str = "fwd"):
+    """HBM bytes per step from the committed PMC summary, if it was taken
     on the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"traffic_attn_fwd_{workload_key}.json")
+    path = os.path.join(PROFILES, f"traffic_attn_{mode}_{workload_key}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(mode):
         return None
     return float(t["hbm_bytes_per_launch"]) * launches
 
@@ -372,7 +375,8 @@ def main():
         achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
     out_bytes = out.element_size()
     # stored counter readings belong to the workload as defined (not to an overridden window)
-    traffic = stored_traffic(args.workload) if args.window is None and not args.backward else None
+    mode = "decode" if is_decode else "bwd" if args.backward else "fwd"
+    traffic = stored_traffic(args.workload, mode=mode) if args.window is None else None
 
     cold = None
     if args.cold_steps > 0:

@@ -38,17 +38,26 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-def is_attn(name: str) -> bool:
-    """The library's attention kernels (rocprofv3 prints some names mangled,
-    some demangled)."""
-    return "attn_fwd" in name and "mi_attn" in name
+# The library's kernels of each pass (rocprofv3 prints some names mangled,
+# some demangled); a pass's "step" is one launch of each of its kernels.
+KERNELS = {
+    "fwd": ("attn_fwd16p_kernel", "attn_fwd_kernel"),
+    "bwd": ("delta_kernel", "dkdv_kernel", "dq_kernel"),
+    "decode": ("decode_kernel", "decode_merge_kernel"),
+}
+MODE = "fwd"
 
 
 def short_name(mangled: str) -> str:
-    for key in ("attn_fwd16p_kernel", "attn_fwd_kernel"):
-        if key in mangled:
-            return key
+    for names in KERNELS.values():
+        for key in names:
+            if key in mangled:
+                return key
     return mangled[:60]
+
+
+def is_attn(name: str) -> bool:
+    return "mi_attn" in name and short_name(name) in KERNELS[MODE]
 
 
 def read_csv(path):
@@ -60,8 +69,13 @@ def trace_summary(args) -> str:
     stats = read_csv(os.path.join(args.trace, "run_kernel_stats.csv"))
     trace = read_csv(os.path.join(args.trace, "run_kernel_trace.csv"))
     attn = [r for r in trace if is_attn(r["Kernel_Name"])]
-    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in attn]
-    timed = durs[-args.steps:]
+    kinds = sorted({short_name(r["Kernel_Name"]) for r in attn}, key=KERNELS[MODE].index)
+    per_kind = {k: [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in attn
+                    if short_name(r["Kernel_Name"]) == k] for k in kinds}
+    # timed launches: the last --steps of each kernel; a step's time is their sum
+    timed_k = {k: v[-args.steps:] for k, v in per_kind.items()}
+    timed = [sum(x) for x in zip(*timed_k.values())]
+    durs = [d for v in per_kind.values() for d in v]
     bench = None
     if args.bench_json and os.path.exists(args.bench_json):
         with open(args.bench_json) as f:
@@ -69,8 +83,7 @@ def trace_summary(args) -> str:
                 if line.startswith("{"):
                     bench = json.loads(line)
     r0 = attn[0] if attn else {}
-    lines = [f"# rocprofv3 kernel trace: {short_name(r0.get('Kernel_Name', ''))}, "
-             f"workload {args.workload}", "",
+    lines = [f"# rocprofv3 kernel trace: {' + '.join(kinds)}, workload {args.workload}", "",
              "Command (run from the repository root on one MI355X):", "",
              "```", args.trace_cmd, "```", "",
              "## Kernel statistics (all dispatches, as rocprofv3 --stats prints them)", "",
@@ -80,14 +93,19 @@ def trace_summary(args) -> str:
         lines.append(f"| {short_name(s['Name'])} | {s['Calls']} | "
                      f"{int(s['TotalDurationNs']) / 1e6:.3f} | {float(s['AverageNs']) / 1e3:.1f} | "
                      f"{int(s['MinNs']) / 1e3:.1f} | {int(s['MaxNs']) / 1e3:.1f} |")
-    lines += ["", "## Attention kernel", "",
-              f"- launch: grid {r0.get('Grid_Size_X')}x{r0.get('Grid_Size_Y')} work-items, "
-              f"workgroup {r0.get('Workgroup_Size_X')}, LDS {r0.get('LDS_Block_Size')} B, "
-              f"scratch {r0.get('Scratch_Size')} B, arch VGPR {r0.get('VGPR_Count')}, "
-              f"AGPR {r0.get('Accum_VGPR_Count')}, SGPR {r0.get('SGPR_Count')}",
-              f"- dispatches: {len(durs)} (warmup + timed)",
-              f"- mean over the {len(timed)} timed dispatches: {statistics.mean(timed):.1f} us "
-              f"(median {statistics.median(timed):.1f}, min {min(timed):.1f}, max {max(timed):.1f})"]
+    lines += ["", "## Kernels of the pass", ""]
+    for k in kinds:
+        rk = next(r for r in attn if short_name(r["Kernel_Name"]) == k)
+        tk = timed_k[k]
+        lines += [f"- {k}: grid {rk.get('Grid_Size_X')}x{rk.get('Grid_Size_Y')} work-items, "
+                  f"workgroup {rk.get('Workgroup_Size_X')}, LDS {rk.get('LDS_Block_Size')} B, "
+                  f"scratch {rk.get('Scratch_Size')} B, arch VGPR {rk.get('VGPR_Count')}, "
+                  f"AGPR {rk.get('Accum_VGPR_Count')}, SGPR {rk.get('SGPR_Count')}; "
+                  f"{len(per_kind[k])} dispatches; mean over the {len(tk)} timed ones "
+                  f"{statistics.mean(tk):.1f} us (median {statistics.median(tk):.1f}, "
+                  f"min {min(tk):.1f}, max {max(tk):.1f})"]
+    lines += [f"- one step (one launch of each): mean {statistics.mean(timed):.1f} us over "
+              f"{len(timed)} timed steps (median {statistics.median(timed):.1f})"]
     if bench:
         rf = bench["roofline"]
         lines += [f"- the same run's bench line: kernel_ms {rf['kernel_ms']} (HIP events around "
@@ -99,20 +117,28 @@ def trace_summary(args) -> str:
 
 
 def counter_values(d, name):
+    """Per kernel of the pass: its readings of counter `name` (one per
+    dispatch); and the calibration copies' readings."""
     rows = read_csv(os.path.join(d, "run_counter_collection.csv"))
-    attn = [float(r["Counter_Value"]) for r in rows
-            if is_attn(r["Kernel_Name"]) and r["Counter_Name"] == name]
+    attn = {}
+    for r in rows:
+        if is_attn(r["Kernel_Name"]) and r["Counter_Name"] == name:
+            attn.setdefault(short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
     copy = [float(r["Counter_Value"]) for r in rows
             if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == name]
-    kname = next(r["Kernel_Name"] for r in rows if is_attn(r["Kernel_Name"]))
-    return attn, copy, kname
+    return attn, copy
 
 
 def counters_summary(args) -> str:
     rows = read_csv(os.path.join(args.counters, "run_counter_collection.csv"))
+    dominant = KERNELS[MODE][1] if MODE == "bwd" else None  # dkdv: the slowest kernel
     by = {}
     for r in rows:
         if not is_attn(r["Kernel_Name"]):
+            continue
+        if dominant and short_name(r["Kernel_Name"]) != dominant:
+            continue
+        if MODE == "decode" and short_name(r["Kernel_Name"]) != "decode_kernel":
             continue
         d = by.setdefault(int(r["Dispatch_Id"]), {"kname": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
                                                   "wg": int(r["Workgroup_Size"]),
@@ -143,8 +169,12 @@ def counters_summary(args) -> str:
 def traffic_summary(args):
     from bench import algorithmic_bytes, kernel_source_hash
     import workloads
-    fa, fc, kname = counter_values(args.fetch, "FETCH_SIZE")
-    wa, wc, _ = counter_values(args.write, "WRITE_SIZE")
+    fak, fc = counter_values(args.fetch, "FETCH_SIZE")
+    wak, wc = counter_values(args.write, "WRITE_SIZE")
+    kname = " + ".join(sorted(fak, key=KERNELS[MODE].index))
+    # a step's readings: the sum over the pass's kernels of their mean per dispatch
+    fa = [sum(statistics.mean(v) for v in fak.values())]
+    wa = [sum(statistics.mean(v) for v in wak.values())]
     durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
             for d in (args.fetch, args.write)
             for r in read_csv(os.path.join(d, "run_counter_collection.csv"))
@@ -160,6 +190,10 @@ def traffic_summary(args):
     write_b = statistics.mean(wa) * fw * 1024
     w = workloads.ALL[args.workload]
     alg = algorithmic_bytes(w, 2 if w.dtype != "f32" else 4)
+    if MODE == "bwd":  # the backward reads q, k, v, out, dout, lse and writes dq, dk, dv (+ delta)
+        e = 2
+        alg = float(w.total_q * w.hq * (w.d_qk + 2 * w.d_v) * e + w.total_q * w.hq * 4 * 2
+                    + w.total_kv * w.hkv * (w.d_qk + w.d_v) * e * 2 + w.total_q * w.hq * w.d_qk * e)
     lines = [f"# HBM traffic: {short_name(kname)}, workload {args.workload}", "",
              "Commands (one PMC pass each, run from the repository root on one MI355X):", "",
              "```", args.pmc_cmd.replace("{COUNTER}", "FETCH_SIZE").replace("{DIR}", "prof_fetch"),
@@ -177,9 +211,9 @@ def traffic_summary(args):
              f"- ratio: {(fetch_b + write_b) / alg:.2f}",
              f"- HBM rate in these runs: {(fetch_b + write_b) / dur_ns:.1f} GB/s over a mean dispatch of "
              f"{dur_ns / 1e3:.1f} us ({100 * (fetch_b + write_b) / dur_ns / 8000:.1f}% of 8 TB/s)",
-             f"- kernel source sha256[:16]: {kernel_source_hash()}"]
-    data = {"workload": args.workload, "kernel": short_name(kname),
-            "kernel_source_sha256_16": kernel_source_hash(),
+             f"- kernel source sha256[:16]: {kernel_source_hash(MODE)}"]
+    data = {"workload": args.workload, "kernel": kname, "pass": MODE,
+            "kernel_source_sha256_16": kernel_source_hash(MODE),
             "hbm_bytes_per_launch": fetch_b + write_b,
             "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
             "fetch_factor": ff, "write_factor": fw, "algorithmic_bytes": alg,
@@ -202,28 +236,35 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--counters")
     ap.add_argument("--counters-cmd", default="")
+    ap.add_argument("--mode", default="fwd", choices=sorted(KERNELS),
+                    help="which pass's kernels the runs time: forward, backward or decode")
     args = ap.parse_args()
+    global MODE
+    MODE = args.mode
+    tag = args.workload if MODE == "fwd" else f"{args.workload}_{MODE}"
     os.makedirs(args.out_dir, exist_ok=True)
+    first = {"fwd": None, "bwd": "attn_bwd", "decode": "attn_decode"}[MODE]
     if args.trace:
         txt = trace_summary(args)
-        kname = "attn_fwd16p_kernel" if "attn_fwd16p" in txt else "attn_fwd_kernel"
-        p = os.path.join(args.out_dir, f"{kname}_{args.workload}_trace.md")
+        kname = first or ("attn_fwd16p_kernel" if "attn_fwd16p" in txt else "attn_fwd_kernel")
+        p = os.path.join(args.out_dir, f"{kname}_{tag}_trace.md")
         with open(p, "w") as f:
             f.write(txt)
         print("wrote", p)
     if args.counters:
         txt = counters_summary(args)
-        kname = "attn_fwd16p_kernel" if "attn_fwd16p" in txt else "attn_fwd_kernel"
-        p = os.path.join(args.out_dir, f"{kname}_{args.workload}_counters.md")
+        kname = first or ("attn_fwd16p_kernel" if "attn_fwd16p" in txt else "attn_fwd_kernel")
+        p = os.path.join(args.out_dir, f"{kname}_{tag}_counters.md")
         with open(p, "w") as f:
             f.write(txt)
         print("wrote", p)
     if args.fetch and args.write:
         txt, data = traffic_summary(args)
-        p = os.path.join(args.out_dir, f"{data['kernel']}_{args.workload}_hbm.md")
+        kname = first or data["kernel"]
+        p = os.path.join(args.out_dir, f"{kname}_{tag}_hbm.md")
         with open(p, "w") as f:
             f.write(txt)
-        pj = os.path.join(args.out_dir, f"traffic_attn_fwd_{args.workload}.json")
+        pj = os.path.join(args.out_dir, f"traffic_attn_{MODE}_{args.workload}.json")
         with open(pj, "w") as f:
             json.dump(data, f, indent=1)
         print("wrote", p, pj)

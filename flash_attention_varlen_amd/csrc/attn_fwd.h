@@ -61,7 +61,9 @@ int tile_bm(int in_dtype, int dqk, int dv);
 // pair) and launches the template for (bias, out type) on `stream`.
 #define MI_ATTN_FWD_INSTANCES(X)                                                        \
   X(bf16, __bf16, 64, 64) X(bf16, __bf16, 128, 128) X(bf16, __bf16, 192, 128)           \
+  X(bf16, __bf16, 96, 96) X(bf16, __bf16, 256, 256)                                     \
   X(f16, _Float16, 64, 64) X(f16, _Float16, 128, 128) X(f16, _Float16, 192, 128)        \
+  X(f16, _Float16, 96, 96) X(f16, _Float16, 256, 256)                                   \
   X(f32, float, 64, 64) X(f32, float, 128, 128)
 #define MI_ATTN_FWD_INSTANCE_NAME(tag, dqk, dv) launch_fwd_##tag##_##dqk##_##dv
 #define MI_ATTN_FWD_DECLARE(tag, T, dqk, dv)                                            \

@@ -9,6 +9,8 @@ int tile_bn(int in_dtype, int dqk, int dv) {
   if (in_dtype == kF32) return Geo<float, 64, 64>::BN;
   if (dqk == 64 && dv == 64) return WaveBlocks<64, 64>::kReportBN;
   if (dqk == 128 && dv == 128) return WaveBlocks<128, 128>::kReportBN;
+  if (dqk == 256 && dv == 256) return WaveBlocks<256, 256>::kReportBN;
+  if (dqk == 96 && dv == 96) return WaveBlocks<96, 96>::kReportBN;
   return WaveBlocks<192, 128>::kReportBN;
 }
 
@@ -16,6 +18,8 @@ int tile_bm(int in_dtype, int dqk, int dv) {
   if (in_dtype == kF32) return kBM;
   if (dqk == 64 && dv == 64) return 4 * 32 * WaveBlocks<64, 64>::NB;
   if (dqk == 128 && dv == 128) return 4 * 32 * WaveBlocks<128, 128>::NB;
+  if (dqk == 256 && dv == 256) return 4 * 32 * WaveBlocks<256, 256>::NB;
+  if (dqk == 96 && dv == 96) return 4 * 32 * WaveBlocks<96, 96>::NB;
   return 4 * 32 * WaveBlocks<192, 128>::NB;
 }
 

@@ -635,13 +635,13 @@ struct KSwz {
   // 16-byte-chunk swizzle of K rows: D=128 rows are 256 B (all 64 banks), so
   // 16 consecutive keys take 16 distinct chunk slots; 128 B / 384 B rows
   // alternate bank halves with key parity, so pairs of keys share a pattern.
-  __device__ static int f(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
+  __device__ static int f(int key) { return D % 128 == 0 ? (key & 15) : ((key >> 1) & 7); }
 };
 template <int D>
 struct VSwz {
   // V rows are read four keys at a time by the transposing read; the four
   // keys must land in four different 4-chunk groups.
-  __device__ static int f(int key) { return D == 128 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2); }
+  __device__ static int f(int key) { return D % 128 == 0 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2); }
 };
 
 // A pointer the compiler cannot prove wave-uniform, made uniform (every lane
@@ -767,6 +767,11 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Row width (elements) of a head dim's K / V rows in LDS: the 96-wide head
+// is laid out like the 128-wide one (16 chunk slots per row, 12 used), so
+// that its rows keep the power-of-two swizzles of the 128-wide layout.
+constexpr int lds_dim(int d) { return d == 96 ? 128 : d; }
+
 // Per head-dim pair: NB query blocks of 32 rows per wave, NMB key blocks
 // of 32 keys per tile, OCC workgroups per CU (the register budget).  The
 // 192-wide contraction keeps 32-key tiles: its Q fragments need 48
@@ -780,12 +785,16 @@ struct WaveBlocks {
   // has room for 128-key tiles, which halves its per-tile overheads (barrier,
   // max exchange, copy issue) per key.
   static constexpr int NMB = (DQK > 128 || (BIAS && DQK == 128)) ? 1 : (DQK == 64 && !BIAS) ? 4 : 2;
-  static constexpr int OCC = 2;
-  // K/V buffer slots.  Where four of each fit the LDS of two workgroups per
-  // CU (80 KB each) copies run one more step ahead and the workgroup
-  // synchronises every second step instead of every step.
+  // Workgroups per CU: two, except for the 256-wide head, whose output
+  // block and Q fragments need the registers of a whole SIMD per wave.
+  static constexpr int OCC = DV == 256 ? 1 : 2;
+  // K/V buffer slots.  Where four of each fit the LDS share of a workgroup
+  // (80 KB with two per CU) copies run one more step ahead and the
+  // workgroup synchronises every second step instead of every step.
   static constexpr int NSLOT =
-      MI_ATTN_MAX_SLOTS >= 4 && 4 * 32 * NMB * (DQK + DV) * 2 <= 80 * 1024 ? 4 : 2;
+      MI_ATTN_MAX_SLOTS >= 4 &&
+              4 * 32 * NMB * (lds_dim(DQK) + lds_dim(DV)) * 2 <= (OCC == 1 ? 152 : 80) * 1024
+          ? 4 : 2;
   // keys per tile as reported by mi_attn_tile_shape (tile counts are given
   // in these units): the bias-free tile
   static constexpr int kReportBN = 32 * (DQK > 128 ? 1 : DQK == 64 ? 4 : 2);
@@ -815,21 +824,25 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   constexpr int BM = 4 * RW;   // query rows per workgroup
   constexpr int BN = 32 * NMB; // keys per tile
   constexpr int NKS = BN / 16; // PV k-steps per tile
-  constexpr int KRB = DQK * 2;
-  constexpr int VRB = DV * 2;
-  constexpr int VCPR = DV / 8;
+  constexpr int DQK_L = lds_dim(DQK);  // K row width in LDS
+  constexpr int DV_L = lds_dim(DV);    // V row width in LDS
+  constexpr int KRB = DQK_L * 2;
+  constexpr int VRB = DV_L * 2;
+  constexpr int VCPR = DV_L / 8;
   constexpr int K_BYTES = BN * KRB;
   constexpr int V_BYTES = BN * VRB;
   constexpr int KLOADS = K_BYTES / (kThreads * 16);
   constexpr int VLOADS = V_BYTES / (kThreads * 16);
   constexpr int KSTEPS = DQK / 16;
   constexpr int NDB = DV / 32;
-  constexpr int OUT_RB = DV * (int)sizeof(OutT);
+  constexpr int OUT_RB = DV * (int)sizeof(OutT);       // bytes of an output row
   constexpr int OUT_CPR = OUT_RB / 16;
+  constexpr int OUT_RBL = DV_L * (int)sizeof(OutT);    // its staging row in LDS
+  constexpr int OUT_CPRL = OUT_RBL / 16;               // (a power of two)
   static_assert(K_BYTES % (kThreads * 16) == 0 && V_BYTES % (kThreads * 16) == 0, "tile loads");
   // output rows staged per pass (a wave stages in one K or V buffer)
   constexpr int STAGE_BYTES = K_BYTES < V_BYTES ? K_BYTES : V_BYTES;
-  constexpr int STAGE_ROWS = 32 * OUT_RB <= STAGE_BYTES ? 32 : STAGE_BYTES / OUT_RB;
+  constexpr int STAGE_ROWS = 32 * OUT_RBL <= STAGE_BYTES ? 32 : STAGE_BYTES / OUT_RBL;
   static_assert(STAGE_ROWS >= 1 && 32 % STAGE_ROWS == 0, "output staging");
 
   // K and V buffers (NSLOT of each) as separate LDS objects.  Each access
@@ -1002,10 +1015,13 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
 #pragma unroll
   for (int i = 0; i < KLOADS; ++i) {
     if (i < KN) {
+      constexpr int DL = ROPE ? DN : DQK_L;
       const int pos = i * kThreads + tid;  // 16-byte slot in the LDS tile
-      const int key = pos / (DN / 8);
-      const int c = (pos % (DN / 8)) ^ KSwz<DN>::f(key);
-      koff[i] = (uint32_t)(key * k_st_b + c * 16);
+      const int key = pos / (DL / 8);
+      const int c = (pos % (DL / 8)) ^ KSwz<DL>::f(key);
+      // slots past the row's DN / 8 chunks (96-wide head) read past the
+      // buffer window: zeros, never read back
+      koff[i] = c < DN / 8 ? (uint32_t)(key * k_st_b + c * 16) : 0x80000000u;
     } else {
       const int pos = (i - KN) * kThreads + tid;
       const int key = pos / 8;
@@ -1017,8 +1033,8 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   for (int i = 0; i < VLOADS; ++i) {
     const int pos = i * kThreads + tid;
     const int key = pos / VCPR;
-    const int c = (pos % VCPR) ^ VSwz<DV>::f(key);
-    voff[i] = (uint32_t)(key * v_st_b + c * 16);
+    const int c = (pos % VCPR) ^ VSwz<DV_L>::f(key);
+    voff[i] = c < DV / 8 ? (uint32_t)(key * v_st_b + c * 16) : 0x80000000u;
   }
   // buffer of compile-time slot S
   auto kbuf = [&](auto S) __attribute__((device)) -> lds_char* {
@@ -1056,7 +1072,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
       const int c = (2 * (kk - DN / 16) + hf) ^ KSwz<64>::f(key);
       return kt + BN * DN * 2 + key * 128 + c * 16;
     } else {
-      const int c = (2 * kk + hf) ^ KSwz<DQK>::f(key);
+      const int c = (2 * kk + hf) ^ KSwz<DQK_L>::f(key);
       return kt + key * KRB + c * 16;
     }
   };
@@ -1103,7 +1119,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int key = 16 * kk + 8 * h + vkey_lane;
-      const int c = (4 * db + vchunk_lane) ^ VSwz<DV>::f(key);
+      const int c = (4 * db + vchunk_lane) ^ VSwz<DV_L>::f(key);
       const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) v4i16_t*)(vt + key * VRB + c * 16 + vbyte_lane));
       const u32x2_t xw = __builtin_bit_cast(u32x2_t, x);
@@ -1583,8 +1599,8 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
             const float v0 = o[n][db][4 * qd] * inv, v1 = o[n][db][4 * qd + 1] * inv;
             const float v2 = o[n][db][4 * qd + 2] * inv, v3 = o[n][db][4 * qd + 3] * inv;
             const int byte = d0 * (int)sizeof(OutT);
-            const int c = (byte >> 4) ^ (sr & (OUT_CPR - 1));
-            lds_char* dst = ostage + sr * OUT_RB + c * 16 + (byte & 15);
+            const int c = (byte >> 4) ^ (sr & (OUT_CPRL - 1));
+            lds_char* dst = ostage + sr * OUT_RBL + c * 16 + (byte & 15);
             if constexpr (sizeof(OutT) == 4) {
               *(__attribute__((address_space(3))) f32x4_t*)dst = (f32x4_t){v0, v1, v2, v3};
             } else {
@@ -1597,6 +1613,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
       __builtin_amdgcn_wave_barrier();
       constexpr int RPI = 64 / OUT_CPR;  // rows per wave-wide pass
       const int cc = lane % OUT_CPR;
+      const bool store_lane = lane < RPI * OUT_CPR;  // (12-chunk rows leave 4 lanes idle)
       const int qb = w0 + 32 * n + pass * STAGE_ROWS;  // first row of this pass
       // The pass's rows through one buffer window: rows past the sequence
       // end fall outside it and their stores are dropped.
@@ -1610,10 +1627,10 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
 #pragma unroll
       for (int it = 0; it < (STAGE_ROWS + RPI - 1) / RPI; ++it) {
         const int q = it * RPI + lane / OUT_CPR;
-        const int c = cc ^ (q & (OUT_CPR - 1));
-        if (q < STAGE_ROWS) {
+        const int c = cc ^ (q & (OUT_CPRL - 1));
+        if (store_lane && q < STAGE_ROWS) {
           const u32x4_t val =
-              *(const __attribute__((address_space(3))) u32x4_t*)(ostage + q * OUT_RB + c * 16);
+              *(const __attribute__((address_space(3))) u32x4_t*)(ostage + q * OUT_RBL + c * 16);
           __builtin_amdgcn_raw_buffer_store_b128(val, orsrc, (int)(q * o_st_b) + cc * 16, 0, 0);
         }
       }

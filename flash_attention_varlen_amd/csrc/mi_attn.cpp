@@ -47,6 +47,8 @@ bool dims_supported(int32_t dt, int32_t dqk, int32_t dv) {
   if (dqk == 64 && dv == 64) return true;
   if (dqk == 128 && dv == 128) return true;
   if (dqk == 192 && dv == 128) return dt != MI_ATTN_F32;
+  if (dqk == 256 && dv == 256) return dt != MI_ATTN_F32;
+  if (dqk == 96 && dv == 96) return dt != MI_ATTN_F32;
   return false;
 }
 
@@ -140,7 +142,7 @@ int check_fwd_params(const mi_attn_fwd_params* p, bool* empty) {
   if (!dims_supported(dt, p->d_qk, p->d_v))
     return fail(MI_ATTN_ERR_UNSUPPORTED,
                 "head dims (d_qk=%d, d_v=%d) unsupported for this dtype; supported: (64,64), "
-                "(128,128), and (192,128) for 16-bit inputs",
+                "(128,128), and (96,96), (192,128) and (256,256) for 16-bit inputs",
                 p->d_qk, p->d_v);
   if (p->hq <= 0 || p->hkv <= 0)
     return fail(MI_ATTN_ERR_INVALID_ARG, "head counts must be positive (hq=%d, hkv=%d)", p->hq,

@@ -26,8 +26,10 @@
  * no Lq x Lk matrix is ever stored.
  *
  * Supported set (anything else is refused, nothing is launched):
- *   (d_qk, d_v) in {(64,64), (128,128), (192,128)}; bf16 / fp16 inputs for
- *   all three, fp32 inputs for (64,64) and (128,128);
+ *   (d_qk, d_v) in {(64,64), (96,96), (128,128), (192,128), (256,256)};
+ *   bf16 / fp16 inputs for all five (the mtlattn page, section "Drop-in for
+ *   scaled_dot_product_attention", lists head dims 64, 96, 128 and 256 for
+ *   its fast path), fp32 inputs for (64,64) and (128,128);
  *   out dtype = input dtype or fp32; hq % hkv == 0; window > 0 needs causal.
  * The refusal follows the correct-or-refuse contract on the triton-msl
  * part-1 post (section "Correct-or-refuse"): an unsupported request returns

@@ -39,14 +39,17 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_tile_shape():
     assert fav.mi_attn_version() == 150
     for dt in (fav.BF16, fav.F16):
-        for dqk, dv in ((64, 64), (128, 128), (192, 128)):
+        for dqk, dv in ((64, 64), (96, 96), (128, 128), (192, 128), (256, 256)):
             bm, bn = fav.mi_attn_tile_shape(dt, dqk, dv)
             assert bm % 128 == 0 and bn % 32 == 0 and bm > 0 and bn > 0
     assert fav.mi_attn_tile_shape(fav.F32, 64, 64) == (128, 32)
     with pytest.raises(fav.MiAttnError):
         fav.mi_attn_tile_shape(fav.F32, 192, 128)
     with pytest.raises(fav.MiAttnError):
-        fav.mi_attn_tile_shape(fav.BF16, 96, 96)
+        fav.mi_attn_tile_shape(fav.BF16, 80, 80)
+    for dqk, dv in ((96, 96), (256, 256)):  # 16-bit only
+        with pytest.raises(fav.MiAttnError):
+            fav.mi_attn_tile_shape(fav.F32, dqk, dv)
 
 
 @pytest.mark.parametrize("cls,cname", [(fav.MiAttnFwdParams, "mi_attn_fwd_params"),
@@ -90,7 +93,10 @@ def _valid_params():
 REFUSALS = {
     "bad_dtype": (dict(in_dtype=7), fav.ERR_UNSUPPORTED),
     "bad_out_dtype": (dict(out_dtype=fav.F16), fav.ERR_UNSUPPORTED),
-    "head_dims": (dict(d_qk=96, d_v=96), fav.ERR_UNSUPPORTED),
+    "head_dims": (dict(d_qk=80, d_v=80), fav.ERR_UNSUPPORTED),
+    "head_dims_mixed": (dict(d_qk=256, d_v=128), fav.ERR_UNSUPPORTED),
+    "f32_d96": (dict(in_dtype=fav.F32, out_dtype=fav.F32, d_qk=96, d_v=96), fav.ERR_UNSUPPORTED),
+    "f32_d256": (dict(in_dtype=fav.F32, out_dtype=fav.F32, d_qk=256, d_v=256), fav.ERR_UNSUPPORTED),
     "f32_latent": (dict(in_dtype=fav.F32, out_dtype=fav.F32, d_qk=192, d_v=128), fav.ERR_UNSUPPORTED),
     "gqa_ratio": (dict(hq=6, hkv=4), fav.ERR_UNSUPPORTED),
     "zero_heads": (dict(hkv=0), fav.ERR_INVALID_ARG),
@@ -171,7 +177,7 @@ def test_version_1_0_struct_is_accepted():
     lib = fav.load_library()
     p.struct_size = fav.MiAttnFwdParams.bias_ranges.offset
     p.bias_ranges = 1 << 20  # beyond the 1.0 struct: must not be read
-    p.d_qk = p.d_v = 96
+    p.d_qk = p.d_v = 80
     assert lib.mi_attn_varlen_fwd(ctypes.byref(p), None) == fav.ERR_UNSUPPORTED
     assert "head dims" in fav.mi_attn_last_error()
 

@@ -4,8 +4,9 @@ kernels on two K/V slots; every step waiting for its own tile copies behind
 a barrier before any read).  A slot refilled while still being read, or a
 tile read before its copy landed, would make the results depend on timing;
 the variants remove that freedom, so their outputs must equal the shipping
-kernels' bit for bit on the four-slot instances (latent head, biased heads)
-and the two-slot ones (the GQA causal prefill)."""
+kernels' bit for bit on the four-slot instances (latent head, biased heads,
+the 256-wide head) and the two-slot ones (the GQA causal prefill, the 96-
+and 64-wide heads)."""
 import contextlib
 
 import pytest
@@ -33,6 +34,11 @@ CASES = {
                          dtype="bf16", causal=True, seed=93),
     "window_f16_d64": W(name="lds_window_f16_d64", seqlens_q=(1200,), seqlens_kv=(1200,), hq=4,
                         hkv=4, d_qk=64, d_v=64, dtype="f16", causal=True, window=300, seed=94),
+    # the 256-wide head runs four slots (one workgroup per CU), the 96-wide two
+    "causal_bf16_d256": W(name="lds_causal_bf16_d256", seqlens_q=(500, 77), seqlens_kv=(500, 77),
+                          hq=2, hkv=1, d_qk=256, d_v=256, dtype="bf16", causal=True, seed=95),
+    "full_f16_d96": W(name="lds_full_f16_d96", seqlens_q=(600, 31), seqlens_kv=(600, 31), hq=2,
+                      hkv=2, d_qk=96, d_v=96, dtype="f16", causal=False, seed=96),
 }
 
 
