@@ -66,6 +66,7 @@ class MiAttnFwdParams(ctypes.Structure):
         ("q_rope_stride_tok", ctypes.c_int64), ("q_rope_stride_head", ctypes.c_int64),
         ("k_rope_stride_tok", ctypes.c_int64), ("k_rope_stride_head", ctypes.c_int64),
         ("alibi_slopes", ctypes.c_void_p), ("alibi_stride_seq", ctypes.c_int64),
+        ("mask", ctypes.c_void_p),
     ]
 
 
@@ -234,10 +235,12 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     ``stream`` (a ``torch.cuda.Stream``, a raw ``hipStream_t`` handle, or
     None for the current stream) is where the kernel runs; outputs and the
     converted bias are allocated on it too.  The caller orders the inputs'
-    producers before it.  A bool ``attn_bias`` (True = visible) becomes an
-    fp32 0 / -inf tensor whose last dim is padded to a multiple of 4; an
-    fp32 bias whose strides are not multiples of 4 elements is copied into
-    such a layout.  ``bias_ranges`` (from ``bias_key_ranges`` on the same
+    producers before it.  A bool ``attn_bias`` (True = visible) becomes a
+    byte mask that the kernels read directly (copied, last dim padded to a
+    multiple of 4, only when its strides are not multiples of 4); an fp32
+    bias whose strides are not multiples of 4 elements is copied into such a
+    layout.  (The differentiable path turns a bool mask into the fp32 0 /
+    -inf bias the backward reads.)  ``bias_ranges`` (from ``bias_key_ranges`` on the same
     bias) lets the kernels skip key tiles that are -inf for all their rows.
 
     Latent-attention head: with ``q_rope`` ``[Tq, Hq, 64]`` and ``k_rope``
@@ -342,13 +345,19 @@ def bias_key_ranges(attn_bias, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int, s
         raise MiAttnError(ERR_INVALID_ARG, "attn_bias must be [Tq, H or 1, max_kv] on device")
     s_obj = _stream_of(stream, attn_bias.device)
     with torch.cuda.stream(s_obj):
-        bias = _aligned_bias(attn_bias) if attn_bias.dtype in (torch.float32, torch.bool) else None
-        if bias is None:
+        if attn_bias.dtype == torch.bool:
+            bias = _aligned_mask(attn_bias)
+        elif attn_bias.dtype == torch.float32:
+            bias = _aligned_bias(attn_bias)
+        else:
             raise MiAttnError(ERR_INVALID_ARG, "attn_bias must be fp32 or bool")
         tq, hb, cols = bias.shape
         ranges = torch.empty(hb, tq, 2, dtype=torch.int32, device=bias.device)
         p = MiAttnFwdParams()
-        p.bias = bias.data_ptr()
+        if bias.dtype == torch.uint8:
+            p.mask = bias.data_ptr()
+        else:
+            p.bias = bias.data_ptr()
         p.cu_seqlens_q, p.cu_seqlens_kv = cu_seqlens_q.data_ptr(), cu_seqlens_kv.data_ptr()
         p.num_seqs = cu_seqlens_q.numel() - 1
         p.max_seqlen_q = int(max_seqlen_q)
@@ -359,6 +368,23 @@ def bias_key_ranges(attn_bias, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int, s
         p.bias_stride_tok, p.bias_stride_head = bias.stride(0), bias.stride(1)
         mi_attn_bias_key_ranges(p, ranges.data_ptr(), int(s_obj.cuda_stream))
     return ranges
+
+
+def _aligned_mask(mask):
+    """uint8 view [Tq, H, C] of a bool mask (True = visible) whose strides are
+    multiples of 4 bytes and whose data is 4-byte aligned; copied into such a
+    layout (last dim padded to a multiple of 4) when it is not one."""
+    import torch
+    m = mask.view(torch.uint8)
+    if m.stride(-1) == 1 and m.stride(0) % 4 == 0 and m.stride(1) % 4 == 0 and \
+            m.data_ptr() % 4 == 0:
+        return m
+    cols = m.shape[2]
+    buf = torch.zeros(m.shape[0], m.shape[1], (cols + 3) // 4 * 4, dtype=torch.uint8,
+                      device=m.device)
+    view = buf[:, :, :cols]
+    view.copy_(m)
+    return view
 
 
 def _aligned_bias(bias):
@@ -394,7 +420,8 @@ def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen
                               "attn_bias must be fp32 or bool [Tq, H or 1, max_kv] on device")
         if bias.shape[0] != tq or bias.shape[1] not in (1, hq):
             raise MiAttnError(ERR_INVALID_ARG, "attn_bias must be [Tq, H or 1, max_kv]")
-        bias = _aligned_bias(bias)
+        # a bool mask goes to the kernels as bytes; an fp32 bias as it is
+        bias = _aligned_mask(bias) if bias.dtype == torch.bool else _aligned_bias(bias)
     if out is None:
         out = torch.empty(tq, hq, dv, dtype=out_dtype, device=q.device)
     elif out.shape != (tq, hq, dv) or out.dtype != out_dtype or out.stride(-1) != 1:
@@ -410,7 +437,10 @@ def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen
     p.out = out.data_ptr()
     p.lse = lse.data_ptr() if lse is not None else None
     p.cu_seqlens_q, p.cu_seqlens_kv = cu_seqlens_q.data_ptr(), cu_seqlens_kv.data_ptr()
-    p.bias = bias.data_ptr() if bias is not None else None
+    if bias is not None and bias.dtype == torch.uint8:
+        p.mask = bias.data_ptr()
+    else:
+        p.bias = bias.data_ptr() if bias is not None else None
     p.bias_ranges = bias_ranges.data_ptr() if bias_ranges is not None else None
     if q_rope is not None:
         p.q_rope, p.k_rope = q_rope.data_ptr(), k_rope.data_ptr()

@@ -30,6 +30,7 @@ struct KernelArgs {
   const void* q_rope;  // optional: last 64 dims of the 192-wide q / k (q, k then hold 128)
   const void* k_rope;
   const float* alibi;  // optional ALiBi slopes, alibi[seq * alibi_ss + head]
+  const uint8_t* mask;  // optional byte mask [total_q, bias_heads, bias_cols] (strides b_st, b_sh)
   int32_t* tile_counts;
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
   int64_t b_st, b_sh;

@@ -109,6 +109,16 @@ __device__ __forceinline__ int wave_max_i32(int x) {
   return x;
 }
 
+// Where the logits' additive bias comes from (the kernels' BSRC parameter):
+// an fp32 tensor, ALiBi slopes, or a byte mask (nonzero = visible, 0 = -inf).
+enum : int { kBiasTensor = 0, kBiasAlibi = 1, kBiasMask = 2 };
+
+// The four bias values of four consecutive keys of a byte-mask row.
+__device__ __forceinline__ f32x4_t mask_bias4(uint32_t w) {
+  return (f32x4_t){(w & 0xffu) ? 0.0f : kNegInf, (w & 0xff00u) ? 0.0f : kNegInf,
+                   (w & 0xff0000u) ? 0.0f : kNegInf, (w & 0xff000000u) ? 0.0f : kNegInf};
+}
+
 // ALiBi bias of query position pos (in key coordinates) for key `key`:
 // minus the head's slope times their distance.  The distance is an exact
 // integer below 2^24, so the value is the product rounded once.
@@ -255,9 +265,9 @@ struct Geo {
 // ----------------------------------------------------------------------------
 // The kernel.
 // ----------------------------------------------------------------------------
-// ALIBI: the bias is computed from per-head slopes instead of read (BIAS
-// is then set too: the logits carry a bias either way).
-template <typename T, int DQK, int DV, bool BIAS, typename OutT, bool ALIBI = false>
+// BSRC: where the bias comes from when BIAS is set (kBiasTensor, kBiasAlibi:
+// computed from per-head slopes, kBiasMask: a byte mask).
+template <typename T, int DQK, int DV, bool BIAS, typename OutT, int BSRC = kBiasTensor>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs a) {
   using G = Geo<T, DQK, DV>;
   using E = Elem<T>;
@@ -301,7 +311,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
   if (causal) kv_hi = min(lk, r1 - 1 + off + 1);
   int kv_lo = 0;
   if (W > 0) kv_lo = max(0, r0 + off - W + 1);
-  if constexpr (BIAS && !ALIBI) {
+  if constexpr (BIAS && BSRC != kBiasAlibi) {
     // keys outside the hull of the rows' bias ranges have a -inf bias
     if (a.bias_ranges != nullptr) {
       const int32_t* rg = a.bias_ranges +
@@ -450,9 +460,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
 
   const float c_scale = a.scale_log2;
   const float* brow = nullptr;
-  const float neg_slope = ALIBI ? -a.alibi[(int64_t)seq * a.alibi_ss + head] : 0.0f;
-  if constexpr (BIAS && !ALIBI) {
+  const uint8_t* mrow = nullptr;
+  const float neg_slope = BSRC == kBiasAlibi ? -a.alibi[(int64_t)seq * a.alibi_ss + head] : 0.0f;
+  if constexpr (BIAS && BSRC == kBiasTensor) {
     brow = a.bias + (int64_t)(cq0 + (row_ok ? my_row : 0)) * a.b_st +
+           (int64_t)(a.bias_heads == 1 ? 0 : head) * a.b_sh;
+  }
+  if constexpr (BIAS && BSRC == kBiasMask) {
+    mrow = a.mask + (int64_t)(cq0 + (row_ok ? my_row : 0)) * a.b_st +
            (int64_t)(a.bias_heads == 1 ? 0 : head) * a.b_sh;
   }
 
@@ -519,9 +534,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
             const int key0 = kb + 32 * mb + 8 * qd + 4 * hf;
             f32x4_t bv;
             const int blim = min(lk, a.bias_cols);  // bias columns read: below both
-            if constexpr (ALIBI) {
+            if constexpr (BSRC == kBiasAlibi) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) bv[e] = alibi_bias(neg_slope, my_row + off, key0 + e);
+            } else if constexpr (BSRC == kBiasMask) {
+              uint32_t w = 0xffffffffu;  // past the mask's columns: visible (bias 0)
+              if (row_ok && key0 + 3 < blim) {
+                w = *reinterpret_cast<const uint32_t*>(mrow + key0);
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (row_ok && key0 + e < blim && mrow[key0 + e] == 0) w &= ~(0xffu << (8 * e));
+              }
+              bv = mask_bias4(w);
             } else if (row_ok && key0 + 3 < blim) {
               bv = *reinterpret_cast<const f32x4_t*>(brow + key0);
             } else {
@@ -804,12 +829,12 @@ struct WaveBlocks {
 // k_rope tensors (the latent-attention head without concatenation); the K
 // tile then holds a 128-wide "nope" part and a 64-wide "rope" part.
 template <typename T, int DQK, int DV, bool BIAS, typename OutT, bool ROPE = false,
-          bool ALIBI = false>
+          int BSRC = kBiasTensor>
 __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void attn_fwd16p_kernel(
     const KernelArgs a) {
   using E = Elem<T>;
   static_assert(!ROPE || DQK == 192, "split nope / rope operands only for the 192-wide head");
-  static_assert(!ALIBI || BIAS, "ALiBi logits take the biased path");
+  static_assert(BSRC == kBiasTensor || BIAS, "ALiBi and masks take the biased path");
   constexpr int DN = ROPE ? DQK - 64 : DQK;  // width of the q / k operand (the nope part)
   // A row's running max m lags the true row max by less than
   // 2^kRescaleThreshold: O and l are rescaled between tiles only when a row's
@@ -959,7 +984,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   // skipped exactly as masked tiles are; a wave also stops after the last
   // tile its own rows can see.
   int wave_bias_hi = lk;
-  if constexpr (BIAS && !ALIBI) {
+  if constexpr (BIAS && BSRC != kBiasAlibi) {
     if (a.bias_ranges != nullptr) {
       const int32_t* rg = a.bias_ranges +
           ((int64_t)(a.bias_heads == 1 ? 0 : head) * a.total_q + cq0) * 2;
@@ -1148,11 +1173,18 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   // the exponent's argument multiplies them by log2(e).
   const float c_nat = a.scale_log2 * (1.0f / kLog2e);
   const float* brow[NB];
-  const float neg_slope = ALIBI ? -a.alibi[(int64_t)seq * a.alibi_ss + head] : 0.0f;
-  if constexpr (BIAS && !ALIBI) {
+  const uint8_t* mrow[NB];
+  const float neg_slope = BSRC == kBiasAlibi ? -a.alibi[(int64_t)seq * a.alibi_ss + head] : 0.0f;
+  if constexpr (BIAS && BSRC == kBiasTensor) {
 #pragma unroll
     for (int n = 0; n < NB; ++n)
       brow[n] = a.bias + (int64_t)(cq0 + (row_ok[n] ? my_row[n] : 0)) * a.b_st +
+                (int64_t)(a.bias_heads == 1 ? 0 : head) * a.b_sh;
+  }
+  if constexpr (BIAS && BSRC == kBiasMask) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      mrow[n] = a.mask + (int64_t)(cq0 + (row_ok[n] ? my_row[n] : 0)) * a.b_st +
                 (int64_t)(a.bias_heads == 1 ? 0 : head) * a.b_sh;
   }
 
@@ -1232,10 +1264,20 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           const int key0 = kb + 32 * mb + 8 * qd + 4 * hf;
-          if constexpr (ALIBI) {
+          if constexpr (BSRC == kBiasAlibi) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               bv[n][mb][qd][e] = alibi_bias(neg_slope, my_row[n] + off, key0 + e);
+          } else if constexpr (BSRC == kBiasMask) {
+            uint32_t w = 0xffffffffu;  // past the mask's columns: visible (bias 0)
+            if (row_ok[n] && key0 + 3 < blim) {
+              w = *reinterpret_cast<const uint32_t*>(mrow[n] + key0);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (row_ok[n] && key0 + e < blim && mrow[n][key0 + e] == 0) w &= ~(0xffu << (8 * e));
+            }
+            bv[n][mb][qd] = mask_bias4(w);
           } else if (row_ok[n] && key0 + 3 < blim) {
             bv[n][mb][qd] = *reinterpret_cast<const f32x4_t*>(brow[n] + key0);
           } else {
@@ -1644,24 +1686,29 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   }
 }
 
-template <typename T, int DQK, int DV, bool BIAS, typename OutT, bool ROPE, bool ALIBI = false>
+template <typename T, int DQK, int DV, bool BIAS, typename OutT, bool ROPE, int BSRC = kBiasTensor>
 hipError_t launch_one(const KernelArgs& a, dim3 grid, hipStream_t stream) {
   if constexpr (Elem<T>::kWide) {
-    hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, BIAS, OutT, ALIBI>), grid, dim3(kThreads), 0,
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DQK, DV, BIAS, OutT, BSRC>), grid, dim3(kThreads), 0,
                        stream, a);
   } else {
-    hipLaunchKernelGGL((attn_fwd16p_kernel<T, DQK, DV, BIAS, OutT, ROPE, ALIBI>), grid,
+    hipLaunchKernelGGL((attn_fwd16p_kernel<T, DQK, DV, BIAS, OutT, ROPE, BSRC>), grid,
                        dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
 
-// a.alibi set: the bias comes from the slopes (a tensor bias is refused with it)
+// a.alibi / a.mask set: the bias comes from the slopes / the byte mask (the
+// host refuses them together with each other or with a bias tensor)
 template <typename T, int DQK, int DV, bool ROPE>
 hipError_t launch_rope(const KernelArgs& a, bool bias, bool out_f32, dim3 grid, hipStream_t s) {
   if (a.alibi != nullptr) {
-    return out_f32 ? launch_one<T, DQK, DV, true, float, ROPE, true>(a, grid, s)
-                   : launch_one<T, DQK, DV, true, T, ROPE, true>(a, grid, s);
+    return out_f32 ? launch_one<T, DQK, DV, true, float, ROPE, kBiasAlibi>(a, grid, s)
+                   : launch_one<T, DQK, DV, true, T, ROPE, kBiasAlibi>(a, grid, s);
+  }
+  if (a.mask != nullptr) {
+    return out_f32 ? launch_one<T, DQK, DV, true, float, ROPE, kBiasMask>(a, grid, s)
+                   : launch_one<T, DQK, DV, true, T, ROPE, kBiasMask>(a, grid, s);
   }
   if (bias) {
     return out_f32 ? launch_one<T, DQK, DV, true, float, ROPE>(a, grid, s)

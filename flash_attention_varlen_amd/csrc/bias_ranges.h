@@ -7,7 +7,8 @@
 namespace mi_attn {
 
 struct BiasRangeArgs {
-  const float* bias;
+  const float* bias;     // fp32 bias, or
+  const uint8_t* mask;   // a byte mask (nonzero = visible), b_st / b_sh in bytes
   const int32_t* cu_q;
   const int32_t* cu_kv;
   int32_t* ranges;  // [bias_heads, total_q, 2]

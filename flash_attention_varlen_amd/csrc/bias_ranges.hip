@@ -67,13 +67,56 @@ __global__ __launch_bounds__(256) void bias_key_ranges_kernel(const BiasRangeArg
   }
 }
 
+// The same for a byte mask: the first and one-past-last key whose mask
+// byte is nonzero; 4 keys per lane and 32-bit load.
+__global__ __launch_bounds__(256) void mask_key_ranges_kernel(const BiasRangeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int seq = blockIdx.y;
+  const int hb = blockIdx.z;
+  const int r = blockIdx.x * 4 + wave;
+  const int cq0 = a.cu_q[seq];
+  const int lq = a.cu_q[seq + 1] - cq0;
+  if (r >= lq) return;
+  const int lk = min(a.cu_kv[seq + 1] - a.cu_kv[seq], a.bias_cols);
+  const uint8_t* row = a.mask + (int64_t)(cq0 + r) * a.b_st + (int64_t)hb * a.b_sh;
+  int lo = 0x7fffffff, hi = 0;
+  const int full = lk & ~3;
+  for (int j0 = 4 * lane; j0 < full; j0 += 4 * 64) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(row + j0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((w >> (8 * e)) & 0xffu) {
+        lo = min(lo, j0 + e);
+        hi = max(hi, j0 + e + 1);
+      }
+  }
+  if (lane < lk - full && row[full + lane] != 0) {
+    lo = min(lo, full + lane);
+    hi = max(hi, full + lane + 1);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, __shfl_xor(lo, o));
+    hi = max(hi, __shfl_xor(hi, o));
+  }
+  if (lane == 0) {
+    int32_t* out = a.ranges + ((int64_t)hb * a.total_q + cq0 + r) * 2;
+    out[0] = hi > 0 ? lo : 0;
+    out[1] = hi;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_bias_key_ranges(const BiasRangeArgs& a, int max_seqlen_q, int num_seqs,
                                   int bias_heads, hipStream_t stream) {
   (void)hipGetLastError();
   const dim3 grid((unsigned)((max_seqlen_q + 3) / 4), (unsigned)num_seqs, (unsigned)bias_heads);
-  hipLaunchKernelGGL(bias_key_ranges_kernel, grid, dim3(256), 0, stream, a);
+  if (a.mask != nullptr)
+    hipLaunchKernelGGL(mask_key_ranges_kernel, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(bias_key_ranges_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -231,10 +231,14 @@ int check_fwd_params(const mi_attn_fwd_params* p, bool* empty) {
                 p->hq, p->d_v);
   if (dt != MI_ATTN_F32 && p->out_stride_tok * elem_size(p->out_dtype) * 32 > INT32_MAX)
     return fail(MI_ATTN_ERR_UNSUPPORTED, "out token stride too large (more than 64 MiB per token)");
-  const bool has_bias = p->bias != nullptr;
+  if (p->mask != nullptr && p->bias != nullptr)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "give a bias or a mask, not both");
+  const bool has_mask = p->mask != nullptr;
+  const bool has_bias = p->bias != nullptr || has_mask;
   if (p->alibi_slopes != nullptr) {
     if (has_bias)
-      return fail(MI_ATTN_ERR_UNSUPPORTED, "ALiBi slopes and a bias tensor together are not supported");
+      return fail(MI_ATTN_ERR_UNSUPPORTED,
+                  "ALiBi slopes together with a bias tensor or a mask are not supported");
     if ((reinterpret_cast<uintptr_t>(p->alibi_slopes) & 3u) != 0 || p->alibi_stride_seq < 0)
       return fail(MI_ATTN_ERR_INVALID_ARG,
                   "alibi_slopes must be 4-byte aligned with a non-negative sequence stride");
@@ -242,10 +246,16 @@ int check_fwd_params(const mi_attn_fwd_params* p, bool* empty) {
   if (has_bias) {
     if (p->bias_heads != 1 && p->bias_heads != p->hq)
       return fail(MI_ATTN_ERR_UNSUPPORTED, "bias_heads must be 1 or hq (got %d)", p->bias_heads);
-    if (!aligned16(p->bias) || p->bias_stride_tok < 0 || p->bias_stride_head < 0 ||
-        p->bias_stride_tok % 4 != 0 || p->bias_stride_head % 4 != 0)
+    if (has_mask) {
+      if ((reinterpret_cast<uintptr_t>(p->mask) & 3u) != 0 || p->bias_stride_tok < 0 ||
+          p->bias_stride_head < 0 || p->bias_stride_tok % 4 != 0 || p->bias_stride_head % 4 != 0)
+        return fail(MI_ATTN_ERR_INVALID_ARG,
+                    "mask must be 4-byte aligned with strides that are multiples of 4 bytes");
+    } else if (!aligned16(p->bias) || p->bias_stride_tok < 0 || p->bias_stride_head < 0 ||
+               p->bias_stride_tok % 4 != 0 || p->bias_stride_head % 4 != 0) {
       return fail(MI_ATTN_ERR_INVALID_ARG,
                   "bias must be 16-byte aligned with strides that are multiples of 4");
+    }
     if (p->bias_cols <= 0) return fail(MI_ATTN_ERR_INVALID_ARG, "bias_cols must be > 0");
     if (p->bias_ranges != nullptr && (reinterpret_cast<uintptr_t>(p->bias_ranges) & 7u) != 0)
       return fail(MI_ATTN_ERR_INVALID_ARG, "bias_ranges must be 8-byte aligned");
@@ -281,6 +291,7 @@ int plan_decode(const mi_attn_fwd_params* p, int64_t max_seqlen_kv, int32_t num_
     return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode takes no q_rope / k_rope");
   if (p->alibi_slopes != nullptr)
     return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode takes no ALiBi slopes");
+  if (p->mask != nullptr) return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode takes no mask");
   if (num_splits < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "num_splits must be >= 0 (0 = auto)");
   if (max_seqlen_kv < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "max_seqlen_kv must be >= 0");
   const int64_t group = p->hq / p->hkv;
@@ -398,7 +409,7 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
   bool empty = false;
   const int rc_check = check_fwd_params(p, &empty);
   if (rc_check != MI_ATTN_OK || empty) return rc_check;
-  const bool has_bias = p->bias != nullptr;
+  const bool has_bias = p->bias != nullptr || p->mask != nullptr;  // a tensor bias or a byte mask
 
   int32_t bm = 0, bn = 0;
   if (mi_attn_tile_shape(dt, p->d_qk, p->d_v, &bm, &bn) != MI_ATTN_OK) return MI_ATTN_ERR_UNSUPPORTED;
@@ -425,6 +436,7 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
   a.cu_q = p->cu_seqlens_q;
   a.cu_kv = p->cu_seqlens_kv;
   a.bias = p->bias;
+  a.mask = p->mask;
   a.bias_ranges = has_bias ? p->bias_ranges : nullptr;
   a.q_rope = p->q_rope;
   a.k_rope = p->k_rope;
@@ -767,16 +779,20 @@ int mi_attn_bias_key_ranges(const mi_attn_fwd_params* p_in, int32_t* ranges, voi
   const int rc_copy = copy_params(p_in, &local);
   if (rc_copy != MI_ATTN_OK) return rc_copy;
   const mi_attn_fwd_params* p = &local;
-  if (p->bias == nullptr || ranges == nullptr || p->cu_seqlens_q == nullptr ||
+  const bool has_mask = p->mask != nullptr;
+  if ((p->bias == nullptr) == !has_mask || ranges == nullptr || p->cu_seqlens_q == nullptr ||
       p->cu_seqlens_kv == nullptr)
-    return fail(MI_ATTN_ERR_INVALID_ARG, "bias, ranges and both cu_seqlens are required");
+    return fail(MI_ATTN_ERR_INVALID_ARG,
+                "a bias or a mask (one of them), ranges and both cu_seqlens are required");
   if (p->hq <= 0 || (p->bias_heads != 1 && p->bias_heads != p->hq))
     return fail(MI_ATTN_ERR_UNSUPPORTED, "bias_heads must be 1 or hq (got %d, hq %d)",
                 p->bias_heads, p->hq);
-  if (!aligned16(p->bias) || p->bias_stride_tok < 0 || p->bias_stride_head < 0 ||
-      p->bias_stride_tok % 4 != 0 || p->bias_stride_head % 4 != 0)
-    return fail(MI_ATTN_ERR_INVALID_ARG,
-                "bias must be 16-byte aligned with strides that are multiples of 4");
+  if (has_mask ? ((reinterpret_cast<uintptr_t>(p->mask) & 3u) != 0)
+               : !aligned16(p->bias))
+    return fail(MI_ATTN_ERR_INVALID_ARG, "bias must be 16-byte aligned, a mask 4-byte aligned");
+  if (p->bias_stride_tok < 0 || p->bias_stride_head < 0 || p->bias_stride_tok % 4 != 0 ||
+      p->bias_stride_head % 4 != 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "bias / mask strides must be multiples of 4");
   if ((reinterpret_cast<uintptr_t>(ranges) & 7u) != 0)
     return fail(MI_ATTN_ERR_INVALID_ARG, "ranges must be 8-byte aligned");
   if (p->bias_cols <= 0) return fail(MI_ATTN_ERR_INVALID_ARG, "bias_cols must be > 0");
@@ -791,6 +807,7 @@ int mi_attn_bias_key_ranges(const mi_attn_fwd_params* p_in, int32_t* ranges, voi
   }
   mi_attn::BiasRangeArgs a{};
   a.bias = p->bias;
+  a.mask = p->mask;
   a.cu_q = p->cu_seqlens_q;
   a.cu_kv = p->cu_seqlens_kv;
   a.ranges = ranges;

@@ -167,6 +167,18 @@ typedef struct mi_attn_fwd_params {
    * bias tensor. */
   const float* alibi_slopes;
   int64_t alibi_stride_seq;
+  /* Added in version 1.5 (NULL for older callers): a boolean mask read by
+   * the kernels in place of the fp32 bias, one byte per element (the
+   * mtlattn 0.3.0 page, section "Use", turns a bool mask into the 0 / -inf
+   * additive bias; reading the bytes moves a quarter of the fp32 bias's
+   * bytes).  uint8 [total_q, bias_heads, bias_cols], nonzero = visible
+   * (bias 0), 0 = masked (bias -inf), addressed with bias_heads, bias_cols,
+   * bias_stride_tok and bias_stride_head exactly as the bias (strides in
+   * bytes here, multiples of 4; 4-byte aligned).  Columns at or past
+   * bias_cols count as visible, as a bias of 0 does.  bias_ranges (from
+   * mi_attn_bias_key_ranges with this mask) apply as for a bias.  Not
+   * together with bias or alibi_slopes; the decode entry points refuse it. */
+  const uint8_t* mask;
 } mi_attn_fwd_params;
 
 /*
@@ -180,10 +192,11 @@ typedef struct mi_attn_fwd_params {
 int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream);
 
 /*
- * Key ranges of the bias rows: for every bias head hb and query row t (global)
+ * Key ranges of the bias (or mask) rows: for every bias head hb and query row t (global)
  * of sequence s, ranges[(hb * total_q + t) * 2 + 0 .. 1] = [lo, hi), the
  * first and one-past-last key j < min(Lk(s), bias_cols) whose bias value
- * p->bias[t][hb][j] is not -inf ([0, 0) when there is none).  Reads the
+ * p->bias[t][hb][j] is not -inf, or with p->mask set (and no bias) whose
+ * mask byte is nonzero ([0, 0) when there is none).  Reads the
  * bias, cu_seqlens, sizes and strides of *p (the same struct a forward call
  * takes; q/k/v/out are not used) and writes ranges, an int32 device buffer
  * of 2 * bias_heads * total_q elements, 8-byte aligned, owned by the caller.

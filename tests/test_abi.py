@@ -144,6 +144,17 @@ REFUSALS = {
                              bias_stride_tok=64, bias_stride_head=0), fav.ERR_UNSUPPORTED),
     "alibi_misaligned": (dict(alibi_slopes=(1 << 20) + 2), fav.ERR_INVALID_ARG),
     "alibi_negative_stride": (dict(alibi_slopes=1 << 20, alibi_stride_seq=-8), fav.ERR_INVALID_ARG),
+    # byte mask: not with a bias or ALiBi; 4-byte aligned, strides multiples of 4 bytes
+    "mask_and_bias": (dict(mask=1 << 20, bias=1 << 20, bias_heads=1, bias_cols=64,
+                           bias_stride_tok=64, bias_stride_head=0), fav.ERR_INVALID_ARG),
+    "mask_and_alibi": (dict(mask=1 << 20, alibi_slopes=1 << 20, bias_heads=1, bias_cols=64,
+                            bias_stride_tok=64, bias_stride_head=0), fav.ERR_UNSUPPORTED),
+    "mask_misaligned": (dict(mask=(1 << 20) + 2, bias_heads=1, bias_cols=64, bias_stride_tok=64,
+                             bias_stride_head=0), fav.ERR_INVALID_ARG),
+    "mask_odd_stride": (dict(mask=1 << 20, bias_heads=1, bias_cols=63, bias_stride_tok=63,
+                             bias_stride_head=0), fav.ERR_INVALID_ARG),
+    "mask_heads": (dict(mask=1 << 20, bias_heads=3, bias_cols=64, bias_stride_tok=64,
+                        bias_stride_head=64), fav.ERR_UNSUPPORTED),
     # with split operands q / k hold 128 dims; without them a 128-wide stride is short of 192
     "latent_short_q_stride": (dict(d_qk=192, q_stride_tok=128, q_stride_head=0, hq=2, hkv=2,
                                    out_stride_tok=2 * 128), fav.ERR_UNSUPPORTED),
@@ -184,6 +195,8 @@ def test_version_1_0_struct_is_accepted():
 
 RANGE_REFUSALS = {
     "no_bias": (dict(bias=None), fav.ERR_INVALID_ARG),
+    "bias_and_mask": (dict(mask=1 << 20), fav.ERR_INVALID_ARG),
+    "misaligned_mask": (dict(bias=None, mask=(1 << 20) + 1), fav.ERR_INVALID_ARG),
     "bias_heads": (dict(bias_heads=3), fav.ERR_UNSUPPORTED),
     "odd_bias_stride": (dict(bias_stride_tok=66), fav.ERR_INVALID_ARG),
     "zero_cols": (dict(bias_cols=0), fav.ERR_INVALID_ARG),
@@ -261,6 +274,8 @@ DECODE_REFUSALS = {
     "fp32": (dict(in_dtype=fav.F32, out_dtype=fav.F32), 1 << 20, fav.ERR_UNSUPPORTED),
     "latent_dims": (dict(d_qk=192, d_v=128), 1 << 20, fav.ERR_UNSUPPORTED),
     "alibi": (dict(alibi_slopes=1 << 20), 1 << 20, fav.ERR_UNSUPPORTED),
+    "mask": (dict(mask=1 << 20, bias_heads=1, bias_cols=64, bias_stride_tok=64,
+                  bias_stride_head=0), 1 << 20, fav.ERR_UNSUPPORTED),
     "rope": (dict(q_rope=1 << 20, k_rope=1 << 20, q_rope_stride_tok=8 * 64, q_rope_stride_head=64,
                   k_rope_stride_tok=2 * 64, k_rope_stride_head=64), 1 << 20, fav.ERR_UNSUPPORTED),
     "bias": (dict(bias=1 << 20, bias_heads=1, bias_cols=64, bias_stride_tok=64, bias_stride_head=64),

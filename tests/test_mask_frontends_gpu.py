@@ -86,3 +86,48 @@ def test_forward_with_ranges_is_exact(case):
     assert int(tc1.sum()) < int(tc0.sum())
     ref_out, ref_lse = run_oracle(inp)
     check(case, out1.cpu().numpy(), lse1.cpu().numpy(), ref_out, ref_lse, w.dtype)
+
+
+# ---------------------------------------------------------------- byte masks
+def _bool_mask(seqlens, heads, cols, seed):
+    """True = visible: the finite entries of the banded bias."""
+    return torch.isfinite(_banded_bias(seqlens, heads, cols, seed))
+
+
+@pytest.mark.parametrize("case", ["bf16_d128_h1", "f16_d64_hq", "bf16_d192_hq", "f32_d64_h1",
+                                  "bf16_d256_h1", "f16_d96_hq"])
+@pytest.mark.parametrize("flags", ["full", "causal_window"])
+def test_byte_mask_equals_fp32_bias(case, flags):
+    """A bool mask read by the kernels as bytes gives bit for bit the result
+    of the same mask as an fp32 0 / -inf bias (same logits, same sums); odd
+    column counts go through the padded copy; the key ranges of the mask
+    equal those of the bias and skipping with them changes nothing."""
+    dt, d, h = case.split("_")
+    d = int(d[1:])
+    dqk, dv = (192, 128) if d == 192 else (d, d)
+    lens = (300, 1, 77)
+    hq = 4
+    causal = flags != "full"
+    w = W(name=f"bytemask_{case}", seqlens_q=lens, seqlens_kv=lens, hq=hq, hkv=2, d_qk=dqk, d_v=dv,
+          dtype=dt, causal=causal, window=90 if causal else 0, seed=73)
+    inp = workloads.make_inputs(w)
+    mask = _bool_mask(lens, 1 if h == "h1" else hq, 301, seed=74)
+    fbias = torch.zeros(mask.shape).masked_fill_(~mask, float("-inf"))
+    dev = "cuda"
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    cq, ck = inp.cu_seqlens_q.to(dev), inp.cu_seqlens_kv.to(dev)
+    say(f"[byte mask] {case} {flags}")
+    kw = dict(causal=causal, window=w.window, out_dtype=torch.float32, return_lse=True)
+    out_m, lse_m = fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, attn_bias=mask.to(dev), **kw)
+    out_b, lse_b = fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, attn_bias=fbias.to(dev), **kw)
+    rg_m = fav.bias_key_ranges(mask.to(dev), cq, ck, w.max_seqlen_q)
+    rg_b = fav.bias_key_ranges(fbias.to(dev), cq, ck, w.max_seqlen_q)
+    out_r, lse_r = fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, attn_bias=mask.to(dev),
+                                        bias_ranges=rg_m, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(rg_m, rg_b)
+    assert torch.equal(out_m, out_b) and torch.equal(lse_m, lse_b)
+    assert torch.equal(out_r, out_m) and torch.equal(lse_r, lse_m)
+    inp.bias = fbias
+    ref_out, ref_lse = run_oracle(inp)
+    check(f"bytemask_{case}", out_m.cpu().numpy(), lse_m.cpu().numpy(), ref_out, ref_lse, w.dtype)
