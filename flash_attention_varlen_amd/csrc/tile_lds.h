@@ -12,8 +12,19 @@ namespace {
 // ----------------------------------------------------------------------------
 // LDS tiles of the backward and decode kernels.  A tile is `ROWS` rows of D
 // 16-bit elements, row-major, with the 16-byte chunks of row r XOR-swizzled
-// by VSwz<D>::f(r) (the layout the transposing read below expects).
+// by TSwz<D>::f(r).  The tiles are read both ways: as row fragments (one
+// 16-byte chunk of 16 different rows per LDS cycle: the swizzle must map
+// those rows to 16 different bank quads, i.e. be a bijection of the row
+// bits that the row stride leaves inside one 256-byte bank line) and through
+// the transposing read (four consecutive rows per read: their chunks must
+// fall in four different 4-chunk groups, which VSwz's high bits give).  The
+// low two bits, XOR-ed with (r >> 2) & 3, complete the bijection without
+// changing the 4-chunk group, so both reads are free of bank conflicts.
 // ----------------------------------------------------------------------------
+template <int D>
+struct TSwz {
+  __device__ static int f(int row) { return VSwz<D>::f(row) | ((row >> 2) & 3); }
+};
 
 // Per-lane byte offsets (from the tile's first row in global memory) of the
 // chunks this thread copies, for LOADS copies of NT x 16 bytes (NT threads
@@ -25,7 +36,7 @@ __device__ __forceinline__ void tile_offsets(uint32_t (&off)[LOADS], int64_t st_
   for (int i = 0; i < LOADS; ++i) {
     const int pos = i * NT + tid;
     const int row = pos / CPR;
-    const int c = (pos % CPR) ^ VSwz<D>::f(row);
+    const int c = (pos % CPR) ^ TSwz<D>::f(row);
     off[i] = (uint32_t)(row * st_b + c * 16);
   }
 }
@@ -48,7 +59,7 @@ __device__ __forceinline__ void load_tile(const char* base, int64_t st_b, int ro
 // (an MFMA operand row fragment).
 template <int D>
 __device__ __forceinline__ u32x4_t row_frag(const lds_char* tile, int row, int ks, int hf) {
-  const int c = (2 * ks + hf) ^ VSwz<D>::f(row);
+  const int c = (2 * ks + hf) ^ TSwz<D>::f(row);
   return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(tile + row * (D * 2) + c * 16);
 }
 
@@ -65,7 +76,7 @@ __device__ __forceinline__ u32x4_t tr_frag(const lds_char* tile, int ks, int db,
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int row = 16 * ks + 8 * h + key_lane;
-    const int c = (4 * db + chunk_lane) ^ VSwz<D>::f(row);
+    const int c = (4 * db + chunk_lane) ^ TSwz<D>::f(row);
     const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) v4i16_t*)(tile + row * (D * 2) + c * 16 + byte_lane));
     const u32x2_t xw = __builtin_bit_cast(u32x2_t, x);
