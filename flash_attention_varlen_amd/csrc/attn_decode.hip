@@ -236,36 +236,73 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   }
 }
 
-// One thread per (row, head, 4 consecutive d): merge the chunks.
+// One workgroup per (row, head): merge the chunks.  Wave 0 finds the max M
+// of the chunks' running maxima and the merged sum L; then every thread
+// takes 4 consecutive dims of a strided subset of the chunks, and the
+// partial sums meet in LDS (fixed order: the result does not depend on
+// timing).
 template <typename OutT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
-  const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  constexpr int DG = D / 4;            // 4-dim groups per row
+  constexpr int CL = 256 / DG;         // chunk lanes: threads per dim group
+  __shared__ float s_ml[2];
+  __shared__ __attribute__((aligned(16))) float s_part[CL][D];
+  const int tid = threadIdx.x;
   const int64_t pairs = a.total_q * a.hq;
-  if (item >= pairs * (D / 4)) return;
-  const int64_t pair = item / (D / 4);
-  const int d0 = 4 * (int)(item % (D / 4));
+  const int64_t pair = blockIdx.x;
   const int64_t t = pair / a.hq;
   const int h = (int)(pair % a.hq);
-  float M = kNegInf;
-  for (int c = 0; c < a.n_chunks; ++c) M = __builtin_fmaxf(M, a.ws_ml[2 * ((int64_t)c * pairs + pair)]);
-  float L = 0.0f, acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (tid < 64) {
+    float m = kNegInf;
+    for (int c = tid; c < a.n_chunks; c += 64) m = __builtin_fmaxf(m, a.ws_ml[2 * ((int64_t)c * pairs + pair)]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+    float l = 0.0f;
+    if (m != kNegInf) {
+      for (int c = tid; c < a.n_chunks; c += 64) {
+        const int64_t w = (int64_t)c * pairs + pair;
+        const float mc = a.ws_ml[2 * w];
+        if (mc != kNegInf) l += a.ws_ml[2 * w + 1] * fast_exp2(mc - m);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+    if (tid == 0) {
+      s_ml[0] = m;
+      s_ml[1] = l;
+    }
+  }
+  __syncthreads();
+  const float M = s_ml[0], L = s_ml[1];
+  const int dg = tid % DG, cl = tid / DG;
+  const int d0 = 4 * dg;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (M != kNegInf) {
-    for (int c = 0; c < a.n_chunks; ++c) {
+    for (int c = cl; c < a.n_chunks; c += CL) {
       const int64_t w = (int64_t)c * pairs + pair;
       const float m = a.ws_ml[2 * w];
       if (m == kNegInf) continue;
       const float f = fast_exp2(m - M);
-      L += a.ws_ml[2 * w + 1] * f;
       const f32x4_t ov = *reinterpret_cast<const f32x4_t*>(a.ws_o + w * D + d0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] += ov[e] * f;
     }
   }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  OutT* op = reinterpret_cast<OutT*>(a.out) + t * a.o_st + (int64_t)h * a.o_sh + d0;
-  store4<OutT>(op, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-  if (d0 == 0 && a.lse != nullptr)
-    a.lse[(int64_t)h * a.total_q + t] = L > 0.0f ? (M + fast_log2(L)) * kLn2 : kNegInf;
+  *reinterpret_cast<f32x4_t*>(&s_part[cl][d0]) = (f32x4_t){acc[0], acc[1], acc[2], acc[3]};
+  __syncthreads();
+  if (cl == 0) {
+#pragma unroll
+    for (int j = 1; j < CL; ++j) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&s_part[j][d0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += v[e];
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    OutT* op = reinterpret_cast<OutT*>(a.out) + t * a.o_st + (int64_t)h * a.o_sh + d0;
+    store4<OutT>(op, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    if (d0 == 0 && a.lse != nullptr)
+      a.lse[(int64_t)h * a.total_q + t] = L > 0.0f ? (M + fast_log2(L)) * kLn2 : kNegInf;
+  }
 }
 
 template <typename T, int D>
@@ -278,8 +315,7 @@ hipError_t launch_decode_dims(const DecodeArgs& a, bool out_f32, int nb, unsigne
     hipLaunchKernelGGL((decode_kernel<T, D, 2>), grid, dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t items = a.total_q * a.hq * (D / 4);
-  const dim3 mgrid((unsigned)((items + 255) / 256));
+  const dim3 mgrid((unsigned)(a.total_q * a.hq));  // one workgroup per (row, head)
   if (out_f32)
     hipLaunchKernelGGL((decode_merge_kernel<float, D>), mgrid, dim3(256), 0, stream, a);
   else

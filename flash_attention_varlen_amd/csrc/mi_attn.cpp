@@ -307,6 +307,9 @@ int plan_decode(const mi_attn_fwd_params* p, int64_t max_seqlen_kv, int32_t num_
   const int64_t tiles = (vis + kDecodeTileKeys - 1) / kDecodeTileKeys + 1;  // +1: unaligned start
   const int64_t units = (int64_t)p->num_seqs * p->hkv;
   if (units > INT32_MAX) return fail(MI_ATTN_ERR_UNSUPPORTED, "too many (sequence, kv head) units");
+  // the merge runs one 256-thread workgroup per (row, head)
+  if ((int64_t)p->total_q * p->hq > (int64_t)1 << 24)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "too many (row, head) pairs for the merge (at most 2^24)");
   int64_t splits = num_splits > 0 ? num_splits : (kDecodeTargetWaves + units - 1) / units;
   splits = std::max<int64_t>(1, std::min<int64_t>(splits, tiles));
   const size_t row_bytes = (size_t)p->total_q * (size_t)p->hq * (size_t)(p->d_v + 2) * 4;
