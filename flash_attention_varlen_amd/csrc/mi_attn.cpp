@@ -273,7 +273,11 @@ struct DecodePlan {
 };
 
 constexpr int kDecodeTileKeys = 32;
-constexpr int64_t kDecodeTargetWaves = 4096;  // 16 one-wave workgroups per CU
+// One one-wave workgroup per SIMD (256 CUs x 4): every chunk runs in the
+// first and only round of workgroups.  Measured on the 8 x (10K-51K key)
+// decode workload: 256 / 512 / 1024 / 2048 / 4096 / 8192 / 16384 target
+// waves gave 1.94 / 3.58 / 4.49 / 4.28 / 4.15 / 3.86 / 3.66 TB/s.
+constexpr int64_t kDecodeTargetWaves = 1024;
 
 // Checks a decode call and plans its chunks: num_splits chunks per (sequence,
 // kv head) if > 0, else enough for kDecodeTargetWaves workgroups; at most
