@@ -203,6 +203,9 @@ def main():
                     help="with a bias, do not compute the bias key ranges (visit every tile)")
     ap.add_argument("--window", type=int, default=None,
                     help="override the window width of a sliding-window workload (cost vs W)")
+    ap.add_argument("--no-interval-rows", action="store_true",
+                    help="with a bias: compute its key ranges only, so that the forward reads "
+                         "the bias of every row (no interval flags)")
     ap.add_argument("--split-rope", action="store_true",
                     help="latent workload: pass q, k as 128-wide nope tensors plus 64-wide "
                          "q_rope / k_rope tensors instead of the concatenation")
@@ -275,9 +278,12 @@ def main():
     lse = torch.empty(w.hq, w.total_q, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    # With a bias, each step first computes the bias rows' key ranges (one
-    # read of the bias), then the forward skips the -inf tiles outside them.
+    # With a bias, each step first computes the bias rows' key ranges and
+    # interval flags (one read of the bias), then the forward skips the -inf
+    # tiles outside the ranges and masks interval rows without reading their
+    # bias.
     use_ranges = bias is not None and not args.no_bias_ranges
+    use_pure = use_ranges and not args.no_interval_rows
 
     is_decode = w.name.startswith("decode")
     if is_decode:
@@ -313,14 +319,18 @@ def main():
                                           w.max_seqlen_kv, scale=w.softmax_scale, causal=w.causal,
                                           window=w.window, dq=dq_b, dk=dk_b, dv=dv_b, stream=stream)
             return
-        rg = None
-        if use_ranges:
+        rg = pure = None
+        if use_pure:
+            rg, pure = fav.bias_key_ranges(bias, cq, ck, w.max_seqlen_q, stream=stream,
+                                           return_pure=True)
+        elif use_ranges:
             rg = fav.bias_key_ranges(bias, cq, ck, w.max_seqlen_q, stream=stream)
         if mid_event is not None:
             mid_event.record(stream)
         fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, scale=w.softmax_scale,
                              causal=w.causal, window=w.window, attn_bias=bias, out=out, lse=lse,
-                             out_dtype=out_dtype, stream=stream, bias_ranges=rg, **rope_kw)
+                             out_dtype=out_dtype, stream=stream, bias_ranges=rg, bias_pure=pure,
+                             **rope_kw)
 
     # GPU clocks depend on the load state: a cold GPU reads well below its
     # warmed rate (the mtlattn 0.3.0 page, section "Performance", gives the
@@ -440,6 +450,7 @@ def main():
             "host_wall_s": round(wall, 3),
             "prewarm": {"ms": args.prewarm_ms, "launches": prewarm_launches},
             "bias_ranges_pass_ms": round(sum(pre_ms) / len(pre_ms), 4) if use_ranges else None,
+            "interval_rows": use_pure if bias is not None else None,
             "parallelism": "single GPU",
         },
         "roofline": {

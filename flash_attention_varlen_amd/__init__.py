@@ -67,6 +67,7 @@ class MiAttnFwdParams(ctypes.Structure):
         ("k_rope_stride_tok", ctypes.c_int64), ("k_rope_stride_head", ctypes.c_int64),
         ("alibi_slopes", ctypes.c_void_p), ("alibi_stride_seq", ctypes.c_int64),
         ("mask", ctypes.c_void_p),
+        ("bias_pure", ctypes.c_void_p),
     ]
 
 
@@ -219,7 +220,8 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
                      scale: Optional[float] = None, causal: bool = False, window: int = 0,
                      attn_bias=None, out_dtype=None, return_lse: bool = False, out=None,
                      lse=None, tile_counts=None, stream=None, bias_ranges=None,
-                     max_seqlen_kv=None, q_rope=None, k_rope=None, alibi_slopes=None):
+                     max_seqlen_kv=None, q_rope=None, k_rope=None, alibi_slopes=None,
+                     bias_pure=None):
     """Fused varlen attention forward.  Returns ``out`` or ``(out, lse)``.
 
     q ``[Tq, Hq, Dqk]``, k ``[Tk, Hkv, Dqk]``, v ``[Tk, Hkv, Dv]`` (device,
@@ -241,7 +243,10 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     bias whose strides are not multiples of 4 elements is copied into such a
     layout.  (The differentiable path turns a bool mask into the fp32 0 /
     -inf bias the backward reads.)  ``bias_ranges`` (from ``bias_key_ranges`` on the same
-    bias) lets the kernels skip key tiles that are -inf for all their rows.
+    bias) lets the kernels skip key tiles that are -inf for all their rows;
+    ``bias_pure`` (from ``bias_key_ranges(..., return_pure=True)``, with those
+    ranges) lets them mask rows that are plain key intervals instead of
+    reading their bias.
 
     Latent-attention head: with ``q_rope`` ``[Tq, Hq, 64]`` and ``k_rope``
     ``[Tk, Hkv, 64]`` (bf16 / fp16, ``v`` 128 wide), q and k are the 128-wide
@@ -317,12 +322,18 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
         if (bias_ranges.dtype != torch.int32 or not bias_ranges.is_contiguous()
                 or bias_ranges.shape != (attn_bias.shape[1], tq, 2)):
             raise MiAttnError(ERR_INVALID_ARG, "bias_ranges must be contiguous int32 [H_b, Tq, 2]")
+    if bias_pure is not None:
+        if bias_ranges is None:
+            raise MiAttnError(ERR_INVALID_ARG, "bias_pure needs the bias_ranges it was computed with")
+        if (bias_pure.dtype != torch.uint8 or not bias_pure.is_contiguous()
+                or bias_pure.shape != (attn_bias.shape[1], tq)):
+            raise MiAttnError(ERR_INVALID_ARG, "bias_pure must be contiguous uint8 [H_b, Tq]")
     with torch.cuda.stream(s_obj):
         return _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
                                            scale, causal, window, attn_bias, out_dtype,
                                            return_lse, out, lse, tile_counts, s_obj, tq, hq, dqk,
                                            tk, hkv, dv, bias_ranges, q_rope, k_rope,
-                                           alibi_slopes)
+                                           alibi_slopes, bias_pure)
 
 
 def _stream_of(stream, device):
@@ -334,12 +345,18 @@ def _stream_of(stream, device):
     return torch.cuda.ExternalStream(int(stream), device=device)
 
 
-def bias_key_ranges(attn_bias, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int, stream=None):
+def bias_key_ranges(attn_bias, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int, stream=None,
+                    return_pure: bool = False):
     """int32 ``[H_b, Tq, 2]``: for each bias row, the first and one-past-last
     key of its sequence whose bias is not -inf (``[0, 0)`` if none).  Pass the
     result as ``bias_ranges`` to ``varlen_attention`` with the same bias: the
     kernels then skip, exactly, key tiles whose bias is -inf for all their
-    rows.  Valid for as long as the bias and cu_seqlens are."""
+    rows.  Valid for as long as the bias and cu_seqlens are.
+
+    With ``return_pure`` also uint8 ``[H_b, Tq]``, 1 for the rows that are
+    plain key intervals (bias exactly 0 on the range, -inf elsewhere; for a
+    bool mask, True exactly on the range): returns ``(ranges, pure)``, to be
+    passed as ``bias_ranges`` and ``bias_pure``."""
     import torch
     if attn_bias.dim() != 3 or not attn_bias.is_cuda or attn_bias.stride(-1) != 1:
         raise MiAttnError(ERR_INVALID_ARG, "attn_bias must be [Tq, H or 1, max_kv] on device")
@@ -353,7 +370,9 @@ def bias_key_ranges(attn_bias, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int, s
             raise MiAttnError(ERR_INVALID_ARG, "attn_bias must be fp32 or bool")
         tq, hb, cols = bias.shape
         ranges = torch.empty(hb, tq, 2, dtype=torch.int32, device=bias.device)
+        pure = torch.empty(hb, tq, dtype=torch.uint8, device=bias.device) if return_pure else None
         p = MiAttnFwdParams()
+        p.bias_pure = pure.data_ptr() if pure is not None else None
         if bias.dtype == torch.uint8:
             p.mask = bias.data_ptr()
         else:
@@ -367,7 +386,7 @@ def bias_key_ranges(attn_bias, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int, s
         p.bias_cols = cols
         p.bias_stride_tok, p.bias_stride_head = bias.stride(0), bias.stride(1)
         mi_attn_bias_key_ranges(p, ranges.data_ptr(), int(s_obj.cuda_stream))
-    return ranges
+    return (ranges, pure) if return_pure else ranges
 
 
 def _aligned_mask(mask):
@@ -410,7 +429,7 @@ def _aligned_bias(bias):
 def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, scale, causal,
                                 window, attn_bias, out_dtype, return_lse, out, lse, tile_counts,
                                 s_obj, tq, hq, dqk, tk, hkv, dv, bias_ranges=None, q_rope=None,
-                                k_rope=None, alibi_slopes=None):
+                                k_rope=None, alibi_slopes=None, bias_pure=None):
     import torch
     bias = attn_bias
     if bias is not None:
@@ -442,6 +461,7 @@ def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen
     else:
         p.bias = bias.data_ptr() if bias is not None else None
     p.bias_ranges = bias_ranges.data_ptr() if bias_ranges is not None else None
+    p.bias_pure = bias_pure.data_ptr() if bias_pure is not None else None
     if q_rope is not None:
         p.q_rope, p.k_rope = q_rope.data_ptr(), k_rope.data_ptr()
         p.q_rope_stride_tok, p.q_rope_stride_head = q_rope.stride(0), q_rope.stride(1)

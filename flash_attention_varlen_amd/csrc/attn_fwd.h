@@ -31,6 +31,9 @@ struct KernelArgs {
   const void* k_rope;
   const float* alibi;  // optional ALiBi slopes, alibi[seq * alibi_ss + head]
   const uint8_t* mask;  // optional byte mask [total_q, bias_heads, bias_cols] (strides b_st, b_sh)
+  // optional [bias_heads, total_q]: 1 where the row's bias is exactly 0 on
+  // its whole key range (bias_ranges) and -inf elsewhere
+  const uint8_t* bias_pure;
   int32_t* tile_counts;
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
   int64_t b_st, b_sh;

@@ -47,6 +47,11 @@
 #ifndef MI_ATTN_SYNC_COPIES
 #define MI_ATTN_SYNC_COPIES 0
 #endif
+// Four-slot kernels: MI_ATTN_DEEP_COPIES=1 starts each tile copy three steps
+// before its first read and ends every step with a barrier (see step()).
+#ifndef MI_ATTN_DEEP_COPIES
+#define MI_ATTN_DEEP_COPIES 0
+#endif
 
 namespace mi_attn {
 namespace {
@@ -65,6 +70,8 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
 // expcnt in 6:4, lgkmcnt in 11:8): wait for vmcnt == 0 / lgkmcnt == 0 only.
 constexpr int kWaitVm0 = 0x0F70;
+// vmcnt <= n (n < 64), expcnt and lgkmcnt not waited for
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 constexpr int kWaitLgkm0 = 0xC07F;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -691,7 +698,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int D, int LOADS>
 __device__ __forceinline__ void load_tile_part(const char* base, int64_t st_b, int kb, int rows,
                                                lds_char* dst, const uint32_t* off) {
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(base + kb * st_b, (uint32_t)((rows - 1) * st_b + D * 2));
+  // rows <= 0 (a tile past the sequence end): an empty window, all zeros
+  const uint32_t bytes = rows > 0 ? (uint32_t)((rows - 1) * st_b + D * 2) : 0u;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base + kb * st_b, bytes);
 #pragma unroll
   for (int i = 0; i < LOADS; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * kThreads * 16), 16, off[i], 0, 0, 0);
@@ -875,6 +884,9 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   // the current tiles do not overlap the copies in flight into the other
   // buffers and does not wait for those copies before reading.
   constexpr int NSLOT = WaveBlocks<DQK, DV, BIAS>::NSLOT;
+  // deep copies: K copies four and V copies three tiles ahead, a barrier
+  // after every step (four slots only)
+  constexpr bool DEEP = MI_ATTN_DEEP_COPIES && NSLOT == 4;
   constexpr int K_BYTES_HI = NSLOT == 4 ? K_BYTES : 16;  // slots 2 and 3
   constexpr int V_BYTES_HI = NSLOT == 4 ? V_BYTES : 16;
   __shared__ __attribute__((aligned(1024))) char kbuf_0[K_BYTES];
@@ -1015,6 +1027,39 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     my_row[n] = w0 + 32 * n + l32;
     row_ok[n] = my_row[n] < lq;
   }
+  // Rows whose bias is exactly 0 on their key range [rlo, rhi) and -inf
+  // elsewhere (bias_pure, from the key-range pass): when every row of the
+  // wave is such a row, the wave reads no bias at all.  It adds a bias of 0
+  // instead (the same arithmetic, so the same results) and masks keys
+  // outside each row's range on the tiles that cross a range end, as it
+  // masks the causal diagonal.
+  int rlo[NB], rhi[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    rlo[n] = 0;
+    rhi[n] = lk;
+  }
+  bool pure_w = false;
+  int pure_lo_max = 0, pure_hi_min = lk;  // over the wave's rows
+  if constexpr (BIAS && BSRC != kBiasAlibi) {
+    if (a.bias_pure != nullptr && wave_active) {
+      const int64_t rb = (int64_t)(a.bias_heads == 1 ? 0 : head) * a.total_q + cq0;
+      bool all = true;
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+        if (row_ok[n]) {
+          const int2 v = *reinterpret_cast<const int2*>(a.bias_ranges + 2 * (rb + my_row[n]));
+          rlo[n] = v.x;
+          rhi[n] = v.y;
+          all = all && a.bias_pure[rb + my_row[n]] != 0;
+          pure_lo_max = max(pure_lo_max, v.x);
+          pure_hi_min = min(pure_hi_min, v.y);
+        }
+      pure_w = __ballot(!all) == 0ull;
+      pure_lo_max = __builtin_amdgcn_readfirstlane(wave_max_i32(pure_lo_max));
+      pure_hi_min = __builtin_amdgcn_readfirstlane(wave_min_i32(pure_hi_min));
+    }
+  }
   // Tiles from wt_end on hold no key visible to any row of this wave (causal
   // rows that end before the workgroup's last diagonal; no rows at all past
   // the sequence end): the wave skips their work but still does its share of
@@ -1081,10 +1126,13 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   const char* krbase = nullptr;
   if constexpr (ROPE)
     krbase = reinterpret_cast<const char*>(a.k_rope) + ((int64_t)ck0 * a.kr_st + (int64_t)g * a.kr_sh) * 2;
+  // Keys copied: those of the tile range (a tile at or past t_end copies
+  // nothing and reads as zeros).
+  const int kcopy_end = (int)min((int64_t)lk, (int64_t)t_end * BN);
   auto load_k = [&](int t, auto S) __attribute__((device)) {
-    load_tile_part<DN, KN>(kbase, k_st_b, t * BN, min(lk - t * BN, BN), kbuf(S) + wave * 1024, koff);
+    load_tile_part<DN, KN>(kbase, k_st_b, t * BN, min(kcopy_end - t * BN, BN), kbuf(S) + wave * 1024, koff);
     if constexpr (ROPE)
-      load_tile_part<64, KLOADS - KN>(krbase, kr_st_b, t * BN, min(lk - t * BN, BN),
+      load_tile_part<64, KLOADS - KN>(krbase, kr_st_b, t * BN, min(kcopy_end - t * BN, BN),
                                       kbuf(S) + KN * kThreads * 16 + wave * 1024, koff + KN);
   };
   // LDS address of K fragment (k-step kk: head dims 16 kk .. 16 kk + 15) of key
@@ -1102,7 +1150,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     }
   };
   auto load_v = [&](int t, auto S) __attribute__((device)) {
-    load_tile_part<DV, VLOADS>(vbase, v_st_b, t * BN, min(lk - t * BN, BN), vbuf(S) + wave * 1024, voff);
+    load_tile_part<DV, VLOADS>(vbase, v_st_b, t * BN, min(kcopy_end - t * BN, BN), vbuf(S) + wave * 1024, voff);
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T), loaded once.
@@ -1216,15 +1264,17 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   // end, causal diagonal, window start).
   auto tile_needs_mask = [&](int t) __attribute__((device)) -> bool {
     const int kb = t * BN;
-    return (kb + BN > lk) || (causal && kb + BN - 1 > w0 + off) || (W > 0 && kb <= w1 - 1 + off - W);
+    return (kb + BN > lk) || (causal && kb + BN - 1 > w0 + off) || (W > 0 && kb <= w1 - 1 + off - W) ||
+           (pure_w && (kb < pure_lo_max || kb + BN > pure_hi_min));
   };
   // Masks key block mb of query block n of tile t: entry e of the lane holds
   // key kb + 32 mb + 8 (e / 4) + 4 hf + e % 4, visible iff lo < key <= hi
   // (one unsigned compare per entry).
   auto mask_block = [&](int t, f32x16_t& sc, int n, int mb) __attribute__((device)) {
     const int key0 = t * BN + 32 * mb + 4 * hf;
-    const int hi = min(lk - 1, causal ? my_row[n] + off : lk - 1);
-    const int lo = W > 0 ? my_row[n] + off - W : -1;
+    // (rlo, rhi: the row's bias key range, or all keys)
+    const int hi = min(min(lk, rhi[n]) - 1, causal ? my_row[n] + off : lk - 1);
+    const int lo = max(W > 0 ? my_row[n] + off - W : -1, rlo[n] - 1);
     const int base = lo + 1 - key0;         // first visible entry offset
     const uint32_t span = (uint32_t)max(hi - lo, 0);
 #pragma unroll
@@ -1364,16 +1414,34 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     // steps end with one.  Either way a barrier separates the last read of a
     // slot from the copy that refills it, and the end of a copy (each wave's
     // vmcnt wait at its step's end) from the first read of its tile.
+    //
+    // Deep copies (four slots, a barrier after every step): K(t+4) goes to
+    // the slot of K(t), last read in step t-1, and V(t+3) to that of V(t-1),
+    // also last read in step t-1.  A step's copies are first read three
+    // steps later, so each step waits only for the copies of two steps
+    // earlier: they overlap two whole steps of work instead of one.  The
+    // copies are issued whether or not their tile exists (past the end they
+    // read an empty window), so that every step has the same count of
+    // memory operations in flight; the bias loads of the next tile are
+    // issued before them, so that their own wait leaves the copies in flight.
     constexpr int slot = decltype(slot_tag)::value;
-    constexpr int LK = NSLOT == 4 ? 3 : 2;  // K copies run LK tiles ahead
-    constexpr int LV = LK - 1;              // V copies LV tiles ahead
+    constexpr int LK = DEEP ? 4 : NSLOT == 4 ? 3 : 2;  // K copies run LK tiles ahead
+    constexpr int LV = LK - 1;                         // V copies LV tiles ahead
     using KR = std::integral_constant<int, (slot + 1) % NSLOT>;
     using VR = std::integral_constant<int, slot>;
     using KW = std::integral_constant<int, (slot + LK) % NSLOT>;
     using VW = std::integral_constant<int, (slot + LV) % NSLOT>;
-    constexpr bool BAR = NSLOT == 2 || (slot & 1) != 0;
-    if (j + LV < nt) load_v(t + LV, VW{});
-    if (j + LK < nt) load_k(t + LK, KW{});
+    constexpr bool BAR = DEEP || NSLOT == 2 || (slot & 1) != 0;
+    if constexpr (DEEP) {
+      if constexpr (BIAS) {
+        if (!pure_w && t < wt_end && j + 1 < nt) load_bias(t + 1, bpre);
+      }
+      load_v(t + LV, VW{});
+      load_k(t + LK, KW{});
+    } else {
+      if (j + LV < nt) load_v(t + LV, VW{});
+      if (j + LK < nt) load_k(t + LK, KW{});
+    }
     if constexpr (MI_ATTN_SYNC_COPIES) {  // schedule check: copies land before any read
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
@@ -1383,8 +1451,8 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
       if constexpr (BAR) __syncthreads();
       return false;
     }
-    if constexpr (BIAS) {
-      if (j + 1 < nt) load_bias(t + 1, bpre);
+    if constexpr (BIAS && !DEEP) {
+      if (!pure_w && j + 1 < nt) load_bias(t + 1, bpre);
     }
 
     const lds_char* kt = kbuf(KR{});
@@ -1555,7 +1623,13 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of V(t+LV), K(t+LK) have landed
+    if constexpr (DEEP) {
+      // this wave's copies of two steps earlier (read next step) have landed;
+      // this step's and the previous step's may still be in flight
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (KLOADS + VLOADS)));
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of V(t+LV), K(t+LK) have landed
+    }
     if constexpr (BAR) __syncthreads();
     return grow;
   };
@@ -1571,10 +1645,26 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
       using S2 = std::integral_constant<int, 2>;
       if (nt > 1) load_v(t_begin + 1, S1{});
       if (nt > 2) load_k(t_begin + 2, S2{});
+      if constexpr (DEEP) {  // and deep copies one more
+        using S3 = std::integral_constant<int, 3>;
+        if (nt > 2) load_v(t_begin + 2, S2{});
+        if (nt > 3) load_k(t_begin + 3, S3{});
+      }
     }
     // bias of the first tile: in flight together with the first copies
     f32x4_t bpre[NB][NMB][4];
-    if constexpr (BIAS) load_bias(t_begin, bpre);
+    if constexpr (BIAS) {
+      if (pure_w) {  // a bias of 0 for every tile
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) bpre[n][mb][qd] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+      } else {
+        load_bias(t_begin, bpre);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     f32x16_t sa[NB][NMB], sb[NB][NMB];
@@ -1610,9 +1700,15 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
           if (need) rescale(m_pend);
         }
       }
-      // the last step ended without a barrier when it was an even one: the
-      // epilogue reuses the buffers as staging
-      if (nt & 1) __syncthreads();
+      // the epilogue reuses the buffers as staging: every copy (deep copies
+      // run past the last tile) has landed and the last step ended with a
+      // barrier (without deep copies an even step ends without one)
+      if constexpr (DEEP) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __syncthreads();
+      } else {
+        if (nt & 1) __syncthreads();
+      }
     }
   };
   if (t_begin < t_end) run();

@@ -12,6 +12,7 @@ struct BiasRangeArgs {
   const int32_t* cu_q;
   const int32_t* cu_kv;
   int32_t* ranges;  // [bias_heads, total_q, 2]
+  uint8_t* pure;    // optional [bias_heads, total_q]: 1 when the row is a key interval
   int64_t b_st, b_sh;
   int64_t total_q;
   int32_t bias_cols;

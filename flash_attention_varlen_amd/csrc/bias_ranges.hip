@@ -6,7 +6,11 @@
 // competitive with MLX": skipping fully masked tiles is exact), so the
 // forward kernels skip the key tiles outside a workgroup's hull of these
 // ranges.  One wave per row; the row is read once with 16-byte loads, so the
-// pass is bound by HBM bandwidth (4 bytes per bias element).
+// pass is bound by HBM bandwidth (4 bytes per bias element).  Optionally it
+// also marks the rows that are plain key intervals: bias exactly 0 on every
+// key of [lo, hi) (and -inf on the others, by the definition of the range),
+// i.e. the number of zero values equals hi - lo.  The forward kernels mask
+// such rows to their interval instead of reading their bias.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,7 +32,7 @@ __global__ __launch_bounds__(256) void bias_key_ranges_kernel(const BiasRangeArg
   if (r >= lq) return;
   const int lk = min(a.cu_kv[seq + 1] - a.cu_kv[seq], a.bias_cols);
   const float* row = a.bias + (int64_t)(cq0 + r) * a.b_st + (int64_t)hb * a.b_sh;
-  int lo = 0x7fffffff, hi = 0;
+  int lo = 0x7fffffff, hi = 0, zeros = 0;
   // full 16-byte chunks: 64 lanes x 4 keys per pass, four passes in flight
   const int full = lk & ~3;
   for (int j0 = 4 * lane; j0 < full; j0 += 4 * 64 * 4) {
@@ -43,27 +47,35 @@ __global__ __launch_bounds__(256) void bias_key_ranges_kernel(const BiasRangeArg
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < 4; ++e) {
         if (v[u][e] != -__builtin_inff()) {
           const int j = j0 + u * 256 + e;
           lo = min(lo, j);
           hi = max(hi, j + 1);
         }
+        zeros += v[u][e] == 0.0f;
+      }
   }
   // the last lk % 4 keys
-  if (lane < lk - full && row[full + lane] != -__builtin_inff()) {
-    lo = min(lo, full + lane);
-    hi = max(hi, full + lane + 1);
+  if (lane < lk - full) {
+    const float x = row[full + lane];
+    if (x != -__builtin_inff()) {
+      lo = min(lo, full + lane);
+      hi = max(hi, full + lane + 1);
+    }
+    zeros += x == 0.0f;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     lo = min(lo, __shfl_xor(lo, o));
     hi = max(hi, __shfl_xor(hi, o));
+    zeros += __shfl_xor(zeros, o);
   }
   if (lane == 0) {
-    int32_t* out = a.ranges + ((int64_t)hb * a.total_q + cq0 + r) * 2;
-    out[0] = hi > 0 ? lo : 0;
-    out[1] = hi;
+    const int64_t i = (int64_t)hb * a.total_q + cq0 + r;
+    a.ranges[2 * i] = hi > 0 ? lo : 0;
+    a.ranges[2 * i + 1] = hi;
+    if (a.pure != nullptr) a.pure[i] = zeros == (hi > 0 ? hi - lo : 0) ? 1 : 0;
   }
 }
 
@@ -80,7 +92,7 @@ __global__ __launch_bounds__(256) void mask_key_ranges_kernel(const BiasRangeArg
   if (r >= lq) return;
   const int lk = min(a.cu_kv[seq + 1] - a.cu_kv[seq], a.bias_cols);
   const uint8_t* row = a.mask + (int64_t)(cq0 + r) * a.b_st + (int64_t)hb * a.b_sh;
-  int lo = 0x7fffffff, hi = 0;
+  int lo = 0x7fffffff, hi = 0, vis = 0;  // vis: visible keys (the zeros of the bias)
   const int full = lk & ~3;
   for (int j0 = 4 * lane; j0 < full; j0 += 4 * 64) {
     const uint32_t w = *reinterpret_cast<const uint32_t*>(row + j0);
@@ -89,21 +101,25 @@ __global__ __launch_bounds__(256) void mask_key_ranges_kernel(const BiasRangeArg
       if ((w >> (8 * e)) & 0xffu) {
         lo = min(lo, j0 + e);
         hi = max(hi, j0 + e + 1);
+        ++vis;
       }
   }
   if (lane < lk - full && row[full + lane] != 0) {
     lo = min(lo, full + lane);
     hi = max(hi, full + lane + 1);
+    ++vis;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     lo = min(lo, __shfl_xor(lo, o));
     hi = max(hi, __shfl_xor(hi, o));
+    vis += __shfl_xor(vis, o);
   }
   if (lane == 0) {
-    int32_t* out = a.ranges + ((int64_t)hb * a.total_q + cq0 + r) * 2;
-    out[0] = hi > 0 ? lo : 0;
-    out[1] = hi;
+    const int64_t i = (int64_t)hb * a.total_q + cq0 + r;
+    a.ranges[2 * i] = hi > 0 ? lo : 0;
+    a.ranges[2 * i + 1] = hi;
+    if (a.pure != nullptr) a.pure[i] = vis == (hi > 0 ? hi - lo : 0) ? 1 : 0;
   }
 }
 

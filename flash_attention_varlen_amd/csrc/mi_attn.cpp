@@ -260,6 +260,8 @@ int check_fwd_params(const mi_attn_fwd_params* p, bool* empty) {
     if (p->bias_ranges != nullptr && (reinterpret_cast<uintptr_t>(p->bias_ranges) & 7u) != 0)
       return fail(MI_ATTN_ERR_INVALID_ARG, "bias_ranges must be 8-byte aligned");
   }
+  if (p->bias_pure != nullptr && !has_bias)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "bias_pure is given without a bias or a mask");
 
   return MI_ATTN_OK;
 }
@@ -417,6 +419,8 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
   const int rc_check = check_fwd_params(p, &empty);
   if (rc_check != MI_ATTN_OK || empty) return rc_check;
   const bool has_bias = p->bias != nullptr || p->mask != nullptr;  // a tensor bias or a byte mask
+  if (p->bias_pure != nullptr && p->bias_ranges == nullptr)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "bias_pure needs the bias_ranges it was computed with");
 
   int32_t bm = 0, bn = 0;
   if (mi_attn_tile_shape(dt, p->d_qk, p->d_v, &bm, &bn) != MI_ATTN_OK) return MI_ATTN_ERR_UNSUPPORTED;
@@ -445,6 +449,7 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
   a.bias = p->bias;
   a.mask = p->mask;
   a.bias_ranges = has_bias ? p->bias_ranges : nullptr;
+  a.bias_pure = has_bias ? p->bias_pure : nullptr;
   a.q_rope = p->q_rope;
   a.k_rope = p->k_rope;
   a.qr_st = p->q_rope_stride_tok;
@@ -818,6 +823,7 @@ int mi_attn_bias_key_ranges(const mi_attn_fwd_params* p_in, int32_t* ranges, voi
   a.cu_q = p->cu_seqlens_q;
   a.cu_kv = p->cu_seqlens_kv;
   a.ranges = ranges;
+  a.pure = const_cast<uint8_t*>(p->bias_pure);  // an output here
   a.b_st = p->bias_stride_tok;
   a.b_sh = p->bias_stride_head;
   a.total_q = p->total_q;

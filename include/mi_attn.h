@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_VERSION 150 /* 1.5.0 */
+#define MI_ATTN_VERSION 160 /* 1.6.0 */
 
 /* Return codes.  On any error nothing is launched and out / lse are untouched. */
 enum {
@@ -179,6 +179,17 @@ typedef struct mi_attn_fwd_params {
    * mi_attn_bias_key_ranges with this mask) apply as for a bias.  Not
    * together with bias or alibi_slopes; the decode entry points refuse it. */
   const uint8_t* mask;
+  /* Added in version 1.6 (NULL for older callers): per bias head and query
+   * row, one byte [bias_heads, total_q] (uint8, device, caller-owned):
+   * nonzero when the row's bias (or mask) is exactly 0 (visible) on every
+   * key of its range [lo, hi) from bias_ranges and -inf (masked) on every
+   * other key, i.e. the row is a plain key interval.  Written by
+   * mi_attn_bias_key_ranges when non-NULL; read by mi_attn_varlen_fwd, which
+   * then needs bias_ranges from the same call: a wave of rows that are all
+   * such intervals reads no bias and masks each row to its interval
+   * instead, with results equal to those of the bias.  Like bias_ranges it
+   * assumes bias_cols >= every sequence's key length. */
+  const uint8_t* bias_pure;
 } mi_attn_fwd_params;
 
 /*
@@ -205,7 +216,10 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p, void* stream);
  * "Use", for the bias; triton-msl part-2 post, section "FlashAttention:
  * faster than PyTorch, competitive with MLX", for skipping masked tiles).
  * The ranges stay valid for as long as the bias and cu_seqlens do: compute
- * them once per bias, pass them in mi_attn_fwd_params.bias_ranges.
+ * them once per bias, pass them in mi_attn_fwd_params.bias_ranges.  With
+ * p->bias_pure non-NULL it also writes, per row, whether the row is a plain
+ * key interval (bias exactly 0 on [lo, hi), -inf elsewhere; mask bytes
+ * nonzero on [lo, hi), 0 elsewhere), for mi_attn_fwd_params.bias_pure.
  * Asynchronous on `stream`; one read of the bias.  Returns MI_ATTN_OK or a
  * negative code (nothing launched).
  */

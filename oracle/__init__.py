@@ -9,10 +9,11 @@ routine on its special cases, closed forms and invariants; none is
 from .ref_attention import (attention_rows, bias_head, finish_rows, kv_head_of, logits,
                             softmax_rows, varlen_attention, visible, visible_counts)
 from .ref_backward import varlen_attention_backward
-from .ref_masks import alibi_bias, bias_key_ranges
+from .ref_masks import alibi_bias, bias_key_ranges, bias_rows_are_intervals
 from .ref_padding import masked_attention, pack_tokens, padding_to_varlen, unpack_tokens
 
-__all__ = ["alibi_bias", "attention_rows", "bias_head", "bias_key_ranges", "finish_rows", "kv_head_of", "logits",
+__all__ = ["alibi_bias", "attention_rows", "bias_head", "bias_key_ranges", "bias_rows_are_intervals",
+           "finish_rows", "kv_head_of", "logits",
            "masked_attention", "pack_tokens", "padding_to_varlen", "softmax_rows",
            "unpack_tokens", "varlen_attention", "varlen_attention_backward", "visible",
            "visible_counts"]

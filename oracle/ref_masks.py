@@ -11,6 +11,11 @@ shares no code with the HIP path.
   kernels may skip every key outside these ranges; the triton-msl part-2
   post (section "FlashAttention: faster than PyTorch, competitive with MLX")
   makes the same point for tiles that are masked in full.
+* ``bias_rows_are_intervals``: for each bias row, whether it is a plain key
+  interval: bias exactly 0 on every key of its range and -inf on every
+  other key.  Such a row's bias adds nothing inside the range and removes
+  every key outside it, so attending over the range alone gives the same
+  result (the same "Use" section: a bool mask is such a 0 / -inf bias).
 * ``alibi_bias``: the ALiBi bias written out as a dense additive bias.  The
   mtlattn 0.3.0 page (section "Use") names ALiBi as one of the patterns the
   additive bias carries but gives no formula; the reading taken is the
@@ -38,6 +43,29 @@ def bias_key_ranges(bias, cu_q, cu_kv):
                 keys = np.nonzero(bias[t, h, :lk] != -np.inf)[0]
                 if keys.size:
                     out[h, t] = (keys[0], keys[-1] + 1)
+    return out
+
+
+def bias_rows_are_intervals(bias, cu_q, cu_kv):
+    """uint8 ``[H_b, Tq]``: 1 when, over the keys ``j < min(Lk, cols)`` of the
+    row's sequence, the bias is exactly 0 on every key of ``[lo, hi)`` (the
+    row's ``bias_key_ranges``) and -inf on every other key; 0 otherwise.  A
+    row that is -inf everywhere is the empty interval (1)."""
+    bias = np.asarray(bias)
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_kv = np.asarray(cu_kv, dtype=np.int64)
+    tq, hb, cols = bias.shape
+    rg = bias_key_ranges(bias, cu_q, cu_kv)
+    out = np.zeros((hb, tq), dtype=np.uint8)
+    for s in range(len(cu_q) - 1):
+        lk = min(int(cu_kv[s + 1] - cu_kv[s]), cols)
+        for t in range(int(cu_q[s]), int(cu_q[s + 1])):
+            for h in range(hb):
+                lo, hi = (int(x) for x in rg[h, t])
+                row = bias[t, h, :lk]
+                inside = row[lo:hi]
+                outside = np.concatenate([row[:lo], row[hi:]])
+                out[h, t] = bool(np.all(inside == 0.0) and np.all(outside == -np.inf))
     return out
 
 

@@ -373,6 +373,64 @@ def _loss_and_grads(q, k, v, cu_q, cu_kv, scale, causal, window, bias, G):
                                                                      causal, window, bias)
 
 
+def pin_interval_rows_hand_worked():
+    """Interval rows by hand: 0 on a contiguous run and -inf elsewhere is an
+    interval; a -inf hole inside the run, any nonzero finite value or a NaN
+    is not; an all -inf row is the empty interval; -0.0 counts as 0; keys at
+    or past the sequence's Lk are not looked at."""
+    ninf, nan = -np.inf, np.nan
+    rows = [
+        ([0, 0, 0, 0, 0], 1),
+        ([ninf, 0, 0, ninf, ninf], 1),
+        ([0, ninf, 0, ninf, ninf], 0),      # hole
+        ([ninf, 0, 0.5, 0, ninf], 0),       # a nonzero value
+        ([ninf, -1.0, 0, ninf, ninf], 0),   # a negative value
+        ([0, 0, 0.5, ninf, ninf], 0),       # nonzero at the range's last key
+        ([ninf] * 5, 1),                    # empty
+        ([-0.0, 0, ninf, ninf, ninf], 1),   # negative zero
+        ([0, nan, ninf, ninf, ninf], 0),    # NaN
+        ([ninf, ninf, ninf, ninf, 0], 1),
+        ([0, 0, 0, ninf, 2.0], 1),          # the last key is past Lk = 4
+    ]
+    bias = np.array([r for r, _ in rows], dtype=np.float64)[:, None, :]
+    cu_q = np.arange(len(rows) + 1)
+    cu_kv = np.array([0] + [5] * (len(rows) - 1) + [4]).cumsum()
+    got = oracle.bias_rows_are_intervals(bias, cu_q, cu_kv)
+    assert got.shape == (1, len(rows))
+    assert list(got[0]) == [want for _, want in rows], list(got[0])
+
+
+def pin_interval_rows_attend_their_range():
+    """On an interval row, attention with the bias equals attention with no
+    bias over the row's key range alone (the bias-free definition applied to
+    the sub-sequence)."""
+    rng = np.random.default_rng(21)
+    lens, d = [9, 14], 8
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    tq = int(cu[-1])
+    q = rng.standard_normal((tq, 1, d))
+    k = rng.standard_normal((tq, 1, d))
+    v = rng.standard_normal((tq, 1, d))
+    bias = np.full((tq, 1, max(lens)), -np.inf)
+    for s, n in enumerate(lens):
+        for i in range(n):
+            lo = int(rng.integers(0, n))
+            hi = int(rng.integers(lo + 1, n + 1))
+            bias[cu[s] + i, 0, lo:hi] = 0.0
+    assert np.all(oracle.bias_rows_are_intervals(bias, cu, cu) == 1)
+    rg = oracle.bias_key_ranges(bias, cu, cu)
+    out, _ = oracle.varlen_attention(q, k, v, cu, cu, None, False, 0, bias)
+    for s, n in enumerate(lens):
+        for i in range(n):
+            t = cu[s] + i
+            lo, hi = rg[0, t]
+            kk = k[cu[s] + lo:cu[s] + hi, 0]
+            vv = v[cu[s] + lo:cu[s] + hi, 0]
+            z = kk @ q[t, 0] / np.sqrt(d)
+            p = np.exp(z - z.max())
+            assert np.allclose(out[t, 0], p @ vv / p.sum(), rtol=0, atol=1e-12)
+
+
 def pin_backward_finite_differences():
     """Central differences of L = sum(out * G) in fp64 against dq, dk, dv, over
     causal / full / window, cross-attention lengths, GQA and a bias with -inf
@@ -596,4 +654,5 @@ ALL_PINS = [pin_brute_force_tiny, pin_sdpa_special_case, pin_rows_sum_to_one,
             pin_bias_ranges_skip_is_exact, pin_backward_finite_differences,
             pin_backward_sdpa_special_case, pin_backward_closed_forms, pin_padding_hand_worked,
             pin_masked_attention_sdpa, pin_packed_matches_masked, pin_alibi_hand_worked,
-            pin_alibi_causal_is_a_linear_key_bias]
+            pin_alibi_causal_is_a_linear_key_bias, pin_interval_rows_hand_worked,
+            pin_interval_rows_attend_their_range]

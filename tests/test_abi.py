@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_tile_shape():
-    assert fav.mi_attn_version() == 150
+    assert fav.mi_attn_version() == 160
     for dt in (fav.BF16, fav.F16):
         for dqk, dv in ((64, 64), (96, 96), (128, 128), (192, 128), (256, 256)):
             bm, bn = fav.mi_attn_tile_shape(dt, dqk, dv)
@@ -155,6 +155,10 @@ REFUSALS = {
                              bias_stride_head=0), fav.ERR_INVALID_ARG),
     "mask_heads": (dict(mask=1 << 20, bias_heads=3, bias_cols=64, bias_stride_tok=64,
                         bias_stride_head=64), fav.ERR_UNSUPPORTED),
+    # interval flags of the bias rows: only with a bias or a mask, and with their ranges
+    "pure_without_bias": (dict(bias_pure=1 << 20), fav.ERR_INVALID_ARG),
+    "pure_without_ranges": (dict(bias_pure=1 << 20, bias=1 << 20, bias_heads=1, bias_cols=64,
+                                 bias_stride_tok=64, bias_stride_head=0), fav.ERR_INVALID_ARG),
     # with split operands q / k hold 128 dims; without them a 128-wide stride is short of 192
     "latent_short_q_stride": (dict(d_qk=192, q_stride_tok=128, q_stride_head=0, hq=2, hkv=2,
                                    out_stride_tok=2 * 128), fav.ERR_UNSUPPORTED),

@@ -48,6 +48,11 @@ MASK_MUTATIONS = {
     "alibi_first_seq_slopes": ("sl = slopes if slopes.ndim == 1 else slopes[s]",
                                "sl = slopes if slopes.ndim == 1 else slopes[0]"),
     "alibi_head_reversed": ("= -sl[h] * abs(pos - j)", "= -sl[hq - 1 - h] * abs(pos - j)"),
+    "interval_nonpositive_ok": ("np.all(inside == 0.0)", "np.all(inside <= 0.0)"),
+    "interval_last_key_unchecked": ("inside = row[lo:hi]", "inside = row[lo:hi - 1]"),
+    "interval_finite_ok": ("np.all(inside == 0.0)", "np.all(np.isfinite(inside))"),
+    "interval_empty_not_interval": ("out[h, t] = bool(np.all(inside == 0.0)",
+                                    "out[h, t] = hi > lo and bool(np.all(inside == 0.0)"),
 }
 
 # mutations of the backward oracle (oracle/ref_backward.py)
