@@ -140,7 +140,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
 
 
 def variant_library(name: str) -> ctypes.CDLL:
-    """A schedule variant of the library (``slots2``, ``synccopies``), built
+    """A schedule variant of the library (``slots2``, ``synccopies``, ``shallow``), built
     beside it for the LDS race check; its results must equal the shipping
     library's bit for bit."""
     from .build import variant_path

@@ -28,10 +28,12 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
 # Sources compiled once each.
 PLAIN = ["attn_bwd.hip", "attn_decode.hip", "bias_ranges.hip", "padding.hip", "mi_attn.cpp"]
 # The forward (dispatcher + instances) is also built in schedule variants
-# that only the LDS race test loads: all 16-bit kernels with two K/V slots,
-# and every step waiting for its own copies behind a barrier before any
-# read.  Both must give results bitwise equal to the shipping library.
-VARIANTS = {"slots2": ["-DMI_ATTN_MAX_SLOTS=2"], "synccopies": ["-DMI_ATTN_SYNC_COPIES=1"]}
+# that only the LDS race test loads: all 16-bit kernels with two K/V slots;
+# every step waiting for its own copies behind a barrier before any read;
+# the four-slot kernels with copies one step less ahead.  All must give
+# results bitwise equal to the shipping library.
+VARIANTS = {"slots2": ["-DMI_ATTN_MAX_SLOTS=2"], "synccopies": ["-DMI_ATTN_SYNC_COPIES=1"],
+            "shallow": ["-DMI_ATTN_DEEP_COPIES=0"]}
 VARIANT_DIR = os.path.join(PKG, "variants")
 
 

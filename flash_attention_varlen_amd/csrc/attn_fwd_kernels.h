@@ -40,17 +40,19 @@
 // Schedule switches for the LDS race check (the shipping build uses the
 // defaults): MI_ATTN_MAX_SLOTS=2 gives every 16-bit kernel two K/V slots;
 // MI_ATTN_SYNC_COPIES=1 makes each step wait for its tile copies behind a
-// barrier before it reads anything.
+// barrier before it reads anything; MI_ATTN_DEEP_COPIES=0 runs the
+// four-slot kernels' copies one step less ahead, with a barrier every
+// second step.
 #ifndef MI_ATTN_MAX_SLOTS
 #define MI_ATTN_MAX_SLOTS 4
 #endif
 #ifndef MI_ATTN_SYNC_COPIES
 #define MI_ATTN_SYNC_COPIES 0
 #endif
-// Four-slot kernels: MI_ATTN_DEEP_COPIES=1 starts each tile copy three steps
-// before its first read and ends every step with a barrier (see step()).
+// Four-slot kernels: each tile copy starts three steps before its first
+// read and every step ends with a barrier (see step()).
 #ifndef MI_ATTN_DEEP_COPIES
-#define MI_ATTN_DEEP_COPIES 0
+#define MI_ATTN_DEEP_COPIES 1
 #endif
 
 namespace mi_attn {

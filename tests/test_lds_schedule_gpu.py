@@ -1,12 +1,13 @@
 """LDS race check of the forward's copy schedule: the shipping library
-against two schedule variants built from the same source (all 16-bit
+against three schedule variants built from the same source (all 16-bit
 kernels on two K/V slots; every step waiting for its own tile copies behind
-a barrier before any read).  A slot refilled while still being read, or a
-tile read before its copy landed, would make the results depend on timing;
-the variants remove that freedom, so their outputs must equal the shipping
-kernels' bit for bit on the four-slot instances (latent head, biased heads,
-the 256-wide head) and the two-slot ones (the GQA causal prefill, the 96-
-and 64-wide heads)."""
+a barrier before any read; the four-slot kernels with their copies one step
+less ahead).  A slot refilled while still being read, or a tile read before
+its copy landed, would make the results depend on timing; the variants
+change that timing, so their outputs must equal the shipping kernels' bit
+for bit on the four-slot instances (latent head, biased heads read as a
+bias or as interval rows, the 256-wide head) and the two-slot ones (the GQA
+causal prefill, the 96- and 64-wide heads)."""
 import contextlib
 
 import pytest
@@ -29,6 +30,13 @@ CASES = {
     "bias_f16_d64": W(name="lds_bias_f16_d64", seqlens_q=(900, 33), seqlens_kv=(900, 33), hq=2,
                       hkv=1, d_qk=64, d_v=64, dtype="f16", causal=False, bias="prefix_lm",
                       prefix=300, seed=92),
+    # the same biases as interval rows (key ranges and interval flags given)
+    "interval_bf16_d128": W(name="lds_interval_bf16_d128", seqlens_q=(600, 77),
+                            seqlens_kv=(600, 77), hq=4, hkv=2, d_qk=128, d_v=128, dtype="bf16",
+                            causal=False, bias="prefix_lm", prefix=150, seed=97),
+    "interval_f16_d64": W(name="lds_interval_f16_d64", seqlens_q=(900, 33), seqlens_kv=(900, 33),
+                          hq=2, hkv=1, d_qk=64, d_v=64, dtype="f16", causal=False,
+                          bias="prefix_lm", prefix=300, seed=98),
     "gqa_causal_bf16": W(name="lds_gqa_causal_bf16", seqlens_q=(1000, 333, 64),
                          seqlens_kv=(1000, 333, 64), hq=8, hkv=2, d_qk=128, d_v=128,
                          dtype="bf16", causal=True, seed=93),
@@ -54,14 +62,19 @@ def _library(lib):
 
 def _run(w, dev):
     q, k, v, cq, ck, b = dev
+    rg = pure = None
+    if w.name.startswith("lds_interval"):
+        rg, pure = fav.bias_key_ranges(b, cq, ck, w.max_seqlen_q, return_pure=True)
+        assert bool(pure.all())
     out, lse = fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, scale=w.softmax_scale,
                                     causal=w.causal, window=w.window, attn_bias=b,
-                                    out_dtype=torch.float32, return_lse=True)
+                                    out_dtype=torch.float32, return_lse=True, bias_ranges=rg,
+                                    bias_pure=pure)
     torch.cuda.synchronize()
     return out, lse
 
 
-@pytest.mark.parametrize("variant", ["slots2", "synccopies"])
+@pytest.mark.parametrize("variant", ["slots2", "synccopies", "shallow"])
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_schedule_variant_is_bitwise_equal(name, variant):
     w = CASES[name]
