@@ -164,7 +164,13 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
   tile_offsets<D, LOADS>(goff, a.do_st * 2, tid);
   const float c_scale = a.scale_log2;
 
-  // Stage iteration `it` (query head h = g * group + it % group, tile it / group).
+  // Stage iteration `it` (query head h = g * group + it % group, tile it / group):
+  // the Q and dO tiles go to LDS by direct copies; the rows' lse and delta
+  // are loaded into registers (first wave) and written to LDS by stage_lds
+  // once the step's copies have landed, so no wave waits for a load in the
+  // middle of a step.
+  float st_l = 0.0f, st_d = 0.0f;
+  bool st_row = false;
   auto stage = [&](int it, auto S) __attribute__((device)) {
     constexpr int s = decltype(S)::value;
     const int h = g * a.group + it % a.group;
@@ -174,17 +180,20 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
     const char* gb = reinterpret_cast<const char*>(a.dout) + ((int64_t)(cq0 + q0) * a.do_st + (int64_t)h * a.do_sh) * 2;
     load_tile<D, LOADS>(qb, a.q_st * 2, rows, (lds_char*)(s == 0 ? qt_0 : qt_1), qoff, wave);
     load_tile<D, LOADS>(gb, a.do_st * 2, rows, (lds_char*)(s == 0 ? gt_0 : gt_1), goff, wave);
+    st_row = tid < rows;
+    if (st_row) {
+      st_l = a.lse[(int64_t)h * a.total_q + cq0 + q0 + tid];
+      st_d = a.delta[(int64_t)h * a.total_q + cq0 + q0 + tid];
+    }
+  };
+  auto stage_lds = [&](auto S) __attribute__((device)) {
+    constexpr int s = decltype(S)::value;
     if (tid < BQ) {
       // log2-domain lse (+inf where the row does not exist or sees nothing:
       // its p is then exactly 0) and delta
-      float l2 = __builtin_inff(), d = 0.0f;
-      if (tid < rows) {
-        const float l = a.lse[(int64_t)h * a.total_q + cq0 + q0 + tid];
-        l2 = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
-        d = a.delta[(int64_t)h * a.total_q + cq0 + q0 + tid];
-      }
+      const float l2 = !st_row || st_l == -__builtin_inff() ? __builtin_inff() : st_l * kLog2e;
       (s == 0 ? ls_0 : ls_1)[tid] = l2;
-      (s == 0 ? dl_0 : dl_1)[tid] = d;
+      (s == 0 ? dl_0 : dl_1)[tid] = st_row ? st_d : 0.0f;
     }
   };
 
@@ -267,16 +276,19 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
     using S1 = std::integral_constant<int, 1>;
     stage(0, S0{});
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    stage_lds(S0{});
     __syncthreads();
     for (int it = 0; it < n_it; it += 2) {
       if (it + 1 < n_it) stage(it + 1, S1{});
       compute(it, S0{});
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      if (it + 1 < n_it) stage_lds(S1{});
       __syncthreads();
       if (it + 1 < n_it) {
         if (it + 2 < n_it) stage(it + 2, S0{});
         compute(it + 1, S1{});
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        if (it + 2 < n_it) stage_lds(S0{});
         __syncthreads();
       }
     }
