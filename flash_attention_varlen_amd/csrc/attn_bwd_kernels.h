@@ -80,6 +80,11 @@ __device__ __forceinline__ void store_grad4(T* p, float a, float b, float c, flo
 // dkdv_kernel
 // ----------------------------------------------------------------------------
 // ALIBI: the bias is -slope * |query position - key|, computed (BIAS set too).
+// MFMA operands of the dK / dV kernel are read this many MFMAs ahead.
+#ifndef MI_ATTN_BWD_AHEAD
+#define MI_ATTN_BWD_AHEAD 4
+#endif
+
 template <typename T, int D, typename GradT, bool BIAS, bool ALIBI = false>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
   constexpr int BK = 128;              // keys per workgroup (32 per wave)
@@ -215,16 +220,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
     // Entry e of block qb is query row q0 + 32 qb + 8 (e/4) + 4 hf + e%4 and key my_key.
     const bool need_mask = (causal && kw1 - 1 > q0 + off) || (W > 0 && kw0 <= q0 + BQ - 1 + off - W);
     u32x4_t pb[2][2], sb[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16_t sc, dp;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sc[e] = dp[e] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sc = E::mma(row_frag<D>(qt, 32 * qb + l32, ks, hf), kf[ks], sc);
-        dp = E::mma(row_frag<D>(gt, 32 * qb + l32, ks, hf), vf[ks], dp);
-      }
+    // P and dS of one 32-row block from its scores sc and dP values dp; the
+    // causal / window mask (MASK) only where the step's tile crosses it.
+    auto probs = [&](int qb, f32x16_t& sc, f32x16_t& dp, auto MASK) __attribute__((device)) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 32 * qb + 8 * j + 4 * hf;  // tile row of entries 4j .. 4j + 3
@@ -245,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
             x = __builtin_fmaf(b, kLog2e, x);
           }
           float p = fast_exp2(x - l2[i]);
-          if (need_mask) {
+          if constexpr (decltype(MASK)::value) {
             const int row = q0 + r + i;
             const bool vis = (!causal || my_key <= row + off) && (W == 0 || my_key > row + off - W);
             p = vis ? p : 0.0f;
@@ -254,21 +252,63 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
           dp[e] = p * (dp[e] - dd[i]);
         }
       }
+    };
+    // With one wave per SIMD nothing hides an LDS read's latency but the
+    // wave's own work: every MFMA's operand is read MI_ATTN_BWD_AHEAD MFMAs
+    // before it (a ring of fragments), and scheduling fences keep that order.
+    constexpr int AH = MI_ATTN_BWD_AHEAD;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16_t sc, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[e] = dp[e] = 0.0f;
+      // S = Q K^T, dP = dO V^T: MFMA i takes a Q (even i) or dO (odd i)
+      // fragment of k-step i / 2
+      auto rd_s = [&](int i) __attribute__((device)) -> u32x4_t {
+        return row_frag<D>((i & 1) ? gt : qt, 32 * qb + l32, i >> 1, hf);
+      };
+      u32x4_t fr[AH + 1];
+#pragma unroll
+      for (int i = 0; i < AH; ++i) fr[i] = rd_s(i);
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) {
+        if (i + AH < 2 * KS) fr[(i + AH) % (AH + 1)] = rd_s(i + AH);
+        if (i & 1)
+          dp = E::mma(fr[i % (AH + 1)], vf[i >> 1], dp);
+        else
+          sc = E::mma(fr[i % (AH + 1)], kf[i >> 1], sc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (need_mask)
+        probs(qb, sc, dp, std::true_type{});
+      else
+        probs(qb, sc, dp, std::false_type{});
       pb[qb][0] = pack_b<T>(sc, 0);
       pb[qb][1] = pack_b<T>(sc, 1);
       sb[qb][0] = pack_b<T>(dp, 0);
       sb[qb][1] = pack_b<T>(dp, 1);
     }
-    // dV^T += dO^T P, dK^T += Q^T dS (reduction over the 64 query rows)
+    // dV^T += dO^T P, dK^T += Q^T dS (reduction over the 64 query rows):
+    // MFMA i is (block, k-step, d block) = i / (4 NDB), (i / (2 NDB)) % 2,
+    // (i / 2) % NDB, dV (even i) or dK (odd i)
+    constexpr int NT = 8 * NDB;
+    auto rd_t = [&](int i) __attribute__((device)) -> u32x4_t {
+      const int qb = i / (4 * NDB), kk = (i / (2 * NDB)) % 2, db = (i / 2) % NDB;
+      return tr_frag<D>((i & 1) ? qt : gt, 2 * qb + kk, db, lane);
+    };
+    u32x4_t tf[AH + 1];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int i = 0; i < AH; ++i) tf[i] = rd_t(i);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dv[db] = E::mma(tr_frag<D>(gt, 2 * qb + kk, db, lane), pb[qb][kk], dv[db]);
-          dk[db] = E::mma(tr_frag<D>(qt, 2 * qb + kk, db, lane), sb[qb][kk], dk[db]);
-        }
+    for (int i = 0; i < NT; ++i) {
+      if (i + AH < NT) tf[(i + AH) % (AH + 1)] = rd_t(i + AH);
+      const int qb = i / (4 * NDB), kk = (i / (2 * NDB)) % 2, db = (i / 2) % NDB;
+      if (i & 1)
+        dk[db] = E::mma(tf[i % (AH + 1)], sb[qb][kk], dk[db]);
+      else
+        dv[db] = E::mma(tf[i % (AH + 1)], pb[qb][kk], dv[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   if (n_it > 0) {
