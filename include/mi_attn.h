@@ -1,7 +1,8 @@
 /*
  * mi_attn — fused variable-length attention for AMD MI355X (gfx950): the
- * forward, a split-KV decode form of it, its backward, and the bias
- * key-range pass.
+ * forward, a split-KV decode form of it, its backward, the bias key-range
+ * pass (tile skipping and interval rows) and the key-padding front end
+ * (padded batch <-> packed varlen).
  *
  * C ABI.  No HIP or PyTorch types appear in the signatures: device buffers
  * are plain pointers, sizes and strides are integers, the stream is an
