@@ -17,17 +17,20 @@ pytestmark = pytest.mark.gpu
 W = workloads.Workload
 
 
-def _interval_bias(seqlens, heads, cols, seed, impure_every=0):
+def _interval_bias(seqlens, heads, cols, seed, impure_every=0, seqlens_kv=None):
     """fp32 bias whose rows are 0 on a random key interval (causal-like,
     window-like or arbitrary) and -inf elsewhere; with impure_every > 0,
     every impure_every-th row is spoiled in one of four ways (a -inf hole, a
-    nonzero value, a NaN-free negative value, or -0.0, which stays pure)."""
+    nonzero value, a NaN-free negative value, or -0.0, which stays pure).
+    Key intervals lie within each sequence's key length (seqlens_kv, by
+    default the query lengths)."""
     g = torch.Generator().manual_seed(seed)
     tq = int(sum(seqlens))
     b = torch.full((tq, heads, cols), float("-inf"))
     t0 = 0
-    for n in seqlens:
-        for i in range(n):
+    for nq, n in zip(seqlens, seqlens_kv or seqlens):
+        for r in range(nq):
+            i = min(r, n - 1)  # the row's position among the keys (clamped)
             for h in range(heads):
                 kind = int(torch.randint(0, 3, (1,), generator=g))
                 if kind == 0:      # causal with a prefix
@@ -38,12 +41,12 @@ def _interval_bias(seqlens, heads, cols, seed, impure_every=0):
                 else:              # anywhere
                     lo = int(torch.randint(0, n, (1,), generator=g))
                     hi = int(torch.randint(lo + 1, n + 1, (1,), generator=g))
-                b[t0 + i, h, lo:hi] = 0.0
-                if impure_every and (t0 + i) % impure_every == 0 and hi - lo >= 3:
-                    how = (t0 + i) // impure_every % 4
+                b[t0 + r, h, lo:hi] = 0.0
+                if impure_every and (t0 + r) % impure_every == 0 and hi - lo >= 3:
+                    how = (t0 + r) // impure_every % 4
                     mid = (lo + hi) // 2
-                    b[t0 + i, h, mid] = [float("-inf"), 0.75, -2.0, -0.0][how]
-        t0 += n
+                    b[t0 + r, h, mid] = [float("-inf"), 0.75, -2.0, -0.0][how]
+        t0 += nq
     return b
 
 
@@ -87,7 +90,8 @@ def test_interval_flags_match_oracle(kind):
 @pytest.mark.parametrize("case", ["prefix_f16_d128", "prefix_bf16_d64", "intervals_bf16_d128",
                                   "mixed_f16_d128", "mixed_bf16_d64", "intervals_bf16_d192",
                                   "intervals_f16_d256", "intervals_bf16_d96", "mask_f16_d128",
-                                  "intervals_f32_d64"])
+                                  "intervals_f32_d64", "causal_bf16_d128", "window_f16_d64",
+                                  "cross_bf16_d128"])
 def test_forward_with_interval_rows_is_exact(case):
     """A wave whose rows are all intervals reads no bias and masks each row
     to its range: output and LSE equal, bit for bit, those of the forward
@@ -97,15 +101,19 @@ def test_forward_with_interval_rows_is_exact(case):
     d = int(d[1:])
     dqk, dv = (192, 128) if d == 192 else (d, d)
     lens = (700, 257, 1) if kind == "prefix" else (500, 130, 33)
+    # cross attention: more keys than queries in one sequence, fewer in another
+    lens_kv = (620, 90, 33) if kind == "cross" else lens
     hq = 4
-    w = W(name=f"interval_{case}", seqlens_q=lens, seqlens_kv=lens, hq=hq, hkv=2, d_qk=dqk,
-          d_v=dv, dtype=dt, causal=False, seed=82)
+    # the masks compose with the interval rows (causal / window flags too)
+    causal = kind in ("causal", "window", "cross")
+    w = W(name=f"interval_{case}", seqlens_q=lens, seqlens_kv=lens_kv, hq=hq, hkv=2, d_qk=dqk,
+          d_v=dv, dtype=dt, causal=causal, window=100 if kind == "window" else 0, seed=82)
     inp = workloads.make_inputs(w)
     if kind == "prefix":
         inp.bias = workloads.prefix_lm_bias(lens, 100, max(lens))
     else:
-        inp.bias = _interval_bias(lens, hq if kind != "mask" else 1, max(lens), seed=83,
-                                  impure_every=37 if kind == "mixed" else 0)
+        inp.bias = _interval_bias(lens, hq if kind != "mask" else 1, max(lens_kv), seed=83,
+                                  impure_every=37 if kind == "mixed" else 0, seqlens_kv=lens_kv)
     dev = "cuda"
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     cq, ck = inp.cu_seqlens_q.to(dev), inp.cu_seqlens_kv.to(dev)
@@ -117,7 +125,8 @@ def test_forward_with_interval_rows_is_exact(case):
     tc1 = torch.zeros(n_qt * w.num_seqs * hq, dtype=torch.int32, device=dev)
     tc2 = torch.zeros_like(tc1)
     say(f"[interval fwd] {case}")
-    kw = dict(attn_bias=b, out_dtype=torch.float32, return_lse=True)
+    flags = dict(causal=w.causal, window=w.window)
+    kw = dict(attn_bias=b, out_dtype=torch.float32, return_lse=True, **flags)
     out0, lse0 = fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, **kw)
     rg, pure = fav.bias_key_ranges(b, cq, ck, w.max_seqlen_q, return_pure=True)
     out1, lse1 = fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, bias_ranges=rg,
@@ -125,9 +134,10 @@ def test_forward_with_interval_rows_is_exact(case):
     out2, lse2 = fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, bias_ranges=rg,
                                       bias_pure=pure, tile_counts=tc2, **kw)
     # the input-type output too (the timed configuration)
-    o16 = fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, attn_bias=b, bias_ranges=rg)
+    o16 = fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, attn_bias=b, bias_ranges=rg,
+                               **flags)
     o16p = fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, attn_bias=b, bias_ranges=rg,
-                                bias_pure=pure)
+                                bias_pure=pure, **flags)
     torch.cuda.synchronize()
     say(f"  interval rows {int(pure.sum())} of {pure.numel()}")
     assert torch.equal(out2, out1) and torch.equal(lse2, lse1), "interval masking changed the result"
