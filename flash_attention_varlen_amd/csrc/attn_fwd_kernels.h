@@ -825,8 +825,7 @@ struct WaveBlocks {
   // block and Q fragments need the registers of a whole SIMD per wave.
   static constexpr int OCC = DV == 256 ? 1 : 2;
   // K/V buffer slots.  Where four of each fit the LDS share of a workgroup
-  // (80 KB with two per CU) copies run one more step ahead and the
-  // workgroup synchronises every second step instead of every step.
+  // (80 KB with two per CU) copies run further ahead (step()).
   static constexpr int NSLOT =
       MI_ATTN_MAX_SLOTS >= 4 &&
               4 * 32 * NMB * (lds_dim(DQK) + lds_dim(DV)) * 2 <= (OCC == 1 ? 152 : 80) * 1024
@@ -1412,10 +1411,11 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     // (slot + u) % NSLOT.  This step reads K(t+1) and V(t) and starts the
     // copies of K(t+LK) and V(t+LV), into the slots of the tiles read
     // NSLOT - LK + 1 steps earlier.  With two slots every step ends with a
-    // barrier; with four, copies start one step further ahead and only odd
-    // steps end with one.  Either way a barrier separates the last read of a
-    // slot from the copy that refills it, and the end of a copy (each wave's
-    // vmcnt wait at its step's end) from the first read of its tile.
+    // barrier.  With four (MI_ATTN_DEEP_COPIES=0), copies start one step
+    // further ahead and only odd steps end with one.  Either way a barrier
+    // separates the last read of a slot from the copy that refills it, and
+    // the end of a copy (each wave's vmcnt wait at its step's end) from the
+    // first read of its tile.
     //
     // Deep copies (four slots, a barrier after every step): K(t+4) goes to
     // the slot of K(t), last read in step t-1, and V(t+3) to that of V(t-1),
