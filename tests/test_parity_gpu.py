@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import flash_attention_varlen_amd as fav
 import workloads
 from gpu_helpers import (check, check_sampled, run_gpu, run_oracle, say, to_device)
 
@@ -277,12 +278,22 @@ def test_full_size_workload_sampled(name):
     say(f"[full] {name}")
     inp = workloads.make_inputs(w)
     dev = to_device(inp)
-    out32, lse32 = run_gpu(inp, out_dtype=torch.float32, dev=dev)
+    kw = {}
+    if inp.bias is not None:
+        # the benchmark's launch: the bias rows' key ranges and interval flags
+        q, k, v, cq, ck, b = dev
+        rg, pure = fav.bias_key_ranges(b, cq, ck, w.max_seqlen_q, return_pure=True)
+        kw = dict(bias_ranges=rg, bias_pure=pure)
+    out32, lse32 = run_gpu(inp, out_dtype=torch.float32, dev=dev, **kw)
     # every query head, on sampled rows of every sequence (tile edges, both
     # ends and random rows)
     check_sampled(inp, out32, lse32, list(range(w.hq)), rows_per_seq=12 if w.total_q > 50000 else 24)
     if w.dtype != "f32":
-        outn, lsen = run_gpu(inp, out_dtype=inp.q.dtype, dev=dev)
+        outn, lsen = run_gpu(inp, out_dtype=inp.q.dtype, dev=dev, **kw)
         assert torch.equal(outn, out32.to(inp.q.dtype)), "16-bit output is not RNE(fp32 output)"
         assert torch.equal(lsen, lse32)
+    if kw:
+        # the same as reading the whole bias, bit for bit
+        out_b, lse_b = run_gpu(inp, out_dtype=torch.float32, dev=dev)
+        assert torch.equal(out_b, out32) and torch.equal(lse_b, lse32)
     assert torch.isfinite(out32).all()
