@@ -92,3 +92,18 @@ def test_decode_is_deterministic():
     a = _decode(inp)
     b = _decode(inp)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_decode_full_size_workload():
+    """The benchmark's decode workload (eight one-row sequences against 10K
+    to 51K cached keys, Hq = 32, Hkv = 8, D = 128) in its launch (automatic
+    split count): every row of every head against the oracle, and the bf16
+    output equal to the RNE rounding of the fp32 one."""
+    w = workloads.ALL["decode_bf16"]
+    inp = workloads.make_inputs(w)
+    say(f"[decode] full size {w.name}: kv {w.seqlens_kv}")
+    out, lse = _decode(inp)
+    ref_out, ref_lse = run_oracle(inp)
+    check(w.name, out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, w.dtype)
+    out16, lse16 = _decode(inp, 0, inp.q.dtype)
+    assert torch.equal(out16, out.to(inp.q.dtype)) and torch.equal(lse16, lse)
