@@ -266,7 +266,8 @@ def test_outlier_channels_fp32_accumulation():
 
 FULL = ["tiny_f32", "gqa_causal_bf16", "dense_f16_d128_full", "dense_f16_d128_causal",
         "dense_f16_d128_prefix_lm", "dense_f16_d64_full", "dense_f16_d64_causal",
-        "dense_f16_d64_prefix_lm", "swa_bf16", "mla_bf16"]
+        "dense_f16_d64_prefix_lm", "swa_bf16", "mla_bf16", "dense_bf16_d96_causal",
+        "dense_bf16_d256_causal"]
 
 
 @pytest.mark.parametrize("name", FULL)

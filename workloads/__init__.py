@@ -84,7 +84,7 @@ def cfg2_lengths() -> list:
     return torch.randint(512, 4097, (8,), generator=g).tolist()
 
 
-# The five workloads.  Names say what each is; sizes are spelled out.
+# The workloads.  Names say what each is; sizes are spelled out.
 TINY_F32 = Workload(
     name="tiny_f32_full_3seq_h2_d64", seqlens_q=(17, 64, 129), seqlens_kv=(17, 64, 129),
     hq=2, hkv=2, d_qk=64, d_v=64, dtype="f32", causal=False, scale=1.0 / 8.0, seed=0,
@@ -106,6 +106,17 @@ def dense_f16(d: int, causal: bool, bias: bool = False) -> Workload:
         hq=16, hkv=16, d_qk=d, d_v=d, dtype="f16", causal=causal,
         scale=1.0 / math.sqrt(d), bias="prefix_lm" if bias else None, prefix=1024, seed=3,
         description=f"fp16 dense B=4 L=8192 H=16 D={d} {tag}")
+
+
+def dense_bf16_head(d: int) -> Workload:
+    """The head dims 96 and 256 at the dense causal shape (measurement of the
+    head-dim variants)."""
+    L = (8192,) * 4
+    return Workload(
+        name=f"dense_bf16_b4_l8192_h16_d{d}_causal", seqlens_q=L, seqlens_kv=L,
+        hq=16, hkv=16, d_qk=d, d_v=d, dtype="bf16", causal=True,
+        scale=1.0 / math.sqrt(d), seed=7,
+        description=f"bf16 dense causal B=4 L=8192 H=16 D={d}")
 
 
 SWA_BF16 = Workload(
@@ -142,6 +153,8 @@ ALL = {
     "dense_f16_d64_full": dense_f16(64, False),
     "dense_f16_d64_causal": dense_f16(64, True),
     "dense_f16_d64_prefix_lm": dense_f16(64, False, bias=True),
+    "dense_bf16_d96_causal": dense_bf16_head(96),
+    "dense_bf16_d256_causal": dense_bf16_head(256),
     "swa_bf16": SWA_BF16,
     "mla_bf16": MLA_BF16,
     "decode_bf16": DECODE_BF16,
