@@ -203,6 +203,10 @@ def main():
                     help="with a bias, do not compute the bias key ranges (visit every tile)")
     ap.add_argument("--window", type=int, default=None,
                     help="override the window width of a sliding-window workload (cost vs W)")
+    ap.add_argument("--sdpa-keypad", action="store_true",
+                    help="time the key-padding front end: the workload's sequences as a padded "
+                         "[B, H, N, D] batch with a bool key-padding mask through sdpa() (mask "
+                         "scan, packing, the forward, unpacking), self-attention without a bias")
     ap.add_argument("--no-interval-rows", action="store_true",
                     help="with a bias: compute its key ranges only, so that the forward reads "
                          "the bias of every row (no interval flags)")
@@ -304,7 +308,33 @@ def main():
         dq_b, dk_b, dv_b = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         torch.cuda.synchronize()
 
+    if args.sdpa_keypad:
+        if (bias is not None or w.window or list(w.seqlens_q) != list(w.seqlens_kv)
+                or is_decode or args.backward or rope_kw):
+            print("--sdpa-keypad takes a self-attention forward workload without a bias or window",
+                  file=sys.stderr)
+            sys.exit(2)
+        # the sequences right-padded into [B, N, H, D] buffers, seen as SDPA's [B, H, N, D]
+        nmax = max(w.seqlens_q)
+        pads = []
+        for t in (q, k, v):
+            buf = torch.zeros(w.num_seqs, nmax, t.shape[1], t.shape[2], dtype=t.dtype, device=dev)
+            for i, n in enumerate(w.seqlens_q):
+                c0 = int(inp.cu_seqlens_q[i])
+                buf[i, :n] = t[c0:c0 + n]
+            pads.append(buf.transpose(1, 2))
+        keymask = torch.zeros(w.num_seqs, nmax, dtype=torch.bool, device=dev)
+        for i, n in enumerate(w.seqlens_q):
+            keymask[i, :n] = True
+        keymask4 = keymask[:, None, None, :]
+
     def step(mid_event=None):
+        if args.sdpa_keypad:
+            if mid_event is not None:
+                mid_event.record(stream)
+            fav.sdpa(pads[0], pads[1], pads[2], attn_mask=keymask4, is_causal=w.causal,
+                     scale=w.softmax_scale, enable_gqa=True, stream=stream)
+            return
         if is_decode:
             if mid_event is not None:
                 mid_event.record(stream)
@@ -463,6 +493,8 @@ def main():
             "algorithmic_bytes": algorithmic_bytes(w, out_bytes),
             "kernel": ("decode_kernel + decode_merge_kernel" if is_decode else
                        "delta_kernel + dkdv_kernel + dq_kernel" if args.backward else
+                       "sdpa key-padding front end (whole step: mask scan, packs, "
+                       "attn_fwd16p_kernel, unpack)" if args.sdpa_keypad else
                        "attn_fwd_kernel" if w.dtype == "f32" else "attn_fwd16p_kernel"),
             "kernel_ms": round(kernel_ms, 4),
         },
@@ -473,6 +505,10 @@ def main():
     if args.backward:
         result["config"]["pass"] = "backward"
         result["cpu_baseline"] = None  # the oracle baseline is timed for the forward only
+    if args.sdpa_keypad:
+        result["config"]["front_end"] = (f"sdpa: [B={w.num_seqs}, H, N={max(w.seqlens_q)}, D] "
+                                         f"right-padded batch, bool key-padding mask")
+        result["roofline"]["traffic"] = None
     unit = "GB/s" if is_decode else "useful TFLOP/s"
     print(f"# GPU: {ms_per_step:.4f} ms/step, {value:.1f} {unit} "
           f"({100 * value / peak:.1f}% of {peak})", file=sys.stderr, flush=True)

@@ -68,6 +68,7 @@ class MiAttnFwdParams(ctypes.Structure):
         ("alibi_slopes", ctypes.c_void_p), ("alibi_stride_seq", ctypes.c_int64),
         ("mask", ctypes.c_void_p),
         ("bias_pure", ctypes.c_void_p),
+        ("seqused_q", ctypes.c_void_p), ("seqused_kv", ctypes.c_void_p),
     ]
 
 
@@ -221,7 +222,7 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
                      attn_bias=None, out_dtype=None, return_lse: bool = False, out=None,
                      lse=None, tile_counts=None, stream=None, bias_ranges=None,
                      max_seqlen_kv=None, q_rope=None, k_rope=None, alibi_slopes=None,
-                     bias_pure=None):
+                     bias_pure=None, seqused_q=None, seqused_kv=None):
     """Fused varlen attention forward.  Returns ``out`` or ``(out, lse)``.
 
     q ``[Tq, Hq, Dqk]``, k ``[Tk, Hkv, Dqk]``, v ``[Tk, Hkv, Dv]`` (device,
@@ -256,6 +257,11 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     ``alibi_slopes`` (fp32 ``[Hq]`` or ``[num_seqs, Hq]``, device): the
     kernels add ``-slope * |i + (Lk - Lq) - j|`` to the logit of query row i
     and key j (no bias tensor with it); differentiable like a bias.
+
+    ``seqused_q`` / ``seqused_kv`` (int32 ``[num_seqs]``, device): sequence s
+    uses only the first ``seqused[s]`` rows of its span (a right-padded batch
+    with spans of the padded length); rows of ``out`` past ``seqused_q`` are
+    0 and their ``lse`` -inf (forward only).
     """
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -304,6 +310,8 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
         if attn_bias is not None and attn_bias.requires_grad:
             raise MiAttnError(ERR_UNSUPPORTED, "the bias is a constant: a bias that requires grad "
                                                "is refused")
+        if seqused_q is not None or seqused_kv is not None:
+            raise MiAttnError(ERR_UNSUPPORTED, "seqused_q / seqused_kv are forward only")
         if out_dtype != q.dtype or q.dtype == torch.float32 or out is not None or \
                 lse is not None or tile_counts is not None:
             raise MiAttnError(ERR_UNSUPPORTED,
@@ -316,6 +324,11 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
                                              alibi_slopes)
         return (o, l) if return_lse else o
     s_obj = _stream_of(stream, q.device)
+    for name, t in (("seqused_q", seqused_q), ("seqused_kv", seqused_kv)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()
+                              or tuple(t.shape) != (cu_seqlens_q.numel() - 1,)):
+            raise MiAttnError(ERR_INVALID_ARG, f"{name} must be a contiguous int32 [num_seqs] "
+                                               "device tensor")
     if bias_ranges is not None:
         if attn_bias is None:
             raise MiAttnError(ERR_INVALID_ARG, "bias_ranges needs the attn_bias it was computed from")
@@ -333,7 +346,7 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
                                            scale, causal, window, attn_bias, out_dtype,
                                            return_lse, out, lse, tile_counts, s_obj, tq, hq, dqk,
                                            tk, hkv, dv, bias_ranges, q_rope, k_rope,
-                                           alibi_slopes, bias_pure)
+                                           alibi_slopes, bias_pure, seqused_q, seqused_kv)
 
 
 def _stream_of(stream, device):
@@ -429,7 +442,8 @@ def _aligned_bias(bias):
 def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, scale, causal,
                                 window, attn_bias, out_dtype, return_lse, out, lse, tile_counts,
                                 s_obj, tq, hq, dqk, tk, hkv, dv, bias_ranges=None, q_rope=None,
-                                k_rope=None, alibi_slopes=None, bias_pure=None):
+                                k_rope=None, alibi_slopes=None, bias_pure=None, seqused_q=None,
+                                seqused_kv=None):
     import torch
     bias = attn_bias
     if bias is not None:
@@ -462,6 +476,8 @@ def _varlen_attention_on_stream(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen
         p.bias = bias.data_ptr() if bias is not None else None
     p.bias_ranges = bias_ranges.data_ptr() if bias_ranges is not None else None
     p.bias_pure = bias_pure.data_ptr() if bias_pure is not None else None
+    p.seqused_q = seqused_q.data_ptr() if seqused_q is not None else None
+    p.seqused_kv = seqused_kv.data_ptr() if seqused_kv is not None else None
     if q_rope is not None:
         p.q_rope, p.k_rope = q_rope.data_ptr(), k_rope.data_ptr()
         p.q_rope_stride_tok, p.q_rope_stride_head = q_rope.stride(0), q_rope.stride(1)
@@ -633,12 +649,14 @@ def _fwd_params(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, scale, causa
 def varlen_decode(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int, max_seqlen_kv: int,
                   scale: Optional[float] = None, causal: bool = False, window: int = 0,
                   num_splits: int = 0, out_dtype=None, return_lse: bool = False, out=None,
-                  lse=None, workspace=None, stream=None):
+                  lse=None, workspace=None, stream=None, seqused_kv=None):
     """Split-KV decode (``mi_attn_varlen_decode``): the forward for few query
     rows per sequence against long key/value caches.  Same arguments and
     results as ``varlen_attention`` (bf16 / fp16, head dims 64 / 128, no
-    bias), plus ``max_seqlen_kv``, ``num_splits`` (0 = auto) and an optional
-    preallocated uint8 ``workspace`` (else allocated on the stream)."""
+    bias), plus ``max_seqlen_kv``, ``num_splits`` (0 = auto), an optional
+    preallocated uint8 ``workspace`` (else allocated on the stream) and
+    ``seqused_kv`` (int32 ``[num_seqs]``: the keys in use of each sequence's
+    cache span)."""
     import torch
     tq, hq, dqk = q.shape
     dv = v.shape[2]
@@ -653,6 +671,12 @@ def varlen_decode(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int, max_s
             lse = torch.empty(hq, tq, dtype=torch.float32, device=q.device)
         p = _fwd_params(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, scale, causal, window,
                         out, lse, out_dtype)
+        if seqused_kv is not None:
+            if (seqused_kv.dtype != torch.int32 or not seqused_kv.is_contiguous()
+                    or tuple(seqused_kv.shape) != (cu_seqlens_q.numel() - 1,)):
+                raise MiAttnError(ERR_INVALID_ARG, "seqused_kv must be a contiguous int32 "
+                                                   "[num_seqs] device tensor")
+            p.seqused_kv = seqused_kv.data_ptr()
         need = mi_attn_decode_workspace_size(p, int(max_seqlen_kv), int(num_splits))
         if workspace is None:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -796,6 +820,50 @@ def padding_to_varlen(mask, stream=None, sync: bool = True):
     return ranks, cu, total, longest
 
 
+def mi_attn_padding_lengths(mask_ptr: int, batch: int, seqlen: int, mask_stride_batch: int,
+                            lengths_ptr: int, spans_ptr: int, stats_ptr: int,
+                            stream: int = 0) -> None:
+    """Call the C entry point; raise MiAttnError on a non-OK return."""
+    lib = load_library()
+    f = lib.mi_attn_padding_lengths
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    rc = f(mask_ptr, batch, seqlen, mask_stride_batch, lengths_ptr, spans_ptr, stats_ptr,
+           ctypes.c_void_p(stream))
+    if rc != OK:
+        raise MiAttnError(rc, mi_attn_last_error())
+
+
+def padding_lengths(mask, stream=None, sync: bool = True):
+    """Right-padding check of a key-padding mask (bool or uint8 ``[B, N]`` on
+    the device, True = valid token).  Returns ``(lengths, spans, right_padded,
+    longest)``: int32 ``[B]`` valid counts, int32 ``[B + 1]`` spans ``b * N``
+    and, with ``sync`` (one device-to-host read), whether every row's valid
+    tokens are its first ones and the longest row (else the int32 ``[2]``
+    device tensor).  For a right-padded batch the forward takes the padded
+    tensors as they are: ``cu_seqlens = spans``, ``seqused_q = seqused_kv =
+    lengths``."""
+    import torch
+    if mask.dim() != 2 or not mask.is_cuda or mask.dtype not in (torch.bool, torch.uint8):
+        raise MiAttnError(ERR_INVALID_ARG, "mask must be a bool / uint8 [B, N] device tensor")
+    if mask.shape[1] > 1 and mask.stride(1) != 1:
+        mask = mask.contiguous()
+    bsz, n = mask.shape
+    s_obj = _stream_of(stream, mask.device)
+    with torch.cuda.stream(s_obj):
+        lengths = torch.empty(bsz, dtype=torch.int32, device=mask.device)
+        spans = torch.empty(bsz + 1, dtype=torch.int32, device=mask.device)
+        stats = torch.empty(2, dtype=torch.int32, device=mask.device)
+        mi_attn_padding_lengths(mask.data_ptr(), bsz, n, mask.stride(0) if bsz > 1 else n,
+                                lengths.data_ptr(), spans.data_ptr(), stats.data_ptr(),
+                                int(s_obj.cuda_stream))
+    if not sync:
+        return lengths, spans, stats
+    right, longest = (int(x) for x in stats.tolist())
+    return lengths, spans, bool(right), longest
+
+
 def _pack_params(padded, packed, ranks, cu, bsz, n):
     p = MiAttnPackParams()
     p.padded, p.packed = padded.data_ptr(), packed.data_ptr()
@@ -868,7 +936,10 @@ def sdpa(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: b
     * A boolean key-padding mask (``[B, 1, 1, Nkv]`` or ``[B, Nkv]``, True =
       valid) is turned into varlen form: the valid keys (and, for
       self-attention, the valid queries) are packed and padding is never
-      computed.  Output rows of padded queries are 0.
+      computed.  Output rows of padded queries are 0.  A right-padded
+      self-attention batch whose tensors are views of token-major
+      ``[B, N, H, D]`` storage needs no packing: it runs in place, and the
+      output is then returned as such a view too.
     * Any other mask (bool or float, broadcastable to ``[B, H, Nq, Nkv]``)
       becomes the kernel's additive bias (bool: True -> 0, False -> -inf).
     * ``is_causal`` follows SDPA's top-left diagonal, which equals the
@@ -905,9 +976,24 @@ def sdpa(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: b
         # token-major views [B, N, H, D] of the head-major inputs: no copy
         qv, kv_, vv = query.transpose(1, 2), key.transpose(1, 2), value.transpose(1, 2)
         out_dtype = query.dtype if out_dtype is None else out_dtype
+        keymask = _key_padding_of(attn_mask, bsz, nkv)
+        if keymask is not None and nq == nkv and all(
+                t.stride(0) == nq * t.stride(1) for t in (qv, kv_, vv)):
+            # self-attention on token-major storage: a right-padded batch runs
+            # in place (spans of N tokens, the first lengths[b] used), no packing
+            lengths, spans, right, _ = padding_lengths(keymask, stream=s_obj)
+            if right:
+                flat = [t.as_strided((bsz * nq, t.shape[2], t.shape[3]),
+                                     (t.stride(1), t.stride(2), t.stride(3)))
+                        for t in (qv, kv_, vv)]
+                out_tm = torch.empty(bsz, nq, hq, dv, dtype=out_dtype, device=dev)
+                varlen_attention(flat[0], flat[1], flat[2], spans, spans, nq, scale=scale,
+                                 causal=is_causal, out_dtype=out_dtype, stream=s_obj,
+                                 out=out_tm.view(bsz * nq, hq, dv), seqused_q=lengths,
+                                 seqused_kv=lengths)
+                return out_tm.transpose(1, 2)
         out = torch.empty(bsz, hq, nq, dv, dtype=out_dtype, device=dev)
         ov = out.transpose(1, 2)
-        keymask = _key_padding_of(attn_mask, bsz, nkv)
         if keymask is not None:
             rk, cu_k, tot_k, max_k = padding_to_varlen(keymask, stream=s_obj)
             if nq == nkv:

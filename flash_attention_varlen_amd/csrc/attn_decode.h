@@ -13,6 +13,7 @@ struct DecodeArgs {
   const void* v;
   const int32_t* cu_q;
   const int32_t* cu_kv;
+  const int32_t* seqused_kv;  // optional [num_seqs]: keys used of each sequence's span
   float* ws_o;   // [n_chunks, total_q, hq, d_v] unnormalised partial outputs
   float* ws_ml;  // [n_chunks, total_q, hq, 2] running max (log2 units) and sum
   void* out;

@@ -55,9 +55,10 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   const int chunk = blockIdx.y;
   int cq0 = a.cu_q[seq], cq1 = a.cu_q[seq + 1];
   int ck0 = a.cu_kv[seq], ck1 = a.cu_kv[seq + 1];
-  asm volatile("" : "+s"(cq0), "+s"(cq1), "+s"(ck0), "+s"(ck1));
+  int uk = a.seqused_kv != nullptr ? a.seqused_kv[seq] : 0x7fffffff;
+  asm volatile("" : "+s"(cq0), "+s"(cq1), "+s"(ck0), "+s"(ck1), "+s"(uk));
   const int lq = cq1 - cq0;
-  const int lk = ck1 - ck0;
+  const int lk = max(0, min(ck1 - ck0, uk));  // the cache keys in use
   const int off = lk - lq;
   const bool causal = a.causal != 0;
   const int W = a.window;

@@ -25,6 +25,9 @@ struct KernelArgs {
   float* lse;
   const int32_t* cu_q;
   const int32_t* cu_kv;
+  // optional [num_seqs]: sequence s uses the first seqused[s] rows of its span
+  const int32_t* seqused_q;
+  const int32_t* seqused_kv;
   const float* bias;
   const int32_t* bias_ranges;  // optional [bias_heads, total_q, 2] key ranges of the bias rows
   const void* q_rope;  // optional: last 64 dims of the 192-wide q / k (q, k then hold 128)

@@ -158,6 +158,12 @@ __device__ __forceinline__ KeyHull bias_key_hull(const int32_t* rg, int r0, int 
                  __builtin_amdgcn_readfirstlane(wave_max_i32(whi))};
 }
 
+// Rows of a sequence's span [cu[s], cu[s+1]) that it uses: the first
+// seqused[s] (clamped to the span), or all of them without seqused.
+__device__ __forceinline__ int used_rows(int span, const int32_t* seqused, int seq) {
+  return seqused != nullptr ? max(0, min(span, seqused[seq])) : span;
+}
+
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
@@ -301,10 +307,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
   const int head = blockIdx.x % a.hq;
   const int seq = blockIdx.x / a.hq;
   const int cq0 = a.cu_q[seq];
-  const int lq = a.cu_q[seq + 1] - cq0;
   const int ck0 = a.cu_kv[seq];
-  const int lk = a.cu_kv[seq + 1] - ck0;
-  const int n_qtiles = (lq + kBM - 1) / kBM;
+  // rows used (lq) and written (span_q: rows past lq get out 0, lse -inf)
+  const int span_q = a.cu_q[seq + 1] - cq0;
+  const int lq = used_rows(span_q, a.seqused_q, seq);
+  const int lk = used_rows(a.cu_kv[seq + 1] - ck0, a.seqused_kv, seq);
+  const int n_qtiles = (span_q + kBM - 1) / kBM;
   const int qtile = n_qtiles - 1 - (int)blockIdx.y;  // heaviest causal tiles first
   if (qtile < 0) return;
 
@@ -332,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
   }
   const int t_begin = kv_lo / BN;
   int t_end = kv_hi > 0 ? (kv_hi + BN - 1) / BN : 0;
-  if (t_end < t_begin) t_end = t_begin;
+  if (t_end < t_begin || r0 >= lq) t_end = t_begin;  // (no used row here: zeros only)
 
   if (a.tile_counts != nullptr && tid == 0 && qtile < (int)gridDim.y)
     a.tile_counts[((int64_t)qtile * a.num_seqs + seq) * a.hq + head] = t_end - t_begin;
@@ -631,10 +639,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const KernelArgs 
     __syncthreads();
   }
 
-  // ---- epilogue: out = O / l, lse = (m + log2 l) ln 2
-  if (!wave_active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!row_ok) return;
+  // ---- epilogue: out = O / l, lse = (m + log2 l) ln 2 (rows of the span
+  // past the used ones: 0 and -inf)
+  if (w0 >= span_q) return;
+  const float l_all = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = row_ok ? l_all : 0.0f;
+  if (my_row >= span_q) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   OutT* op = reinterpret_cast<OutT*>(a.out) + (int64_t)(cq0 + my_row) * a.o_st +
              (int64_t)head * a.o_sh;
@@ -971,12 +981,17 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   // past the early exit, one dependent wait at a time.
   int cq0 = a.cu_q[seq], cq1 = a.cu_q[seq + 1];
   int ck0 = a.cu_kv[seq], ck1 = a.cu_kv[seq + 1];
-  asm volatile("" : "+s"(cq0), "+s"(cq1), "+s"(ck0), "+s"(ck1)
+  int uq = a.seqused_q != nullptr ? a.seqused_q[seq] : 0x7fffffff;
+  int uk = a.seqused_kv != nullptr ? a.seqused_kv[seq] : 0x7fffffff;
+  asm volatile("" : "+s"(cq0), "+s"(cq1), "+s"(ck0), "+s"(ck1), "+s"(uq), "+s"(uk)
                : "s"(a.q_st), "s"(a.q_sh), "s"(a.k_st), "s"(a.k_sh), "s"(a.v_st), "s"(a.v_sh),
                  "s"(a.group), "s"(a.causal), "s"(a.window), "s"(a.n_qtiles));
-  const int lq = cq1 - cq0;
-  const int lk = ck1 - ck0;
-  const int n_qtiles = (lq + BM - 1) / BM;
+  // rows of the sequence's spans that it uses (all of them without seqused);
+  // the output rows of the span past lq are written as 0 (lse -inf)
+  const int span_q = cq1 - cq0;
+  const int lq = max(0, min(span_q, uq));
+  const int lk = max(0, min(ck1 - ck0, uk));
+  const int n_qtiles = (span_q + BM - 1) / BM;
   const int qtile = a.n_qtiles - 1 - by;
   if (qtile >= n_qtiles) return;
 
@@ -1009,7 +1024,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   }
   const int t_begin = kv_lo / BN;
   int t_end = kv_hi > 0 ? (kv_hi + BN - 1) / BN : 0;
-  if (t_end < t_begin) t_end = t_begin;
+  if (t_end < t_begin || r0 >= lq) t_end = t_begin;  // (no used row here: zeros only)
 
   if (a.tile_counts != nullptr && tid == 0) {
     // in units of the reported tile width (a multiple of BN)
@@ -1718,13 +1733,18 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
   // ---- epilogue: O / l staged through LDS (the K/V buffers are free after
   // the loop's last barrier), STAGE_ROWS rows of a 32-row query block at a
   // time, so that every output row is written as contiguous 16-byte stores.
-  if (!wave_active) return;
+  if (w0 >= span_q) return;
   // each wave stages its rows in one of the four (now free) buffers
   lds_char* ostage = wave == 0 ? (lds_char*)kbuf_0 : wave == 1 ? (lds_char*)kbuf_1
                    : wave == 2 ? (lds_char*)vbuf_0 : (lds_char*)vbuf_1;
+  // this lane's rows, recomputed here rather than kept through the loop
+  int lane_e = (int)threadIdx.x & 31;
+  asm volatile("" : "+v"(lane_e));
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
-    const float l_tot = l_run[n] + __shfl_xor(l_run[n], 32);
+    const int row_e = w0 + 32 * n + lane_e;
+    const float l_all = l_run[n] + __shfl_xor(l_run[n], 32);
+    const float l_tot = row_e < lq ? l_all : 0.0f;  // rows of the span past lq: 0
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
     for (int pass = 0; pass < 32 / STAGE_ROWS; ++pass) {
@@ -1757,7 +1777,7 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
       const int qb = w0 + 32 * n + pass * STAGE_ROWS;  // first row of this pass
       // The pass's rows through one buffer window: rows past the sequence
       // end fall outside it and their stores are dropped.
-      const int o_rows = min(max(lq - qb, 0), STAGE_ROWS);
+      const int o_rows = min(max(span_q - qb, 0), STAGE_ROWS);
       const int64_t o_st_b = a.o_st * (int64_t)sizeof(OutT);
       const char* obase = uniform_ptr(reinterpret_cast<const char*>(a.out) +
                                       ((int64_t)(cq0 + qb) * a.o_st + (int64_t)head * a.o_sh) *
@@ -1776,9 +1796,9 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
       }
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     }
-    if (a.lse != nullptr && hf == 0 && row_ok[n]) {
+    if (a.lse != nullptr && hf == 0 && row_e < span_q) {
       const float m_use = (m_run[n] == kNegInf) ? 0.0f : m_run[n];
-      a.lse[(int64_t)head * a.total_q + cq0 + my_row[n]] =
+      a.lse[(int64_t)head * a.total_q + cq0 + row_e] =
           l_tot > 0.0f ? (m_use + fast_log2(l_tot)) * kLn2 : kNegInf;
     }
   }

@@ -262,6 +262,9 @@ int check_fwd_params(const mi_attn_fwd_params* p, bool* empty) {
   }
   if (p->bias_pure != nullptr && !has_bias)
     return fail(MI_ATTN_ERR_INVALID_ARG, "bias_pure is given without a bias or a mask");
+  if ((reinterpret_cast<uintptr_t>(p->seqused_q) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(p->seqused_kv) & 3u) != 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "seqused_q / seqused_kv must be 4-byte aligned");
 
   return MI_ATTN_OK;
 }
@@ -298,6 +301,8 @@ int plan_decode(const mi_attn_fwd_params* p, int64_t max_seqlen_kv, int32_t num_
   if (p->alibi_slopes != nullptr)
     return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode takes no ALiBi slopes");
   if (p->mask != nullptr) return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode takes no mask");
+  if (p->seqused_q != nullptr)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "split-KV decode uses every query row (no seqused_q)");
   if (num_splits < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "num_splits must be >= 0 (0 = auto)");
   if (max_seqlen_kv < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "max_seqlen_kv must be >= 0");
   const int64_t group = p->hq / p->hkv;
@@ -335,6 +340,7 @@ int launch_decode(const mi_attn_fwd_params* p, const DecodePlan& plan, void* ws,
   mi_attn::DecodeArgs a{};
   a.q = p->q; a.k = p->k; a.v = p->v;
   a.cu_q = p->cu_seqlens_q; a.cu_kv = p->cu_seqlens_kv;
+  a.seqused_kv = p->seqused_kv;
   a.ws_o = reinterpret_cast<float*>(ws);
   a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + plan.ws_o_bytes);
   a.out = p->out; a.lse = p->lse;
@@ -450,6 +456,8 @@ int mi_attn_varlen_fwd(const mi_attn_fwd_params* p_in, void* stream) {
   a.mask = p->mask;
   a.bias_ranges = has_bias ? p->bias_ranges : nullptr;
   a.bias_pure = has_bias ? p->bias_pure : nullptr;
+  a.seqused_q = p->seqused_q;
+  a.seqused_kv = p->seqused_kv;
   a.q_rope = p->q_rope;
   a.k_rope = p->k_rope;
   a.qr_st = p->q_rope_stride_tok;
@@ -707,6 +715,34 @@ int mi_attn_padding_to_varlen(const uint8_t* mask, int64_t batch, int64_t seqlen
   a.batch = (int32_t)batch;
   a.seqlen = (int32_t)seqlen;
   hipError_t e = mi_attn::launch_padding_ranks(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return MI_ATTN_OK;
+}
+
+int mi_attn_padding_lengths(const uint8_t* mask, int64_t batch, int64_t seqlen,
+                            int64_t mask_stride_batch, int32_t* lengths, int32_t* spans,
+                            int32_t* stats, void* stream) {
+  g_last_error.clear();
+  if (batch < 0 || seqlen < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "negative size");
+  if (batch >= INT32_MAX || seqlen > INT32_MAX || batch * seqlen > INT32_MAX)
+    return fail(MI_ATTN_ERR_UNSUPPORTED, "batch * seqlen must fit in int32 (spans)");
+  if (spans == nullptr || (batch > 0 && lengths == nullptr))
+    return fail(MI_ATTN_ERR_INVALID_ARG, "lengths and spans are required");
+  if (batch * seqlen > 0 && mask == nullptr) return fail(MI_ATTN_ERR_INVALID_ARG, "mask is required");
+  if ((reinterpret_cast<uintptr_t>(lengths) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(spans) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(stats) & 3u) != 0)
+    return fail(MI_ATTN_ERR_INVALID_ARG, "lengths, spans and stats must be 4-byte aligned");
+  if (mask_stride_batch < 0) return fail(MI_ATTN_ERR_INVALID_ARG, "negative mask stride");
+  mi_attn::PadLengthArgs a{};
+  a.mask = mask;
+  a.mask_st = mask_stride_batch;
+  a.lengths = lengths;
+  a.spans = spans;
+  a.stats = stats;
+  a.batch = (int32_t)batch;
+  a.seqlen = (int32_t)seqlen;
+  hipError_t e = mi_attn::launch_padding_lengths(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MI_ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return MI_ATTN_OK;
 }

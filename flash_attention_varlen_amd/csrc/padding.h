@@ -33,7 +33,20 @@ struct PackArgs {
   int32_t unpack;     // 0: padded -> packed; 1: packed -> padded, zeros at padding
 };
 
+// Right-padding check: every row's valid-token count, whether each row's
+// valid tokens are its first ones, and the spans of the padded rows.
+struct PadLengthArgs {
+  const uint8_t* mask;  // [batch, seqlen] bytes, nonzero = valid token
+  int64_t mask_st;      // bytes between batch rows
+  int32_t* lengths;     // [batch]: valid tokens of each row
+  int32_t* spans;       // [batch + 1]: b * seqlen (first a per-row flag, see the kernels)
+  int32_t* stats;       // optional [2]: all rows right-padded (1 / 0), longest row
+  int32_t batch;
+  int32_t seqlen;
+};
+
 hipError_t launch_padding_ranks(const PadRankArgs& a, hipStream_t stream);
+hipError_t launch_padding_lengths(const PadLengthArgs& a, hipStream_t stream);
 hipError_t launch_pack_tokens(const PackArgs& a, hipStream_t stream);
 
 }  // namespace mi_attn

@@ -9,6 +9,9 @@
 // Three kernels, all bound by HBM bandwidth: ranks (one workgroup per batch
 // row: ballot prefix counts over 256-token chunks), a one-workgroup scan of
 // the row counts into cu_seqlens, and a 16-byte-per-lane gather / scatter.
+// A right-padded batch (every row's valid tokens first) needs no packing at
+// all: two more kernels find each row's count and whether the batch is
+// right-padded, for the forward's seqused form.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -94,6 +97,88 @@ __global__ __launch_bounds__(1024) void padding_scan_kernel(const PadRankArgs a)
   }
 }
 
+// Row b's valid-token count and whether its valid tokens are its first ones
+// (the last valid position + 1 equals the count); the flag goes to
+// spans[b + 1] until padding_lengths_stats_kernel overwrites it.
+__global__ __launch_bounds__(256) void padding_lengths_kernel(const PadLengthArgs a) {
+  __shared__ int wave_count[4];
+  __shared__ int wave_end[4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int b = blockIdx.x;
+  const uint8_t* m = a.mask + (int64_t)b * a.mask_st;
+  int count = 0, end = 0;  // this thread's share: valid tokens, last valid position + 1
+  for (int n = tid; n < a.seqlen; n += 256)
+    if (m[n] != 0) {
+      ++count;
+      end = n + 1;
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    count += __shfl_xor(count, o);
+    end = max(end, __shfl_xor(end, o));
+  }
+  if (lane == 0) {
+    wave_count[wave] = count;
+    wave_end[wave] = end;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int c = 0, e = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      c += wave_count[w];
+      e = max(e, wave_end[w]);
+    }
+    a.lengths[b] = c;
+    a.spans[b + 1] = e == c ? 1 : 0;
+  }
+}
+
+// stats = (every row right-padded, longest row); spans[b] = b * seqlen.  One
+// workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void padding_lengths_stats_kernel(const PadLengthArgs a) {
+  __shared__ int wave_all[16];
+  __shared__ int wave_max[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int all = 1, longest = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 1024) {
+    const int b = b0 + tid;
+    int ok = 1, len = 0;
+    if (b < a.batch) {
+      ok = a.spans[b + 1];
+      len = a.lengths[b];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      ok = min(ok, __shfl_xor(ok, o));
+      len = max(len, __shfl_xor(len, o));
+    }
+    if (lane == 0) {
+      wave_all[wave] = ok;
+      wave_max[wave] = len;
+    }
+    __syncthreads();
+    for (int w = 0; w < 16; ++w) {
+      all = min(all, wave_all[w]);
+      longest = max(longest, wave_max[w]);
+    }
+    __syncthreads();  // the flags are read before they are overwritten, and the
+                      // shared slots before the next round rewrites them
+    if (b < a.batch) a.spans[b + 1] = (b + 1) * a.seqlen;
+  }
+  if (tid == 0) {
+    a.spans[0] = 0;
+    if (a.stats) {
+      a.stats[0] = all;
+      a.stats[1] = longest;
+    }
+  }
+}
+
 // One 16-byte chunk per lane: a workgroup takes tok_per_wg tokens (or one
 // token whose chunks it loops over).
 __global__ __launch_bounds__(256) void pack_tokens_kernel(const PackArgs a) {
@@ -130,6 +215,14 @@ hipError_t launch_padding_ranks(const PadRankArgs& a, hipStream_t stream) {
   (void)hipGetLastError();
   if (a.batch > 0) hipLaunchKernelGGL(padding_ranks_kernel, dim3((unsigned)a.batch), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(padding_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_padding_lengths(const PadLengthArgs& a, hipStream_t stream) {
+  (void)hipGetLastError();
+  if (a.batch > 0)
+    hipLaunchKernelGGL(padding_lengths_kernel, dim3((unsigned)a.batch), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(padding_lengths_stats_kernel, dim3(1), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 

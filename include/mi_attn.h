@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_VERSION 160 /* 1.6.0 */
+#define MI_ATTN_VERSION 170 /* 1.7.0 */
 
 /* Return codes.  On any error nothing is launched and out / lse are untouched. */
 enum {
@@ -191,6 +191,20 @@ typedef struct mi_attn_fwd_params {
    * instead, with results equal to those of the bias.  Like bias_ranges it
    * assumes bias_cols >= every sequence's key length. */
   const uint8_t* bias_pure;
+  /* Added in version 1.7 (NULL for older callers): optional int32
+   * [num_seqs] device arrays.  Sequence s then uses only the first
+   * seqused_q[s] query rows of its span cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1
+   * and the first seqused_kv[s] keys of its key span (values clamped to
+   * [0, span]): Lq and Lk above are these counts, the causal diagonal is
+   * end-aligned on them, and keys past seqused_kv are never read.  Unused
+   * query rows of a span get out = 0 and lse = -inf, as rows that see no
+   * key do (mi_attn_varlen_fwd).  This lets
+   * a right-padded batch (spans of one padded length, the valid tokens
+   * first) run without packing, and a decode call read a key cache that is
+   * allocated longer than it is filled.  mi_attn_varlen_decode reads
+   * seqused_kv and refuses seqused_q.  4-byte aligned. */
+  const int32_t* seqused_q;
+  const int32_t* seqused_kv;
 } mi_attn_fwd_params;
 
 /*
@@ -248,6 +262,21 @@ int mi_attn_bias_key_ranges(const mi_attn_fwd_params* p, int32_t* ranges, void* 
 int mi_attn_padding_to_varlen(const uint8_t* mask, int64_t batch, int64_t seqlen,
                               int64_t mask_stride_batch, int32_t* ranks, int32_t* cu_seqlens,
                               int32_t* stats, void* stream);
+
+/*
+ * Right-padding check (added in version 1.7): for the same mask, lengths
+ * (int32 [batch]) gets each row's valid-token count, spans (int32
+ * [batch + 1]) gets b * seqlen, and, if stats is not NULL, stats[0] = 1 when
+ * every row's valid tokens are its first lengths[b] tokens (a right-padded
+ * batch) and 0 otherwise, stats[1] = the longest row.  For a right-padded
+ * batch a forward call can take the padded tensors as they are, with
+ * cu_seqlens = spans and seqused_q / seqused_kv = lengths (mi_attn_fwd_params),
+ * instead of packing them.  Same buffer and size rules as
+ * mi_attn_padding_to_varlen; asynchronous on `stream`.
+ */
+int mi_attn_padding_lengths(const uint8_t* mask, int64_t batch, int64_t seqlen,
+                            int64_t mask_stride_batch, int32_t* lengths, int32_t* spans,
+                            int32_t* stats, void* stream);
 
 /*
  * Gather (mi_attn_pack_tokens) the valid tokens of a padded view

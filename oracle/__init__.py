@@ -10,10 +10,11 @@ from .ref_attention import (attention_rows, bias_head, finish_rows, kv_head_of, 
                             softmax_rows, varlen_attention, visible, visible_counts)
 from .ref_backward import varlen_attention_backward
 from .ref_masks import alibi_bias, bias_key_ranges, bias_rows_are_intervals
-from .ref_padding import masked_attention, pack_tokens, padding_to_varlen, unpack_tokens
+from .ref_padding import (masked_attention, pack_tokens, padding_lengths, padding_to_varlen,
+                          unpack_tokens, used_prefixes)
 
 __all__ = ["alibi_bias", "attention_rows", "bias_head", "bias_key_ranges", "bias_rows_are_intervals",
            "finish_rows", "kv_head_of", "logits",
-           "masked_attention", "pack_tokens", "padding_to_varlen", "softmax_rows",
-           "unpack_tokens", "varlen_attention", "varlen_attention_backward", "visible",
+           "masked_attention", "pack_tokens", "padding_lengths", "padding_to_varlen", "softmax_rows",
+           "unpack_tokens", "used_prefixes", "varlen_attention", "varlen_attention_backward", "visible",
            "visible_counts"]

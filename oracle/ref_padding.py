@@ -13,6 +13,13 @@ than masked.  Written out:
   tokens (-1 at padding), the cumulative valid counts and (total, longest).
 * ``pack_tokens`` / ``unpack_tokens``: the gather into packed rows and the
   scatter back, zeros at padding.
+* ``padding_lengths``: each row's valid count and whether the batch is
+  right-padded (every row's valid tokens come first), the case in which the
+  padded tensors can be attended in place: a sequence is then its row's
+  first ``count`` tokens.
+* ``used_prefixes``: the packed varlen problem that spans with a used prefix
+  each (``seqused``) stand for: sequence s is the first ``used[s]`` rows of
+  its span.
 * ``masked_attention``: the dense definition the packed path must reproduce,
   scaled dot-product attention over ``[B, H, N, D]`` in which a key takes
   part only where the mask marks it valid (and, with ``causal``, only keys at
@@ -41,6 +48,36 @@ def padding_to_varlen(mask):
     cu = np.zeros(b + 1, dtype=np.int64)
     cu[1:] = np.cumsum(counts)
     return ranks, cu, (int(cu[-1]), int(counts.max(initial=0)))
+
+
+def padding_lengths(mask):
+    """``mask`` bool ``[B, N]`` -> (counts int64 ``[B]``, spans int64 ``[B+1]``
+    = ``b * N``, right_padded, longest): right_padded is True when every row's
+    valid tokens are exactly its first ``counts[b]`` positions."""
+    mask = np.asarray(mask, dtype=bool)
+    b, n = mask.shape
+    counts = mask.sum(axis=1).astype(np.int64)
+    right = all(bool(mask[r, :counts[r]].all()) for r in range(b))
+    spans = np.arange(b + 1, dtype=np.int64) * n
+    return counts, spans, right, int(counts.max(initial=0))
+
+
+def used_prefixes(x, cu, used):
+    """Rows ``[total, ...]`` grouped in spans ``cu`` -> (the first ``used[s]``
+    rows of every span, packed, and their cumulative counts).  ``used`` is
+    clamped to ``[0, span]``."""
+    x = np.asarray(x)
+    cu = np.asarray(cu, dtype=np.int64)
+    parts, counts = [], []
+    for s in range(len(cu) - 1):
+        span = int(cu[s + 1] - cu[s])
+        u = min(max(int(used[s]), 0), span)
+        parts.append(x[int(cu[s]):int(cu[s]) + u])
+        counts.append(u)
+    out_cu = np.zeros(len(counts) + 1, dtype=np.int64)
+    out_cu[1:] = np.cumsum(counts)
+    packed = np.concatenate(parts) if parts else x[:0]
+    return packed, out_cu
 
 
 def pack_tokens(padded, mask):

@@ -604,6 +604,50 @@ def pin_packed_matches_masked():
         _close(dense, ref, 1e-12)
 
 
+def pin_padding_lengths_hand_worked():
+    """Counts, spans and the right-padding test by hand: a row whose valid
+    tokens come first is right-padded; one with a hole or valid tokens after
+    padding is not; empty and full rows are."""
+    cases = [
+        ([[1, 1, 1, 0, 0], [1, 1, 1, 1, 1], [0, 0, 0, 0, 0]], [3, 5, 0], True, 5),
+        ([[1, 1, 0, 0, 0], [1, 0, 1, 0, 0]], [2, 2], False, 2),
+        ([[0, 1, 1, 0, 0]], [2], False, 2),
+        ([[1, 1, 1, 1, 0], [0, 0, 0, 0, 1]], [4, 1], False, 4),
+    ]
+    for mask, counts, right, longest in cases:
+        m = np.array(mask, dtype=bool)
+        c, spans, r, lg = oracle.padding_lengths(m)
+        assert list(c) == counts and r == right and lg == longest, (mask, c, r, lg)
+        assert list(spans) == [5 * b for b in range(len(mask) + 1)]
+
+
+def pin_used_prefixes_match_key_padding():
+    """Spans whose first used rows are the sequences (a right-padded batch
+    attended in place) give the dense key-padding result: the used-prefix
+    problem, packed, run through the varlen definition and put back at the
+    spans' first rows (0 elsewhere) equals masked attention with the
+    right-padding mask."""
+    rng = np.random.default_rng(322)
+    bsz, n, hq, hkv, d = 3, 9, 4, 2, 8
+    used = np.array([9, 4, -2])  # a negative count means an empty sequence
+    mask = np.arange(n)[None, :] < used[:, None]
+    q = rng.standard_normal((bsz, hq, n, d))
+    k = rng.standard_normal((bsz, hkv, n, d))
+    v = rng.standard_normal((bsz, hkv, n, d))
+    spans = np.arange(bsz + 1) * n
+    for causal in (False, True):
+        tok = [x.transpose(0, 2, 1, 3).reshape(bsz * n, x.shape[1], d) for x in (q, k, v)]
+        pq, cu = oracle.used_prefixes(tok[0], spans, used)
+        pk, _ = oracle.used_prefixes(tok[1], spans, used)
+        pv, _ = oracle.used_prefixes(tok[2], spans, used)
+        out, _ = oracle.varlen_attention(pq, pk, pv, cu, cu, 1.0 / math.sqrt(d), causal, 0, None)
+        dense = np.zeros((bsz, n, hq, d))
+        for b in range(bsz):
+            dense[b, :cu[b + 1] - cu[b]] = out[cu[b]:cu[b + 1]]
+        ref = oracle.masked_attention(q, k, v, mask, 1.0 / math.sqrt(d), causal)
+        _close(dense.transpose(0, 2, 1, 3), ref, 1e-12)
+
+
 # ---------------------------------------------------------------- ALiBi
 def pin_alibi_hand_worked():
     """Two sequences (3 queries / 3 keys, 1 query / 4 keys) and slopes 0.5,
@@ -655,4 +699,5 @@ ALL_PINS = [pin_brute_force_tiny, pin_sdpa_special_case, pin_rows_sum_to_one,
             pin_backward_sdpa_special_case, pin_backward_closed_forms, pin_padding_hand_worked,
             pin_masked_attention_sdpa, pin_packed_matches_masked, pin_alibi_hand_worked,
             pin_alibi_causal_is_a_linear_key_bias, pin_interval_rows_hand_worked,
-            pin_interval_rows_attend_their_range]
+            pin_interval_rows_attend_their_range, pin_padding_lengths_hand_worked,
+            pin_used_prefixes_match_key_padding]

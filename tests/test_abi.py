@@ -24,7 +24,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == ["mi_attn_bias_key_ranges", "mi_attn_decode_workspace_size", "mi_attn_last_error",
-                     "mi_attn_pack_tokens", "mi_attn_padding_to_varlen", "mi_attn_tile_shape",
+                     "mi_attn_pack_tokens", "mi_attn_padding_lengths", "mi_attn_padding_to_varlen",
+                     "mi_attn_tile_shape",
                      "mi_attn_unpack_tokens", "mi_attn_varlen_bwd", "mi_attn_varlen_decode",
                      "mi_attn_varlen_decode_noalloc", "mi_attn_varlen_fwd", "mi_attn_version"]
     lib = fav.load_library()
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_tile_shape():
-    assert fav.mi_attn_version() == 160
+    assert fav.mi_attn_version() == 170
     for dt in (fav.BF16, fav.F16):
         for dqk, dv in ((64, 64), (96, 96), (128, 128), (192, 128), (256, 256)):
             bm, bn = fav.mi_attn_tile_shape(dt, dqk, dv)
@@ -159,6 +160,8 @@ REFUSALS = {
     "pure_without_bias": (dict(bias_pure=1 << 20), fav.ERR_INVALID_ARG),
     "pure_without_ranges": (dict(bias_pure=1 << 20, bias=1 << 20, bias_heads=1, bias_cols=64,
                                  bias_stride_tok=64, bias_stride_head=0), fav.ERR_INVALID_ARG),
+    "seqused_q_misaligned": (dict(seqused_q=(1 << 20) + 2), fav.ERR_INVALID_ARG),
+    "seqused_kv_misaligned": (dict(seqused_kv=(1 << 20) + 1), fav.ERR_INVALID_ARG),
     # with split operands q / k hold 128 dims; without them a 128-wide stride is short of 192
     "latent_short_q_stride": (dict(d_qk=192, q_stride_tok=128, q_stride_head=0, hq=2, hkv=2,
                                    out_stride_tok=2 * 128), fav.ERR_UNSUPPORTED),
@@ -285,6 +288,7 @@ DECODE_REFUSALS = {
     "bias": (dict(bias=1 << 20, bias_heads=1, bias_cols=64, bias_stride_tok=64, bias_stride_head=64),
              1 << 20, fav.ERR_UNSUPPORTED),
     "too_many_rows": (dict(max_seqlen_q=17), 1 << 20, fav.ERR_UNSUPPORTED),  # 4 heads x 17 > 64
+    "seqused_q": (dict(seqused_q=1 << 20), 1 << 20, fav.ERR_UNSUPPORTED),
     "misaligned_workspace": (dict(max_seqlen_q=1), (1 << 20) + 8, fav.ERR_INVALID_ARG),
     "null_workspace": (dict(max_seqlen_q=1), 0, fav.ERR_INVALID_ARG),
 }
@@ -394,4 +398,28 @@ def test_padding_to_varlen_refuses(name):
     with pytest.raises(fav.MiAttnError) as ei:
         fav.mi_attn_padding_to_varlen(args["mask"], args["batch"], args["seqlen"], args["stride"],
                                       args["ranks"], args["cu"], args["stats"], 0)
+    assert ei.value.code == code, fav.mi_attn_last_error()
+
+
+LENGTH_REFUSALS = {
+    "negative": (dict(batch=-1), fav.ERR_INVALID_ARG),
+    "too_many_tokens": (dict(batch=1 << 16, seqlen=1 << 16), fav.ERR_UNSUPPORTED),
+    "null_spans": (dict(spans=0), fav.ERR_INVALID_ARG),
+    "null_lengths": (dict(lengths=0), fav.ERR_INVALID_ARG),
+    "null_mask": (dict(mask=0), fav.ERR_INVALID_ARG),
+    "misaligned_lengths": (dict(lengths=(1 << 20) + 2), fav.ERR_INVALID_ARG),
+    "misaligned_stats": (dict(stats=(1 << 20) + 1), fav.ERR_INVALID_ARG),
+    "negative_stride": (dict(stride=-1), fav.ERR_INVALID_ARG),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LENGTH_REFUSALS))
+def test_padding_lengths_refuses(name):
+    args = dict(mask=1 << 20, batch=2, seqlen=10, stride=10, lengths=1 << 20, spans=1 << 20,
+                stats=0)
+    changes, code = LENGTH_REFUSALS[name]
+    args.update(changes)
+    with pytest.raises(fav.MiAttnError) as ei:
+        fav.mi_attn_padding_lengths(args["mask"], args["batch"], args["seqlen"], args["stride"],
+                                    args["lengths"], args["spans"], args["stats"], 0)
     assert ei.value.code == code, fav.mi_attn_last_error()

@@ -83,6 +83,13 @@ PADDING_MUTATIONS = {
                              "vis = np.ones((n, n), dtype=bool)"),
     "pad_causal_flipped": ("vis = vis & (j <= i)", "vis = vis & (j >= i)"),
     "pad_kv_head_modulo": ("g = h // (hq // hkv)", "g = h % hkv"),
+    "pad_right_any_valid": ("right = all(bool(mask[r, :counts[r]].all()) for r in range(b))",
+                            "right = all(bool(mask[r, :counts[r]].any() or counts[r] == 0) for r in range(b))"),
+    "pad_spans_unscaled": ("spans = np.arange(b + 1, dtype=np.int64) * n",
+                           "spans = np.arange(b + 1, dtype=np.int64)"),
+    "used_not_clamped_low": ("u = min(max(int(used[s]), 0), span)", "u = min(int(used[s]), span)"),
+    "used_from_span_end": ("parts.append(x[int(cu[s]):int(cu[s]) + u])",
+                           "parts.append(x[int(cu[s + 1]) - u:int(cu[s + 1])])"),
 }
 
 SOURCES = {"attention": inspect.getsource(ref_attention), "masks": inspect.getsource(ref_masks),
