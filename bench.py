@@ -205,8 +205,9 @@ def main():
                     help="override the window width of a sliding-window workload (cost vs W)")
     ap.add_argument("--sdpa-keypad", action="store_true",
                     help="time the key-padding front end: the workload's sequences as a padded "
-                         "[B, H, N, D] batch with a bool key-padding mask through sdpa() (mask "
-                         "scan, packing, the forward, unpacking), self-attention without a bias")
+                         "[B, H, N, D] batch with a bool key-padding mask through sdpa() (the "
+                         "right-padding check, then the forward in place on the padded "
+                         "storage), self-attention without a bias")
     ap.add_argument("--no-interval-rows", action="store_true",
                     help="with a bias: compute its key ranges only, so that the forward reads "
                          "the bias of every row (no interval flags)")
@@ -493,8 +494,8 @@ def main():
             "algorithmic_bytes": algorithmic_bytes(w, out_bytes),
             "kernel": ("decode_kernel + decode_merge_kernel" if is_decode else
                        "delta_kernel + dkdv_kernel + dq_kernel" if args.backward else
-                       "sdpa key-padding front end (whole step: mask scan, packs, "
-                       "attn_fwd16p_kernel, unpack)" if args.sdpa_keypad else
+                       "sdpa key-padding front end (whole step: padding_lengths kernels, "
+                       "attn_fwd16p_kernel in place)" if args.sdpa_keypad else
                        "attn_fwd_kernel" if w.dtype == "f32" else "attn_fwd16p_kernel"),
             "kernel_ms": round(kernel_ms, 4),
         },
