@@ -1518,6 +1518,12 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
     vf[0] = vread(0);
     if (NVF > 1) vf[1] = vread(1);
     __builtin_amdgcn_sched_barrier(0);
+    // The two waves of a SIMD come from different workgroups and drift
+    // apart.  A wave inside its stream (MFMAs with VALU between them) takes
+    // issue priority over one in the VALU-only parts around it (low-half
+    // pass, waits, rescale, the next step's set-up): the matrix pipe idles
+    // less (+0.5 to 1.7% across the workloads).
+    __builtin_amdgcn_s_setprio(1);
     static_for<0, Plan::kOps>([&](auto qc) __attribute__((device)) {
       constexpr int op = Plan::op(decltype(qc)::value);
       constexpr int ix = Plan::index(decltype(qc)::value);
@@ -1598,6 +1604,8 @@ __global__ __launch_bounds__(kThreads, (WaveBlocks<DQK, DV, BIAS>::OCC)) void at
       }
       __builtin_amdgcn_sched_barrier(0);
     });
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     // Low halves of P.  The stream multiplied V by P rounded to 16 bits,
     // which errs by up to 2^-9 (bf16) or 2^-12 (fp16) of each p.  Relative
     // to the row's sum l those errors are at most about sqrt(p_max / l) of
