@@ -299,8 +299,8 @@ def main():
         if need > ws.numel():
             ws = torch.empty(need, dtype=torch.uint8, device=dev)
     if args.backward:
-        if bias is not None or w.dtype == "f32" or w.d_qk != w.d_v or w.d_qk not in (64, 128):
-            print("the backward takes bf16/fp16, head dims 64 or 128, no bias", file=sys.stderr)
+        if bias is not None or w.dtype == "f32" or w.d_qk != w.d_v or w.d_qk not in (64, 96, 128):
+            print("the backward takes bf16/fp16, head dims 64, 96 or 128, no bias", file=sys.stderr)
             sys.exit(2)
         out_f, lse_f = fav.varlen_attention(q, k, v, cq, ck, w.max_seqlen_q, scale=w.softmax_scale,
                                             causal=w.causal, window=w.window, return_lse=True)

@@ -231,7 +231,7 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
     ``torch.float32`` is also accepted); ``lse`` is ``[Hq, Tq]`` fp32
     (natural log).  If q, k or v require grad (and grad mode is on), the call
     is differentiable: ``out``'s gradient flows back through
-    ``mi_attn_varlen_bwd`` (bf16 / fp16, head dims 64 / 128;
+    ``mi_attn_varlen_bwd`` (bf16 / fp16, head dims 64 / 96 / 128;
     ``max_seqlen_kv`` is read from ``cu_seqlens_kv`` when not given; a bias
     enters as a constant, and one that requires grad is refused).
 
@@ -514,7 +514,7 @@ def varlen_attention_backward(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_
                               grad_dtype=None, attn_bias=None, stream=None, alibi_slopes=None):
     """Gradients ``(dq, dk, dv)`` of the forward from its inputs, its output
     ``out`` and ``lse`` and the output gradient ``dout`` (bf16 / fp16,
-    head dims 64 or 128; ``attn_bias``, the forward's additive bias, enters as
+    head dims 64, 96 or 128; ``attn_bias``, the forward's additive bias, enters as
     a constant).  Outputs (and the fp32 [Hq, Tq] delta workspace) are
     allocated on ``stream`` unless given."""
     import torch

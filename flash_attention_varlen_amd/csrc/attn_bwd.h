@@ -44,7 +44,9 @@ struct BwdArgs {
 
 // The backward instances, one per (element type, head dim), compiled in
 // their own translation units (attn_bwd_inst.hip).
-#define MI_ATTN_BWD_INSTANCES(X) X(bf16, __bf16, 64) X(bf16, __bf16, 128) X(f16, _Float16, 64) X(f16, _Float16, 128)
+#define MI_ATTN_BWD_INSTANCES(X)                                                     \
+  X(bf16, __bf16, 64) X(bf16, __bf16, 96) X(bf16, __bf16, 128) X(f16, _Float16, 64) \
+  X(f16, _Float16, 96) X(f16, _Float16, 128)
 #define MI_ATTN_BWD_INSTANCE_NAME(tag, d) launch_bwd_##tag##_##d
 #define MI_ATTN_BWD_DECLARE(tag, T, d)                                                         \
   hipError_t MI_ATTN_BWD_INSTANCE_NAME(tag, d)(const BwdArgs& a, bool grad_f32, bool bias,     \

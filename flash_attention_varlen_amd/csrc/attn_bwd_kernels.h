@@ -46,11 +46,15 @@ template <typename OutT, int DV>
 __global__ __launch_bounds__(256) void delta_kernel(const BwdArgs a) {
   // out and dout in the input type (the forward's default output type)
   constexpr int EPL = 16 / (int)sizeof(OutT);  // elements per 16-byte load
-  constexpr int LPR = DV / EPL;                // lanes per (row, head)
+  constexpr int LPR_D = DV / EPL;              // lanes holding a row's elements
+  // lanes per (row, head): a power of two for the reduction (the 96-wide
+  // head's 12 loads use 16 lanes; the other 4 add 0)
+  constexpr int LPR = LPR_D <= 8 ? 8 : LPR_D <= 16 ? 16 : 32;
+  static_assert(LPR >= LPR_D && 64 % LPR == 0, "lanes per row");
   const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
   const int sub = threadIdx.x % LPR;
   const int64_t total = a.total_q * a.hq;
-  const bool ok = item < total;
+  const bool ok = item < total && sub < LPR_D;
   const int64_t t = ok ? item / a.hq : 0;
   const int h = ok ? (int)(item % a.hq) : 0;
   float acc = 0.0f;
@@ -91,7 +95,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
   constexpr int BQ = 64;               // query rows per step (two 32-row blocks)
   constexpr int KS = D / 16;           // MFMA k-steps over the head dim
   constexpr int NDB = D / 32;          // 32-wide d blocks of dK^T / dV^T
-  constexpr int TILE = BQ * D * 2;     // bytes of one Q or dO tile
+  // LDS rows are DL wide: the 96-wide head is laid out like the 128-wide one
+  // (its 4 pad chunks are copied, beyond the row, and never read), so that
+  // the power-of-two swizzle holds
+  constexpr int DL = lds_dim(D);
+  constexpr int TILE = BQ * DL * 2;    // bytes of one Q or dO tile
   constexpr int LOADS = TILE / (kThreads * 16);
   using E = Elem<T>;
 
@@ -165,8 +173,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
     for (int e = 0; e < 16; ++e) dk[i][e] = dv[i][e] = 0.0f;
 
   uint32_t qoff[LOADS], goff[LOADS];
-  tile_offsets<D, LOADS>(qoff, a.q_st * 2, tid);
-  tile_offsets<D, LOADS>(goff, a.do_st * 2, tid);
+  tile_offsets<DL, LOADS>(qoff, a.q_st * 2, tid);
+  tile_offsets<DL, LOADS>(goff, a.do_st * 2, tid);
   const float c_scale = a.scale_log2;
 
   // Stage iteration `it` (query head h = g * group + it % group, tile it / group):
@@ -265,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
       // S = Q K^T, dP = dO V^T: MFMA i takes a Q (even i) or dO (odd i)
       // fragment of k-step i / 2
       auto rd_s = [&](int i) __attribute__((device)) -> u32x4_t {
-        return row_frag<D>((i & 1) ? gt : qt, 32 * qb + l32, i >> 1, hf);
+        return row_frag<DL>((i & 1) ? gt : qt, 32 * qb + l32, i >> 1, hf);
       };
       u32x4_t fr[AH + 1];
 #pragma unroll
@@ -294,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const BwdArgs a) {
     constexpr int NT = 8 * NDB;
     auto rd_t = [&](int i) __attribute__((device)) -> u32x4_t {
       const int qb = i / (4 * NDB), kk = (i / (2 * NDB)) % 2, db = (i / 2) % NDB;
-      return tr_frag<D>((i & 1) ? qt : gt, 2 * qb + kk, db, lane);
+      return tr_frag<DL>((i & 1) ? qt : gt, 2 * qb + kk, db, lane);
     };
     u32x4_t tf[AH + 1];
 #pragma unroll
@@ -360,7 +368,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdArgs a) {
   constexpr int BN = 32;               // keys per tile
   constexpr int KS = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int TILE = BN * D * 2;
+  constexpr int DL = lds_dim(D);  // LDS row width (as in dkdv_kernel)
+  constexpr int TILE = BN * DL * 2;
   constexpr int LOADS = TILE / (kThreads * 16);
   using E = Elem<T>;
 
@@ -445,8 +454,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdArgs a) {
     for (int e = 0; e < 16; ++e) dq[i][e] = 0.0f;
 
   uint32_t koff[LOADS], voff[LOADS];
-  tile_offsets<D, LOADS>(koff, a.k_st * 2, tid);
-  tile_offsets<D, LOADS>(voff, a.v_st * 2, tid);
+  tile_offsets<DL, LOADS>(koff, a.k_st * 2, tid);
+  tile_offsets<DL, LOADS>(voff, a.v_st * 2, tid);
   const char* kbase = reinterpret_cast<const char*>(a.k) + ((int64_t)ck0 * a.k_st + (int64_t)g * a.k_sh) * 2;
   const char* vbase = reinterpret_cast<const char*>(a.v) + ((int64_t)ck0 * a.v_st + (int64_t)g * a.v_sh) * 2;
   const float c_scale = a.scale_log2;
@@ -471,8 +480,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdArgs a) {
     for (int e = 0; e < 16; ++e) sc[e] = dp[e] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      sc = E::mma(row_frag<D>(kt, l32, ks, hf), qf[ks], sc);
-      dp = E::mma(row_frag<D>(vt, l32, ks, hf), gf[ks], dp);
+      sc = E::mma(row_frag<DL>(kt, l32, ks, hf), qf[ks], sc);
+      dp = E::mma(row_frag<DL>(vt, l32, ks, hf), gf[ks], dp);
     }
     // entry e: key kb + 8 (e/4) + 4 hf + e%4, query my_row
     const bool need_mask = (kb + BN > lk) || (causal && kb + BN - 1 > w0 + off) ||
@@ -510,8 +519,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const BwdArgs a) {
     const u32x4_t s0 = pack_b<T>(dp, 0), s1 = pack_b<T>(dp, 1);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      dq[db] = E::mma(tr_frag<D>(kt, 0, db, lane), s0, dq[db]);
-      dq[db] = E::mma(tr_frag<D>(kt, 1, db, lane), s1, dq[db]);
+      dq[db] = E::mma(tr_frag<DL>(kt, 0, db, lane), s0, dq[db]);
+      dq[db] = E::mma(tr_frag<DL>(kt, 1, db, lane), s1, dq[db]);
     }
   };
 
@@ -553,7 +562,7 @@ hipError_t launch_bwd_grad(const BwdArgs& a, int max_seqlen_q, int max_seqlen_kv
   // delta
   const int64_t items = a.total_q * a.hq;
   {
-    constexpr int LPR = D / 8;
+    constexpr int LPR = D / 8 <= 8 ? 8 : D / 8 <= 16 ? 16 : 32;  // as in delta_kernel
     const int64_t blocks = (items * LPR + 255) / 256;
     hipLaunchKernelGGL((delta_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   }

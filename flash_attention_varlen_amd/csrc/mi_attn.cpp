@@ -531,9 +531,11 @@ int mi_attn_varlen_bwd(const mi_attn_bwd_params* p_in, void* stream) {
   const int32_t dt = p->in_dtype;
   if (dt != MI_ATTN_F16 && dt != MI_ATTN_BF16)
     return fail(MI_ATTN_ERR_UNSUPPORTED, "the backward takes bf16 or fp16 inputs (got dtype %d)", dt);
-  if (!((p->d_qk == 64 && p->d_v == 64) || (p->d_qk == 128 && p->d_v == 128)))
+  if (!((p->d_qk == 64 && p->d_v == 64) || (p->d_qk == 96 && p->d_v == 96) ||
+        (p->d_qk == 128 && p->d_v == 128)))
     return fail(MI_ATTN_ERR_UNSUPPORTED,
-                "backward head dims (d_qk=%d, d_v=%d) unsupported; supported: (64,64), (128,128)",
+                "backward head dims (d_qk=%d, d_v=%d) unsupported; supported: (64,64), (96,96), "
+                "(128,128)",
                 p->d_qk, p->d_v);
   if (p->hq <= 0 || p->hkv <= 0)
     return fail(MI_ATTN_ERR_INVALID_ARG, "head counts must be positive (hq=%d, hkv=%d)", p->hq, p->hkv);

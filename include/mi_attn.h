@@ -324,8 +324,9 @@ int mi_attn_unpack_tokens(const mi_attn_pack_params* p, void* stream);
  * tile by tile.
  *
  * Supported: in_dtype BF16 or F16 (q, k, v, out, dout), dq / dk / dv in
- * in_dtype or fp32, (d_qk, d_v) in {(64,64), (128,128)}, hq % hkv == 0, window > 0 only
- * with causal.  Anything else is refused (MI_ATTN_ERR_UNSUPPORTED).
+ * in_dtype or fp32, (d_qk, d_v) in {(64,64), (96,96), (128,128)}, hq % hkv == 0,
+ * window > 0 only with causal.  Anything else is refused
+ * (MI_ATTN_ERR_UNSUPPORTED).
  */
 typedef struct mi_attn_bwd_params {
   size_t struct_size; /* sizeof(mi_attn_bwd_params) */

@@ -252,6 +252,8 @@ def _valid_bwd_params():
 BWD_REFUSALS = {
     "fp32_inputs": (dict(in_dtype=fav.F32, grad_dtype=fav.F32), fav.ERR_UNSUPPORTED),
     "latent_dims": (dict(d_qk=192, d_v=128), fav.ERR_UNSUPPORTED),
+    "dims_256": (dict(d_qk=256, d_v=256), fav.ERR_UNSUPPORTED),
+    "dims_80": (dict(d_qk=80, d_v=80), fav.ERR_UNSUPPORTED),
     "grad_dtype": (dict(grad_dtype=fav.F16), fav.ERR_UNSUPPORTED),
     "alibi_with_bias": (dict(alibi_slopes=1 << 20, bias=1 << 20, bias_heads=1, bias_cols=64,
                              bias_stride_tok=64, bias_stride_head=0), fav.ERR_UNSUPPORTED),

@@ -75,6 +75,10 @@ def _cases():
                                            d_v=d, dtype=dt, causal=True, seed=80 + d)
             c[f"full_{dt}_d{d}"] = W(name="b", seqlens_q=(200, 77), seqlens_kv=(200, 77), hq=3,
                                      hkv=3, d_qk=d, d_v=d, dtype=dt, causal=False, seed=81 + d)
+    c["gqa_causal_bf16_d96"] = W(name="b", seqlens_q=(300, 1, 129, 64), seqlens_kv=(300, 1, 129, 64),
+                                 hq=8, hkv=2, d_qk=96, d_v=96, dtype="bf16", causal=True, seed=83)
+    c["full_f16_d96"] = W(name="b", seqlens_q=(200, 77), seqlens_kv=(200, 77), hq=3, hkv=3, d_qk=96,
+                          d_v=96, dtype="f16", causal=False, seed=84)
     c["window_bf16_d128"] = W(name="b", seqlens_q=(500, 90), seqlens_kv=(500, 90), hq=4, hkv=1,
                               d_qk=128, d_v=128, dtype="bf16", causal=True, window=70, seed=82)
     c["cross_kv_longer_f16_d64"] = W(name="b", seqlens_q=(5, 130, 1), seqlens_kv=(700, 260, 90),

@@ -1,5 +1,5 @@
 """A seeded fuzzer for the backward (mi_attn_varlen_bwd) through the C ABI,
-against the fp64 oracle: bf16 / fp16, head dims 64 and 128, GQA ratios,
+against the fp64 oracle: bf16 / fp16, head dims 64, 96 and 128, GQA ratios,
 self- and cross-attention with empty and ragged sequences, causal and
 window flags, and no bias, an fp32 bias (1 or Hq heads, with -inf entries)
 or ALiBi slopes.  The tolerances are those of the backward parity tests
@@ -22,7 +22,7 @@ GRAD_TOL = {"bf16": 6e-3, "f16": 1.5e-3}
 def _case(i):
     rng = np.random.default_rng(11000 + i)
     dtype = ["bf16", "f16"][rng.integers(2)]
-    d = int(rng.choice([64, 128]))
+    d = int(rng.choice([64, 96, 128]))
     hkv = int(rng.choice([1, 2]))
     hq = hkv * int(rng.choice([1, 2, 4]))
     ns = int(rng.integers(1, 4))
